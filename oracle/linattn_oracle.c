@@ -196,14 +196,24 @@ int oracle_bwd(const double *q, const double *k, const double *v,
     const int F = cw ? 2 * D : D;
     const int nrep = H / Hkv;
     int fail = 0;
+    /* each query head's share of dk and dv, summed per group afterwards */
+    double *dk_h = malloc(sizeof(double) * (size_t)B * H * N * D);
+    double *dv_h = malloc(sizeof(double) * (size_t)B * H * N * D);
+    if (!dk_h || !dv_h) {
+        free(dk_h); free(dv_h);
+        return 2;
+    }
 
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int bg = 0; bg < B * Hkv; ++bg) {
-        const int b = bg / Hkv, g = bg % Hkv;
-        const double *kh = k + (size_t)bg * N * D;
-        const double *vh = v + (size_t)bg * N * D;
-        double *dkh = dk + (size_t)bg * N * D;
-        double *dvh = dv + (size_t)bg * N * D;
+    for (int bh = 0; bh < B * H; ++bh) {
+        const int b = bh / H, h = bh % H, g = h / nrep;
+        const double *qh = q + (size_t)bh * N * D;
+        const double *gh = gout + (size_t)bh * N * D;
+        const double *kh = k + (size_t)(b * Hkv + g) * N * D;
+        const double *vh = v + (size_t)(b * Hkv + g) * N * D;
+        double *dqh = dq + (size_t)bh * N * D;
+        double *dkh = dk_h + (size_t)bh * N * D;
+        double *dvh = dv_h + (size_t)bh * N * D;
         double *S = malloc(sizeof(double) * (size_t)F * D);
         double *z = malloc(sizeof(double) * F);
         double *qf = malloc(sizeof(double) * (size_t)N * F);
@@ -216,93 +226,103 @@ int oracle_bwd(const double *q, const double *k, const double *v,
             fail = 1;
             goto done;
         }
-        memset(dkh, 0, sizeof(double) * (size_t)N * D);
-        memset(dvh, 0, sizeof(double) * (size_t)N * D);
 
-        for (int r = 0; r < nrep; ++r) {
-            const int h = g * nrep + r;
-            const double *qh = q + (size_t)(b * H + h) * N * D;
-            const double *gh = gout + (size_t)(b * H + h) * N * D;
-            double *dqh = dq + (size_t)(b * H + h) * N * D;
-
-            /* forward sweep: den, out, gn, c and dq */
-            memset(S, 0, sizeof(double) * (size_t)F * D);
-            memset(z, 0, sizeof(double) * F);
-            if (!causal) {
-                for (int j = 0; j < N; ++j) {
-                    features(phi, kh + (size_t)j * D, D, cw, sw, j, kf);
-                    rank1(S, z, kf, vh + (size_t)j * D, F, D);
-                }
-            }
-            for (int i = 0; i < N; ++i) {
-                if (causal) {
-                    features(phi, kh + (size_t)i * D, D, cw, sw, i, kf);
-                    rank1(S, z, kf, vh + (size_t)i * D, F, D);
-                }
-                double *qfi = qf + (size_t)i * F;
-                features(phi, qh + (size_t)i * D, D, cw, sw, i, qfi);
-                double den = eps;
-                for (int f = 0; f < F; ++f) den += qfi[f] * z[f];
-                for (int d = 0; d < D; ++d) o[d] = 0.0;
-                for (int f = 0; f < F; ++f) {
-                    const double *row = S + (size_t)f * D;
-                    for (int d = 0; d < D; ++d) o[d] += qfi[f] * row[d];
-                }
-                const double *gi = gh + (size_t)i * D;
-                double *gni = gn + (size_t)i * D;
-                double go = 0.0;
-                for (int d = 0; d < D; ++d) {
-                    o[d] /= den;
-                    go += gi[d] * o[d];
-                    gni[d] = gi[d] / den;
-                }
-                c[i] = go / den;
-                for (int f = 0; f < F; ++f) {
-                    const double *row = S + (size_t)f * D;
-                    double acc = 0.0;
-                    for (int d = 0; d < D; ++d) acc += row[d] * gni[d];
-                    tmp[f] = acc - c[i] * z[f];
-                }
-                chain(phi, qh + (size_t)i * D, D, cw, sw, i, tmp,
-                      dqh + (size_t)i * D, 0);
-            }
-
-            /* reverse sweep: R, r and this head's share of dk, dv */
-            double *R = S, *rv = z;
-            memset(R, 0, sizeof(double) * (size_t)F * D);
-            memset(rv, 0, sizeof(double) * F);
-            if (!causal) {
-                for (int i = 0; i < N; ++i) {
-                    rank1(R, NULL, qf + (size_t)i * F, gn + (size_t)i * D, F, D);
-                    for (int f = 0; f < F; ++f) rv[f] += c[i] * qf[(size_t)i * F + f];
-                }
-            }
-            for (int j = N - 1; j >= 0; --j) {
-                if (causal) {
-                    rank1(R, NULL, qf + (size_t)j * F, gn + (size_t)j * D, F, D);
-                    for (int f = 0; f < F; ++f) rv[f] += c[j] * qf[(size_t)j * F + f];
-                }
+        /* forward sweep: den, out, gn, c and dq */
+        memset(S, 0, sizeof(double) * (size_t)F * D);
+        memset(z, 0, sizeof(double) * F);
+        if (!causal) {
+            for (int j = 0; j < N; ++j) {
                 features(phi, kh + (size_t)j * D, D, cw, sw, j, kf);
-                const double *vj = vh + (size_t)j * D;
-                for (int f = 0; f < F; ++f) {
-                    const double *row = R + (size_t)f * D;
-                    double acc = 0.0;
-                    for (int d = 0; d < D; ++d) acc += row[d] * vj[d];
-                    tmp[f] = acc - rv[f];
-                }
-                double *dvj = dvh + (size_t)j * D;
-                for (int f = 0; f < F; ++f) {
-                    const double *row = R + (size_t)f * D;
-                    for (int d = 0; d < D; ++d) dvj[d] += row[d] * kf[f];
-                }
-                chain(phi, kh + (size_t)j * D, D, cw, sw, j, tmp,
-                      dkh + (size_t)j * D, 1);
+                rank1(S, z, kf, vh + (size_t)j * D, F, D);
             }
+        }
+        for (int i = 0; i < N; ++i) {
+            if (causal) {
+                features(phi, kh + (size_t)i * D, D, cw, sw, i, kf);
+                rank1(S, z, kf, vh + (size_t)i * D, F, D);
+            }
+            double *qfi = qf + (size_t)i * F;
+            features(phi, qh + (size_t)i * D, D, cw, sw, i, qfi);
+            double den = eps;
+            for (int f = 0; f < F; ++f) den += qfi[f] * z[f];
+            for (int d = 0; d < D; ++d) o[d] = 0.0;
+            for (int f = 0; f < F; ++f) {
+                const double *row = S + (size_t)f * D;
+                for (int d = 0; d < D; ++d) o[d] += qfi[f] * row[d];
+            }
+            const double *gi = gh + (size_t)i * D;
+            double *gni = gn + (size_t)i * D;
+            double go = 0.0;
+            for (int d = 0; d < D; ++d) {
+                o[d] /= den;
+                go += gi[d] * o[d];
+                gni[d] = gi[d] / den;
+            }
+            c[i] = go / den;
+            for (int f = 0; f < F; ++f) {
+                const double *row = S + (size_t)f * D;
+                double acc = 0.0;
+                for (int d = 0; d < D; ++d) acc += row[d] * gni[d];
+                tmp[f] = acc - c[i] * z[f];
+            }
+            chain(phi, qh + (size_t)i * D, D, cw, sw, i, tmp, dqh + (size_t)i * D, 0);
+        }
+
+        /* reverse sweep: R, r and this head's share of dk, dv */
+        double *R = S, *rv = z;
+        memset(R, 0, sizeof(double) * (size_t)F * D);
+        memset(rv, 0, sizeof(double) * F);
+        if (!causal) {
+            for (int i = 0; i < N; ++i) {
+                rank1(R, NULL, qf + (size_t)i * F, gn + (size_t)i * D, F, D);
+                for (int f = 0; f < F; ++f) rv[f] += c[i] * qf[(size_t)i * F + f];
+            }
+        }
+        for (int j = N - 1; j >= 0; --j) {
+            if (causal) {
+                rank1(R, NULL, qf + (size_t)j * F, gn + (size_t)j * D, F, D);
+                for (int f = 0; f < F; ++f) rv[f] += c[j] * qf[(size_t)j * F + f];
+            }
+            features(phi, kh + (size_t)j * D, D, cw, sw, j, kf);
+            const double *vj = vh + (size_t)j * D;
+            for (int f = 0; f < F; ++f) {
+                const double *row = R + (size_t)f * D;
+                double acc = 0.0;
+                for (int d = 0; d < D; ++d) acc += row[d] * vj[d];
+                tmp[f] = acc - rv[f];
+            }
+            double *dvj = dvh + (size_t)j * D;
+            for (int d = 0; d < D; ++d) dvj[d] = 0.0;
+            for (int f = 0; f < F; ++f) {
+                const double *row = R + (size_t)f * D;
+                for (int d = 0; d < D; ++d) dvj[d] += row[d] * kf[f];
+            }
+            chain(phi, kh + (size_t)j * D, D, cw, sw, j, tmp, dkh + (size_t)j * D, 0);
         }
     done:
         free(S); free(z); free(qf); free(gn); free(c); free(kf); free(tmp);
         free(o);
     }
+
+    /* dk, dv of a KV head: its query heads' shares summed in order r = 0.. */
+#pragma omp parallel for schedule(static)
+    for (int bg = 0; bg < B * Hkv; ++bg) {
+        const int b = bg / Hkv, g = bg % Hkv;
+        double *dkg = dk + (size_t)bg * N * D;
+        double *dvg = dv + (size_t)bg * N * D;
+        for (size_t e = 0; e < (size_t)N * D; ++e) {
+            double sk = 0.0, sv = 0.0;
+            for (int r = 0; r < nrep; ++r) {
+                const size_t bh = (size_t)b * H + (size_t)g * nrep + r;
+                sk += dk_h[bh * N * D + e];
+                sv += dv_h[bh * N * D + e];
+            }
+            dkg[e] = sk;
+            dvg[e] = sv;
+        }
+    }
+    free(dk_h);
+    free(dv_h);
     return fail ? 2 : 0;
 }
 
