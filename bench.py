@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark: one step = forward + backward of fused feature-map linear
+attention over one batch of seeded synthetic input, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload: causal, bf16 storage, B=2, H=32, N=16384, D=128, elu+1,
+eps=1e-6 (q, k, v ~ 0.5 N(0,1), grad_out ~ N(0,1), seed 0).  Inputs, outputs
+and workspaces are resident in HBM before timing; W untimed steps, then K
+timed steps between device synchronisations.  One JSON line on stdout:
+throughput (tokens/s), the dominant kernel against its roofline (timed with
+HIP events on the library's own stream), and the CPU oracle's throughput on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 matrix
+FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 (vector and matrix)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_bytes(name, w, s):
+    """Algorithmic HBM bytes of one launch of kernel ``name``: the tensors it
+    must read and write for the part of the method it computes (workspace
+    records excluded).  q-sized = B*H*N*D*s, kv-sized = B*H_kv*N*D*s."""
+    qb = w.B * w.H * w.N * w.D * s
+    kvb = w.B * w.Hkv * w.N * w.D * s
+    rows = w.B * w.H * w.N * 4            # one float per query row (den or c)
+    table = {
+        "state": 2 * kvb,                                 # k, v
+        "fwd_causal": 2 * qb + 2 * kvb,                   # q, k, v -> out
+        "fwd_bidir": 2 * qb,                              # q -> out
+        "bwd_q_causal": 3 * qb + 2 * kvb + 2 * rows,      # q, k, v, g -> dq, den, c
+        "bwd_q_bidir": 3 * qb,                            # q, g -> dq
+        "bwd_kv_causal": 2 * qb + 4 * kvb + 2 * rows,     # q, g, den, c, k, v -> dk, dv
+        "bwd_kv_bidir": 4 * kvb,                          # k, v -> dk, dv
+    }
+    for key, val in table.items():
+        if name.endswith(key) or ("_" + key) in name:
+            return val
+    return None
+
+
+def step_roofline(w, s, causal):
+    """Time of one fwd+bwd step at the roofline: algorithmic bytes at HBM peak
+    vs algorithmic flops at the bf16 matrix peak (state updates and reads,
+    2*F*D per token each; F = 2D with cos/sin)."""
+    br = 2 if w.cos else 1
+    tokD = w.B * w.N * w.D
+    fwd_bytes = s * tokD * (2 * w.H + 2 * w.Hkv) + (8 * w.N if w.cos else 0)
+    bwd_bytes = s * tokD * (3 * w.H + 4 * w.Hkv)
+    fwd_flops = br * 2 * w.D * w.D * w.B * w.N * (w.H + w.Hkv)
+    bwd_flops = br * 2 * w.D * w.D * w.B * w.N * (3 * w.H + 3 * w.Hkv)
+    t_bytes = (fwd_bytes + bwd_bytes) / (HBM_PEAK_GBS * 1e9)
+    t_flops = (fwd_flops + bwd_flops) / (BF16_PEAK_TFLOPS * 1e12)
+    return max(t_bytes, t_flops), fwd_bytes + bwd_bytes, fwd_flops + bwd_flops
+
+
+def cpu_baseline(w, tensors, budget_heads=None):
+    """The CPU oracle, as it is, on whole (batch, KV head) groups at full N,
+    fwd + bwd; throughput scaled to the whole workload by group count."""
+    import numpy as np
+
+    import oracle
+    import seeded_inputs as si
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    n_groups = w.B * w.Hkv
+    nrep = w.H // w.Hkv
+    take = budget_heads or max(1, threads // nrep)
+    take = min(take, n_groups)
+    units = [(b, g) for b in range(w.B) for g in range(w.Hkv)][:take]
+    f64 = {n: si.exact_f64(t) for n, t in tensors.items() if t is not None and t.dim() == 4}
+    parts = [oracle.group_slice(f64["q"], f64["k"], f64["v"], f64["grad_out"], b, g)
+             for b, g in units]
+    q = np.concatenate([p[0] for p in parts])
+    k = np.concatenate([p[1] for p in parts])
+    v = np.concatenate([p[2] for p in parts])
+    g = np.concatenate([p[3] for p in parts])
+    cw = sw = None
+    if tensors.get("cos_weight") is not None:
+        cw, sw = si.exact_f64(tensors["cos_weight"]), si.exact_f64(tensors["sin_weight"])
+    causal = "causal" in w.modes
+    kw = dict(is_causal=causal, phi=w.phi, eps=w.eps, cos_weight=cw, sin_weight=sw)
+    t0 = time.perf_counter()
+    oracle.fwd(q, k, v, **kw)
+    oracle.bwd(q, k, v, g, **kw)
+    dt = time.perf_counter() - t0
+    t_full = dt * n_groups / take
+    return {
+        "value": w.B * w.N / t_full,
+        "unit": "tokens/s",
+        "cores": min(threads, take * nrep),
+        "kind": "oracle",
+        "sample": "%d of %d (batch, KV head) groups (%d query heads each) at full N=%d, "
+                  "fwd+bwd in fp64, %.1f s; scaled by group count" % (take, n_groups, nrep, w.N, dt),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(got --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import linear_attention_transformers_amd as la
+    import seeded_inputs as si
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    la.load_library()
+    name = args.workload or si.HEADLINE
+    w = si.WORKLOADS[name]
+    dtype = w.dtypes[0]
+    causal = "causal" in w.modes
+    s = 2 if dtype == "bf16" else 4
+    dev = torch.device("cuda:0")
+
+    log("bench: drawing %s inputs" % name)
+    t = si.workload_inputs(w, dtype, dev)
+    cw, sw = t["cos_weight"], t["sin_weight"]
+    out = torch.empty_like(t["q"])
+    grads = (torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"]))
+    code = la.LA_BF16 if dtype == "bf16" else la.LA_F32
+    ws_f = torch.empty(la.workspace_bytes("fwd", w.B, w.H, w.Hkv, w.N, w.D, code, causal,
+                                          w.cos), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(la.workspace_bytes("bwd", w.B, w.H, w.Hkv, w.N, w.D, code, causal,
+                                          w.cos), dtype=torch.uint8, device=dev)
+
+    def step():
+        la.fwd(t["q"], t["k"], t["v"], is_causal=causal, phi=w.phi, eps=w.eps, cos_weight=cw,
+               sin_weight=sw, out=out, workspace=ws_f)
+        if w.backward:
+            la.bwd(t["q"], t["k"], t["v"], t["grad_out"], is_causal=causal, phi=w.phi,
+                   eps=w.eps, cos_weight=cw, sin_weight=sw, workspace=ws_b, grads=grads)
+
+    log("bench: %d warmup steps" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log("bench: %d timed steps" % args.steps)
+    la.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    la.timing_enable(False)
+    ktimes = la.timing_collect()
+
+    tokens = w.B * w.N
+    ms_step = elapsed * 1e3 / args.steps
+    value = tokens * args.steps / elapsed
+
+    # dominant kernel by total event time over the timed region
+    dom = max(ktimes.items(), key=lambda kv: kv[1][1])
+    dom_name, (launches, total_ms) = dom
+    avg_s = total_ms / launches / 1e3
+    nbytes = kernel_bytes(dom_name, w, s)
+    roof = {"bound": "hbm", "kernel": dom_name, "achieved": None, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": None, "traffic": None,
+            "avg_launch_ms": avg_s * 1e3, "algorithmic_bytes_per_launch": nbytes}
+    if nbytes is not None:
+        ach = nbytes / avg_s / 1e9
+        roof["achieved"] = ach
+        roof["frac"] = ach / HBM_PEAK_GBS
+    t_roof, step_bytes, step_flops = step_roofline(w, s, causal)
+    matrix = any("mfma" in k for k in ktimes)
+
+    result = {
+        "metric": "fwd+bwd tokens/sec and % roofline, causal bf16 N=16384 D=128",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if matrix else "f32",
+        "data": "synthetic",
+        "config": {"workload": name, "B": w.B, "H": w.H, "H_kv": w.Hkv, "N": w.N, "D": w.D,
+                   "phi": w.phi, "causal": causal, "cos_sin": w.cos, "storage": dtype,
+                   "eps": w.eps, "pass": "fwd+bwd" if w.backward else "fwd"},
+        "roofline": roof,
+        "step_roofline": {"t_roof_ms": t_roof * 1e3, "frac": t_roof * 1e3 / ms_step,
+                          "algorithmic_bytes": step_bytes, "algorithmic_flops": step_flops},
+        "kernels_ms_per_step": {k: v[1] / args.steps for k, v in ktimes.items()},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(w, t)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

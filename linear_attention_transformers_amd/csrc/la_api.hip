@@ -1,0 +1,254 @@
+// la_api.hip -- the C ABI declared in include/linattn.h: argument validation
+// (all of it before any device work), workspace sizing and layout, and
+// dispatch to the kernel families.
+//
+// Validation mirrors what the SVD_linear_Attention pages require of a call:
+// "Module neuralops.core.triton_kernels.gqa", function is_supported, rejects
+// non-positive head counts and num_heads not divisible by num_kv_heads; the
+// linear_attn page's fwd takes cos_weight and sin_weight as a pair.  Where the
+// pages fall back to a different implementation for unsupported inputs, this
+// library returns LA_ERR_UNSUPPORTED instead.
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/linattn.h"
+#include "la_common.h"
+#include "la_kernels.h"
+#include "la_timing.h"
+
+namespace la {
+
+// Per-thread launch timing (see la_timing.h).
+struct TimingRec {
+    const char *name;
+    hipEvent_t start, stop;
+};
+thread_local bool g_timing = false;
+thread_local std::vector<TimingRec> g_recs;
+
+bool timing_on() { return g_timing; }
+
+void timing_begin(const char *name, hipStream_t s) {
+    TimingRec r{name, nullptr, nullptr};
+    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) return;
+    if (hipEventRecord(r.start, s) != hipSuccess) {
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+        return;
+    }
+    g_recs.push_back(r);
+}
+
+void timing_end(hipStream_t s) {
+    if (!g_recs.empty()) (void)hipEventRecord(g_recs.back().stop, s);
+}
+
+}  // namespace la
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+la_status fail(la_status st, const char *msg) {
+    snprintf(g_err, sizeof g_err, "%s", msg);
+    return st;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+la_status check_shape(int B, int H, int H_kv, int N, int D, int dtype, int phi) {
+    if (B <= 0 || H <= 0 || H_kv <= 0 || N <= 0 || D <= 0)
+        return fail(LA_ERR_INVALID, "B, H, H_kv, N and D must be positive");
+    if (H % H_kv != 0) return fail(LA_ERR_INVALID, "H must be a multiple of H_kv");
+    if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_ERR_INVALID, "unknown dtype");
+    if (phi != LA_PHI_ELU1 && phi != LA_PHI_RELU && phi != LA_PHI_IDENTITY)
+        return fail(LA_ERR_INVALID, "unknown feature map");
+    // element counts must stay addressable with 64-bit offsets and the
+    // kernels' 32-bit row indices
+    if ((long long)N * D >= (1LL << 31))
+        return fail(LA_ERR_INVALID, "N * D must be below 2^31");
+    if (D != 32 && D != 64 && D != 128)
+        return fail(LA_ERR_UNSUPPORTED, "head dimension D must be 32, 64 or 128");
+    return LA_OK;
+}
+
+la_status check_common(int B, int H, int H_kv, int N, int D, int dtype, int phi, float eps,
+                       const float *cw, const float *sw, void *ws, size_t ws_bytes,
+                       size_t need) {
+    la_status st = check_shape(B, H, H_kv, N, D, dtype, phi);
+    if (st != LA_OK) return st;
+    if (!isfinite(eps) || eps < 0.f) return fail(LA_ERR_INVALID, "eps must be finite and >= 0");
+    if ((cw == nullptr) != (sw == nullptr))
+        return fail(LA_ERR_INVALID, "cos_w and sin_w must both be given or both be NULL");
+    if (cw && (!aligned(cw, 4) || !aligned(sw, 4)))
+        return fail(LA_ERR_INVALID, "cos_w / sin_w must be 4-byte aligned");
+    if (ws_bytes < need) return fail(LA_ERR_INVALID, "workspace too small");
+    if (need > 0 && ws == nullptr) return fail(LA_ERR_INVALID, "workspace pointer is NULL");
+    if (ws && !aligned(ws, 256)) return fail(LA_ERR_INVALID, "workspace must be 256-byte aligned");
+    return LA_OK;
+}
+
+la::Args make_args(const la::Plan &p, int B, int H, int H_kv, int N, int D, float eps,
+                   const float *cw, const float *sw, void *ws) {
+    la::Args a{};
+    char *w = static_cast<char *>(ws);
+    a.cw = cw;
+    a.sw = sw;
+    a.ws_S = reinterpret_cast<float *>(w + p.off_S);
+    a.ws_Rp = reinterpret_cast<float *>(w + p.off_Rp);
+    a.ws_Rs = reinterpret_cast<float *>(w + p.off_Rs);
+    a.ws_den = reinterpret_cast<float *>(w + p.off_den);
+    a.ws_c = reinterpret_cast<float *>(w + p.off_c);
+    a.B = B;
+    a.H = H;
+    a.Hkv = H_kv;
+    a.N = N;
+    a.D = D;
+    a.F = p.F;
+    a.nrep = H / H_kv;
+    a.L = p.L;
+    a.nseg = p.nseg;
+    a.eps = eps;
+    return a;
+}
+
+la_status launch_status(hipError_t e) {
+    if (e != hipSuccess) {
+        snprintf(g_err, sizeof g_err, "HIP: %s", hipGetErrorString(e));
+        return LA_ERR_HIP;
+    }
+    return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t la_workspace_bytes_ex(int op, int B, int H, int H_kv, int N, int D, int dtype,
+                             int causal, int has_cos, int seg_len) {
+    if (op != LA_OP_FWD && op != LA_OP_BWD) return 0;
+    if (check_shape(B, H, H_kv, N, D, dtype, LA_PHI_ELU1) != LA_OK) return 0;
+    if (seg_len < 0) return 0;
+    return la::make_plan(op == LA_OP_BWD, B, H, H_kv, N, D, causal, has_cos != 0, seg_len).bytes;
+}
+
+size_t la_workspace_bytes(int op, int B, int H, int H_kv, int N, int D, int dtype, int causal,
+                          int has_cos) {
+    return la_workspace_bytes_ex(op, B, H, H_kv, N, D, dtype, causal, has_cos, 0);
+}
+
+la_status la_fwd_ex(const void *q, const void *k, const void *v, void *out, int B, int H,
+                    int H_kv, int N, int D, int dtype, int causal, int phi, float eps,
+                    const float *cos_w, const float *sin_w, void *ws, size_t ws_bytes,
+                    void *stream, int seg_len) {
+    g_err[0] = 0;
+    if (!q || !k || !v || !out) return fail(LA_ERR_INVALID, "q, k, v and out must be non-NULL");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return fail(LA_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
+    if (seg_len < 0) return fail(LA_ERR_INVALID, "seg_len must be >= 0");
+    la_status st = check_shape(B, H, H_kv, N, D, dtype, phi);
+    if (st != LA_OK) return st;
+    const la::Plan p = la::make_plan(0, B, H, H_kv, N, D, causal, cos_w != nullptr, seg_len);
+    st = check_common(B, H, H_kv, N, D, dtype, phi, eps, cos_w, sin_w, ws, ws_bytes, p.bytes);
+    if (st != LA_OK) return st;
+    la::Args a = make_args(p, B, H, H_kv, N, D, eps, cos_w, sin_w, ws);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return launch_status(la::generic_run(a, dtype == LA_BF16, 0, causal != 0, phi, s));
+}
+
+la_status la_fwd(const void *q, const void *k, const void *v, void *out, int B, int H, int H_kv,
+                 int N, int D, int dtype, int causal, int phi, float eps, const float *cos_w,
+                 const float *sin_w, void *ws, size_t ws_bytes, void *stream) {
+    return la_fwd_ex(q, k, v, out, B, H, H_kv, N, D, dtype, causal, phi, eps, cos_w, sin_w, ws,
+                     ws_bytes, stream, 0);
+}
+
+la_status la_bwd_ex(const void *q, const void *k, const void *v, const void *grad_out, void *dq,
+                    void *dk, void *dv, int B, int H, int H_kv, int N, int D, int dtype,
+                    int causal, int phi, float eps, const float *cos_w, const float *sin_w,
+                    void *ws, size_t ws_bytes, void *stream, int seg_len) {
+    g_err[0] = 0;
+    if (!q || !k || !v || !grad_out || !dq || !dk || !dv)
+        return fail(LA_ERR_INVALID, "q, k, v, grad_out, dq, dk and dv must be non-NULL");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(grad_out, 16) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+        return fail(LA_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+    if (seg_len < 0) return fail(LA_ERR_INVALID, "seg_len must be >= 0");
+    la_status st = check_shape(B, H, H_kv, N, D, dtype, phi);
+    if (st != LA_OK) return st;
+    const la::Plan p = la::make_plan(1, B, H, H_kv, N, D, causal, cos_w != nullptr, seg_len);
+    st = check_common(B, H, H_kv, N, D, dtype, phi, eps, cos_w, sin_w, ws, ws_bytes, p.bytes);
+    if (st != LA_OK) return st;
+    la::Args a = make_args(p, B, H, H_kv, N, D, eps, cos_w, sin_w, ws);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = grad_out;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return launch_status(la::generic_run(a, dtype == LA_BF16, 1, causal != 0, phi, s));
+}
+
+la_status la_bwd(const void *q, const void *k, const void *v, const void *grad_out, void *dq,
+                 void *dk, void *dv, int B, int H, int H_kv, int N, int D, int dtype, int causal,
+                 int phi, float eps, const float *cos_w, const float *sin_w, void *ws,
+                 size_t ws_bytes, void *stream) {
+    return la_bwd_ex(q, k, v, grad_out, dq, dk, dv, B, H, H_kv, N, D, dtype, causal, phi, eps,
+                     cos_w, sin_w, ws, ws_bytes, stream, 0);
+}
+
+const char *la_status_string(int status) {
+    switch (status) {
+        case LA_OK: return "LA_OK: success";
+        case LA_ERR_INVALID: return "LA_ERR_INVALID: invalid argument";
+        case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED: unsupported configuration";
+        case LA_ERR_HIP: return "LA_ERR_HIP: HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char *la_last_error(void) { return g_err; }
+
+la_status la_timing_enable(int enable) {
+    la::g_timing = enable != 0;
+    return LA_OK;
+}
+
+int la_timing_collect(la_kernel_time *out, int max_entries) {
+    int n = 0;
+    for (const la::TimingRec &r : la::g_recs) {
+        float ms = 0.f;
+        if (hipEventSynchronize(r.stop) != hipSuccess ||
+            hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+            ms = -1.f;   // not measurable: reported as a negative total
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+        int slot = -1;
+        for (int i = 0; i < n; ++i)
+            if (strncmp(out[i].name, r.name, sizeof out[i].name) == 0) slot = i;
+        if (slot < 0 && n < max_entries && out) {
+            slot = n++;
+            snprintf(out[slot].name, sizeof out[slot].name, "%s", r.name);
+            out[slot].launches = 0;
+            out[slot].total_ms = 0.0;
+        }
+        if (slot >= 0) {
+            out[slot].launches += 1;
+            out[slot].total_ms += ms;
+        }
+    }
+    la::g_recs.clear();
+    return n;
+}
+
+}  // extern "C"

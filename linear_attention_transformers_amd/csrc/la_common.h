@@ -1,0 +1,139 @@
+// la_common.h -- shared definitions of the linear-attention HIP library:
+// storage-type loads/stores, the feature maps, the launch plan and the
+// workspace layout.  Included by every kernel translation unit and by the
+// C-ABI front end.
+//
+// Feature maps (SVD_linear_Attention, "Module
+// neuralops.core.triton_kernels.linear_attn", module docstring): elu+1
+// (alpha = 1), relu, identity.  The cos/sin modulation of the same docstring
+// multiplies phi(x_t) by cos_w[t] and by sin_w[t], giving a feature vector of
+// width F = 2D whose halves are the two branches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace la {
+
+enum Phi : int { kElu1 = 0, kRelu = 1, kIdentity = 2 };
+
+// bfloat16 storage as raw 16-bit words.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x.bits) << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// float32 -> bfloat16, round to nearest even; NaN stays a quiet NaN.
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
+    uint32_t u = __float_as_uint(x);
+    bf16_t r;
+    if ((u & 0x7fffffffu) > 0x7f800000u) {
+        r.bits = static_cast<uint16_t>((u >> 16) | 0x40u);
+        return r;
+    }
+    u += 0x7fffu + ((u >> 16) & 1u);
+    r.bits = static_cast<uint16_t>(u >> 16);
+    return r;
+}
+
+template <int PHI>
+__device__ __forceinline__ float phi_f(float x) {
+    if constexpr (PHI == kElu1) return x > 0.f ? x + 1.f : expf(x);
+    else if constexpr (PHI == kRelu) return x > 0.f ? x : 0.f;
+    else return x;
+}
+
+// Derivative; relu'(0) = 0 and both sides of elu+1 give 1 at 0.
+template <int PHI>
+__device__ __forceinline__ float phi_d(float x) {
+    if constexpr (PHI == kElu1) return x > 0.f ? 1.f : expf(x);
+    else if constexpr (PHI == kRelu) return x > 0.f ? 1.f : 0.f;
+    else return 1.f;
+}
+
+// Everything a kernel needs, passed by value.
+struct Args {
+    const void *q, *k, *v, *g;     // inputs (g = grad_out, backward only)
+    void *out, *dq, *dk, *dv;      // outputs
+    const float *cw, *sw;          // [N] position weights or nullptr
+    float *ws_S;    // [B*Hkv][nseg+1][SD]: per-segment (S, z), then prefix/total
+    float *ws_Rp;   // [B*H][nseg][SD]:     per-head, per-segment (R, r) partials
+    float *ws_Rs;   // [B*Hkv][nseg+1][SD]: suffix (causal) / total (bidir) of (R, r)
+    float *ws_den;  // [B*H][N] denominators (causal backward)
+    float *ws_c;    // [B*H][N] c_i = (g_i . out_i) / den_i (causal backward)
+    int B, H, Hkv, N, D, F, nrep;
+    int L;          // segment length in rows (multiple of every chunk length)
+    int nseg;
+    float eps;
+};
+
+// ---------------------------------------------------------------------------
+// Launch plan and workspace layout (host and device agree on these).
+// ---------------------------------------------------------------------------
+struct Plan {
+    int F;          // feature width (D or 2D)
+    int L;          // segment length
+    int nseg;       // number of segments
+    size_t SD;      // floats per state record: F*D + F
+    size_t off_S, off_Rp, off_Rs, off_den, off_c, bytes;
+};
+
+constexpr int kSegAlign = 64;   // every chunk length divides this
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Segment count: enough (batch, head, segment) work items to give every one
+// of the 256 compute units several workgroups, but never segments shorter
+// than 4 * kSegAlign rows (the state record would outweigh the rows).
+inline Plan make_plan(int op_bwd, int B, int H, int Hkv, int N, int D, int causal,
+                      int has_cos, int seg_len) {
+    Plan p{};
+    p.F = has_cos ? 2 * D : D;
+    p.SD = (size_t)p.F * D + p.F;
+    int L;
+    if (seg_len > 0) {
+        L = (int)align_up((size_t)seg_len, kSegAlign);
+    } else {
+        const long long target = 1024;
+        long long heads = (long long)B * H;
+        long long nseg = (target + heads - 1) / heads;
+        L = (int)align_up((size_t)((N + nseg - 1) / nseg), kSegAlign);
+        if (L < 4 * kSegAlign) L = 4 * kSegAlign;
+    }
+    if (L > (int)align_up((size_t)N, kSegAlign)) L = (int)align_up((size_t)N, kSegAlign);
+    p.L = L;
+    p.nseg = (N + L - 1) / L;
+    const size_t a = 256;
+    size_t off = 0;
+    p.off_S = off;
+    off = align_up(off + sizeof(float) * (size_t)B * Hkv * (p.nseg + 1) * p.SD, a);
+    p.off_Rp = p.off_Rs = p.off_den = p.off_c = off;
+    if (op_bwd) {
+        p.off_Rp = off;
+        off = align_up(off + sizeof(float) * (size_t)B * H * p.nseg * p.SD, a);
+        p.off_Rs = off;
+        off = align_up(off + sizeof(float) * (size_t)B * Hkv * (p.nseg + 1) * p.SD, a);
+        if (causal) {
+            p.off_den = off;
+            off = align_up(off + sizeof(float) * (size_t)B * H * N, a);
+            p.off_c = off;
+            off = align_up(off + sizeof(float) * (size_t)B * H * N, a);
+        }
+    }
+    p.bytes = off;
+    return p;
+}
+
+}  // namespace la

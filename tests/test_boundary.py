@@ -1,0 +1,138 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every function
+include/linattn.h declares, sizes workspaces, and rejects bad arguments with
+the documented status before any device work (these calls never reach the
+GPU, so they run without one)."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import linear_attention_transformers_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(la.LIB_PATH):
+        from linear_attention_transformers_amd import build
+        build.build()
+    return la.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = la.header_functions()
+    assert {"la_fwd", "la_bwd", "la_workspace_bytes", "la_status_string"} <= set(names)
+    nm = subprocess.run(["nm", "-D", "--defined-only", la.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = {line.split()[-1] for line in nm.splitlines() if line.strip()}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    for st in range(4):
+        assert lib.la_status_string(st).startswith(b"LA_")
+    assert lib.la_status_string(99) == b"unknown status"
+
+
+def _fwd(lib, **over):
+    p = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: validation fails first
+    kw = dict(q=p, k=p, v=p, out=p, B=1, H=2, H_kv=2, N=16, D=32, dtype=la.LA_BF16, causal=1,
+              phi=0, eps=1e-6, cw=None, sw=None, ws=p, ws_bytes=1 << 40, stream=None)
+    kw.update(over)
+    return lib.la_fwd(kw["q"], kw["k"], kw["v"], kw["out"], kw["B"], kw["H"], kw["H_kv"],
+                      kw["N"], kw["D"], kw["dtype"], kw["causal"], kw["phi"], kw["eps"], kw["cw"],
+                      kw["sw"], kw["ws"], kw["ws_bytes"], kw["stream"])
+
+
+def _bwd(lib, **over):
+    p = ctypes.c_void_p(1 << 20)
+    kw = dict(q=p, k=p, v=p, g=p, dq=p, dk=p, dv=p, B=1, H=2, H_kv=2, N=16, D=32,
+              dtype=la.LA_F32, causal=0, phi=1, eps=1e-6, cw=None, sw=None, ws=p,
+              ws_bytes=1 << 40, stream=None)
+    kw.update(over)
+    return lib.la_bwd(kw["q"], kw["k"], kw["v"], kw["g"], kw["dq"], kw["dk"], kw["dv"], kw["B"],
+                      kw["H"], kw["H_kv"], kw["N"], kw["D"], kw["dtype"], kw["causal"], kw["phi"],
+                      kw["eps"], kw["cw"], kw["sw"], kw["ws"], kw["ws_bytes"], kw["stream"])
+
+
+FP = ctypes.cast(ctypes.c_void_p(1 << 20), ctypes.POINTER(ctypes.c_float))
+BAD = [
+    ("null q", dict(q=None), la.LA_ERR_INVALID),
+    ("zero B", dict(B=0), la.LA_ERR_INVALID),
+    ("negative N", dict(N=-3), la.LA_ERR_INVALID),
+    ("H not multiple of H_kv", dict(H=3, H_kv=2), la.LA_ERR_INVALID),
+    ("zero H_kv", dict(H_kv=0), la.LA_ERR_INVALID),
+    ("unknown dtype", dict(dtype=7), la.LA_ERR_INVALID),
+    ("unknown phi", dict(phi=3), la.LA_ERR_INVALID),
+    ("negative eps", dict(eps=-1.0), la.LA_ERR_INVALID),
+    ("nan eps", dict(eps=float("nan")), la.LA_ERR_INVALID),
+    ("cos without sin", dict(cw=FP), la.LA_ERR_INVALID),
+    ("sin without cos", dict(sw=FP), la.LA_ERR_INVALID),
+    ("misaligned q", dict(q=ctypes.c_void_p((1 << 20) + 2)), la.LA_ERR_INVALID),
+    ("workspace too small", dict(ws_bytes=8), la.LA_ERR_INVALID),
+    ("null workspace", dict(ws=None), la.LA_ERR_INVALID),
+    ("D = 48", dict(D=48), la.LA_ERR_UNSUPPORTED),
+    ("D = 256", dict(D=256), la.LA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("name,over,status", BAD, ids=[b[0] for b in BAD])
+def test_forward_rejects(lib, name, over, status):
+    assert _fwd(lib, **over) == status
+    assert lib.la_last_error() != b""
+
+
+@pytest.mark.parametrize("name,over,status", BAD, ids=[b[0] for b in BAD])
+def test_backward_rejects(lib, name, over, status):
+    over = {("g" if k == "out" else k): v for k, v in over.items()}
+    assert _bwd(lib, **over) == status
+
+
+def test_backward_rejects_null_gradient(lib):
+    assert _bwd(lib, g=None) == la.LA_ERR_INVALID
+    assert _bwd(lib, dk=None) == la.LA_ERR_INVALID
+
+
+def test_workspace_sizes(lib):
+    for op in (la.LA_OP_FWD, la.LA_OP_BWD):
+        for causal in (0, 1):
+            for cos in (0, 1):
+                n = lib.la_workspace_bytes(op, 2, 4, 2, 1000, 64, la.LA_BF16, causal, cos)
+                assert n > 0 and n % 256 == 0
+    # backward needs more than forward; cos/sin doubles the state
+    f = lib.la_workspace_bytes(la.LA_OP_FWD, 1, 4, 4, 4096, 128, 1, 1, 0)
+    b = lib.la_workspace_bytes(la.LA_OP_BWD, 1, 4, 4, 4096, 128, 1, 1, 0)
+    c = lib.la_workspace_bytes(la.LA_OP_FWD, 1, 4, 4, 4096, 128, 1, 1, 1)
+    assert b > f and c > f
+    # rejected arguments size to zero
+    assert lib.la_workspace_bytes(la.LA_OP_FWD, 1, 3, 2, 16, 32, 1, 1, 0) == 0
+    assert lib.la_workspace_bytes(la.LA_OP_FWD, 1, 2, 2, 16, 48, 1, 1, 0) == 0
+    assert lib.la_workspace_bytes(5, 1, 2, 2, 16, 32, 1, 1, 0) == 0
+    # explicit segment length: more segments, more workspace
+    a = lib.la_workspace_bytes_ex(la.LA_OP_FWD, 1, 2, 2, 4096, 64, 1, 1, 0, 64)
+    z = lib.la_workspace_bytes_ex(la.LA_OP_FWD, 1, 2, 2, 4096, 64, 1, 1, 0, 4096)
+    assert a > z > 0
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 2, 8, 32)
+    with pytest.raises(ValueError):
+        la.fwd(q, q, q)
+    with pytest.raises(ValueError):
+        la.bwd(q, q, q, q)
+    assert not la.is_supported(q, q, q)
+
+
+def test_product_never_imports_oracle():
+    """The library and its binding share no code with the CPU oracle."""
+    pkg = os.path.join(ROOT, "linear_attention_transformers_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read().lower()
+                assert "oracle" not in text, f

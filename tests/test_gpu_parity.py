@@ -1,0 +1,203 @@
+"""GPU parity: the HIP path (through the C ABI and its binding) against the
+CPU oracle on the same seeded inputs.
+
+* small shapes that span several chunks, several segments and a ragged tail,
+  for every storage type, head size, feature map, mode, cos/sin and GQA;
+* edge cases (N = 1, N shorter than a chunk, one row past a chunk boundary);
+* the five specified workloads at full size in the launch configuration the
+  benchmark times, compared on sampled (batch, KV head) groups, which the
+  oracle computes exactly because groups never interact;
+* GQA index mapping: bitwise equal to a pre-expanded run (out, dq), and local
+  (perturbing one query head changes nothing else) -- gqa page, bwd;
+* run-to-run bitwise determinism.
+"""
+import numpy as np
+import pytest
+
+import seeded_inputs as si
+from parity_util import compare, gpu_or_skip, make, np64, oracle_on, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+# --------------------------------------------------------------------------
+# small shapes, full oracle
+# --------------------------------------------------------------------------
+SMALL = []
+for dtype in ("f32", "bf16"):
+    for D in (32, 64, 128):
+        for phi in ("elu+1", "relu"):
+            for causal in (True, False):
+                SMALL.append((dtype, D, phi, causal, False, 4, 2))
+    for D in (32, 64, 128):
+        SMALL.append((dtype, D, "elu+1", True, True, 4, 1))
+        SMALL.append((dtype, D, "relu", False, True, 2, 2))
+    SMALL.append((dtype, 64, "identity", True, False, 2, 2))
+    SMALL.append((dtype, 64, "identity", False, True, 4, 4))
+
+
+def _id(c):
+    dtype, D, phi, causal, cos, H, Hkv = c
+    return "%s-D%d-%s-%s%s-h%dkv%d" % (dtype, D, phi, "causal" if causal else "bidir",
+                                       "-cos" if cos else "", H, Hkv)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[_id(c) for c in SMALL])
+def test_small_shapes(case):
+    torch, la = gpu_or_skip()
+    dtype, D, phi, causal, cos, H, Hkv = case
+    B, N = 2, 300                     # 300 rows: several chunks, ragged tail
+    positive = phi == "identity"
+    t = make(B, H, Hkv, N, D, dtype, scale=0.5, cos=cos, seed=D + H)
+    if positive:   # identity is not non-negative: keep the denominators away from 0
+        for n in ("q", "k"):
+            t[n] = t[n].abs()
+    eps = 1e-6 if not positive else 1.0
+    say("case %s" % _id(case))
+    ref = oracle_on(t, causal, phi, eps)
+    for seg_len in (0, 64):           # automatic split, then many short segments
+        out, grads = run_gpu(la, t, causal, phi, eps, seg_len=seg_len)
+        compare(t, out, grads, ref[0], ref[1], dtype, H, Hkv, label="seg_len=%d" % seg_len)
+
+
+@pytest.mark.parametrize("N", [1, 5, 31, 33, 64, 65, 129])
+@pytest.mark.parametrize("causal", [True, False])
+def test_edge_lengths(N, causal):
+    torch, la = gpu_or_skip()
+    for dtype, D, cos in (("f32", 64, False), ("bf16", 128, True)):
+        t = make(1, 2, 1, N, D, dtype, scale=0.5, cos=cos, seed=N)
+        say("edge N=%d %s D=%d cos=%s causal=%s" % (N, dtype, D, cos, causal))
+        ref = oracle_on(t, causal, "elu+1")
+        out, grads = run_gpu(la, t, causal, "elu+1")
+        compare(t, out, grads, ref[0], ref[1], dtype, 2, 1, label="N=%d" % N)
+
+
+def test_tiny_fp32_workload():
+    """B=1, H=2, N=256, D=32, float32, elu+1, eps=1e-6, both modes, fwd+bwd."""
+    torch, la = gpu_or_skip()
+    w = si.WORKLOADS["tiny_fp32"]
+    t = si.workload_inputs(w, "f32", "cuda")
+    for mode in w.modes:
+        causal = mode == "causal"
+        ref = oracle_on(t, causal, w.phi, w.eps)
+        for seg_len in (0, 64):
+            say("tiny_fp32 %s seg_len=%d" % (mode, seg_len))
+            out, grads = run_gpu(la, t, causal, w.phi, w.eps, seg_len=seg_len)
+            compare(t, out, grads, ref[0], ref[1], "f32", w.H, w.Hkv, label=mode)
+
+
+# --------------------------------------------------------------------------
+# full-size workloads, sampled groups
+# --------------------------------------------------------------------------
+def _sample_groups(w, count):
+    rng = np.random.default_rng(123)
+    units = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+    idx = sorted(rng.choice(len(units), size=min(count, len(units)), replace=False))
+    # always include the first and the last group
+    pick = {units[0], units[-1]} | {units[i] for i in idx}
+    return sorted(pick)[:max(count, 2)]
+
+
+FULL = [("causal_fwd_b4h16n4096d64", "bf16", 6), ("bidir_enc_b16h12n2048d64", "bf16", 6),
+        ("bidir_enc_b16h12n2048d64", "f32", 6), ("causal_train_b2h32n16384d128", "bf16", 4),
+        ("causal_gqa_cos_b1h32kv8n65536d128", "bf16", 1)]
+
+
+@pytest.mark.parametrize("name,dtype,count", FULL, ids=["%s-%s" % (n, d) for n, d, _ in FULL])
+def test_full_size_workloads(name, dtype, count):
+    torch, la = gpu_or_skip()
+    w = si.WORKLOADS[name]
+    say("workload %s %s: drawing inputs" % (name, dtype))
+    t = si.workload_inputs(w, dtype, "cuda")
+    causal = w.modes == ("causal",)
+    say("workload %s %s: GPU run" % (name, dtype))
+    out, grads = run_gpu(la, t, causal, w.phi, w.eps, backward=w.backward)
+    groups = _sample_groups(w, count)
+    say("workload %s: oracle on groups %s" % (name, groups))
+    ref = oracle_on(t, causal, w.phi, w.eps, backward=w.backward, groups=groups)
+    compare(t, out, grads, ref[0], ref[1], dtype, w.H, w.Hkv, groups=groups, label=name)
+    # every output is finite everywhere, not only on the sampled groups
+    assert torch.isfinite(out).all()
+    if grads is not None:
+        assert all(torch.isfinite(x).all() for x in grads)
+
+
+# --------------------------------------------------------------------------
+# GQA head-index mapping (gqa page, bwd: head axis viewed as (H_kv, n_rep))
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_gqa_bitwise_equals_expanded(dtype, causal):
+    torch, la = gpu_or_skip()
+    B, H, Hkv, N, D = 2, 8, 2, 200, 64
+    nrep = H // Hkv
+    t = make(B, H, Hkv, N, D, dtype, scale=0.5, cos=True, seed=7)
+    e = dict(t)
+    e["k"] = t["k"].repeat_interleave(nrep, dim=1).contiguous()
+    e["v"] = t["v"].repeat_interleave(nrep, dim=1).contiguous()
+    out_g, (dq_g, dk_g, dv_g) = run_gpu(la, t, causal, "relu")
+    out_e, (dq_e, dk_e, dv_e) = run_gpu(la, e, causal, "relu")
+    assert torch.equal(out_g, out_e)
+    assert torch.equal(dq_g, dq_e)
+    # KV gradients: sum over the n_rep axis of the expanded gradients
+    dk_sum = dk_e.float().view(B, Hkv, nrep, N, D).sum(2)
+    dv_sum = dv_e.float().view(B, Hkv, nrep, N, D).sum(2)
+    tol = 1e-4 if dtype == "f32" else 2e-2
+    for a, b in ((dk_g, dk_sum), (dv_g, dv_sum)):
+        err = (a.float() - b).abs().max() / b.abs().max()
+        assert err <= tol, float(err)
+
+
+def test_gqa_locality():
+    torch, la = gpu_or_skip()
+    B, H, Hkv, N, D = 1, 8, 2, 150, 32
+    t = make(B, H, Hkv, N, D, "f32", seed=9)
+    base_out, base_g = run_gpu(la, t, True, "elu+1")
+    p = dict(t)
+    p["q"] = t["q"].clone()
+    p["q"][0, 5] += 0.25                      # query head 5 -> KV head 5 // 4 = 1
+    out, grads = run_gpu(la, p, True, "elu+1")
+    for h in range(H):
+        if h != 5:
+            assert torch.equal(out[0, h], base_out[0, h])
+            assert torch.equal(grads[0][0, h], base_g[0][0, h])
+    assert torch.equal(grads[1][0, 0], base_g[1][0, 0])   # other KV head untouched
+    assert torch.equal(grads[2][0, 0], base_g[2][0, 0])
+    assert not torch.equal(grads[1][0, 1], base_g[1][0, 1])
+
+
+def test_deterministic():
+    torch, la = gpu_or_skip()
+    t = make(2, 4, 2, 1000, 128, "bf16", scale=0.5, cos=True, seed=3)
+    a_out, a_g = run_gpu(la, t, True, "relu")
+    b_out, b_g = run_gpu(la, t, True, "relu")
+    assert torch.equal(a_out, b_out)
+    for x, y in zip(a_g, b_g):
+        assert torch.equal(x, y)
+
+
+def test_zero_rows_relu_exact():
+    """relu rows whose q is all <= 0 give exactly zero output and dq."""
+    torch, la = gpu_or_skip()
+    t = make(1, 2, 2, 100, 64, "f32", seed=5)
+    t["q"][:, :, ::7] = -t["q"][:, :, ::7].abs()
+    out, (dq, _, _) = run_gpu(la, t, True, "relu")
+    assert torch.count_nonzero(out[:, :, ::7]) == 0
+    assert torch.count_nonzero(dq[:, :, ::7]) == 0
+
+
+def test_binding_errors_on_gpu():
+    torch, la = gpu_or_skip()
+    q = torch.zeros(1, 3, 16, 32, device="cuda")
+    k = torch.zeros(1, 2, 16, 32, device="cuda")
+    with pytest.raises(ValueError):
+        la.fwd(q, k, k)                                   # 3 % 2 != 0
+    q = torch.zeros(1, 2, 16, 48, device="cuda")
+    with pytest.raises(ValueError):
+        la.fwd(q, q, q)                                   # D = 48 unsupported
+    q = torch.zeros(1, 2, 16, 32, device="cuda", dtype=torch.float16)
+    with pytest.raises(ValueError):
+        la.fwd(q, q, q)                                   # fp16 storage not served
+    q = torch.zeros(1, 2, 16, 32, device="cuda")
+    with pytest.raises(ValueError):
+        la.fwd(q, q, q, cos_weight=torch.ones(16, device="cuda"))
