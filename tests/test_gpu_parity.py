@@ -66,9 +66,12 @@ def test_edge_lengths(N, causal):
     torch, la = gpu_or_skip()
     for dtype, D, cos in (("f32", 64, False), ("bf16", 128, True)):
         t = make(1, 2, 1, N, D, dtype, scale=0.5, cos=cos, seed=N)
-        say("edge N=%d %s D=%d cos=%s causal=%s" % (N, dtype, D, cos, causal))
-        ref = oracle_on(t, causal, "elu+1")
-        out, grads = run_gpu(la, t, causal, "elu+1")
+        # with one row and a tiny eps, out = v exactly up to eps and dq, dk are
+        # O(eps): a normwise comparison would measure rounding noise only
+        eps = 0.5 if N == 1 else 1e-6
+        say("edge N=%d %s D=%d cos=%s causal=%s eps=%g" % (N, dtype, D, cos, causal, eps))
+        ref = oracle_on(t, causal, "elu+1", eps)
+        out, grads = run_gpu(la, t, causal, "elu+1", eps)
         compare(t, out, grads, ref[0], ref[1], dtype, 2, 1, label="N=%d" % N)
 
 
