@@ -92,6 +92,22 @@ la_status check_common(int B, int H, int H_kv, int N, int D, int dtype, int phi,
     return LA_OK;
 }
 
+// The kernels that serve a call decide how the sequence is split: the
+// matrix-core forward runs one workgroup per (batch, KV head, segment), the
+// float32 kernels one per (batch, query head, segment).
+bool uses_mfma_fwd(int op_bwd, int dtype, int causal, int D) {
+    return !op_bwd && la::mfma_fwd_serves(dtype == LA_BF16, causal != 0, D);
+}
+
+la::Plan plan_for(int op_bwd, int B, int H, int H_kv, int N, int D, int dtype, int causal,
+                  int has_cos, int seg_len) {
+    if (uses_mfma_fwd(op_bwd, dtype, causal, D))
+        return la::make_plan(op_bwd, B, H, H_kv, N, D, causal, has_cos, seg_len,
+                             (long long)B * H_kv, 512);
+    return la::make_plan(op_bwd, B, H, H_kv, N, D, causal, has_cos, seg_len, (long long)B * H,
+                         1024);
+}
+
 la::Args make_args(const la::Plan &p, int B, int H, int H_kv, int N, int D, float eps,
                    const float *cw, const float *sw, void *ws) {
     la::Args a{};
@@ -133,7 +149,7 @@ size_t la_workspace_bytes_ex(int op, int B, int H, int H_kv, int N, int D, int d
     if (op != LA_OP_FWD && op != LA_OP_BWD) return 0;
     if (check_shape(B, H, H_kv, N, D, dtype, LA_PHI_ELU1) != LA_OK) return 0;
     if (seg_len < 0) return 0;
-    return la::make_plan(op == LA_OP_BWD, B, H, H_kv, N, D, causal, has_cos != 0, seg_len).bytes;
+    return plan_for(op == LA_OP_BWD, B, H, H_kv, N, D, dtype, causal, has_cos != 0, seg_len).bytes;
 }
 
 size_t la_workspace_bytes(int op, int B, int H, int H_kv, int N, int D, int dtype, int causal,
@@ -152,7 +168,7 @@ la_status la_fwd_ex(const void *q, const void *k, const void *v, void *out, int 
     if (seg_len < 0) return fail(LA_ERR_INVALID, "seg_len must be >= 0");
     la_status st = check_shape(B, H, H_kv, N, D, dtype, phi);
     if (st != LA_OK) return st;
-    const la::Plan p = la::make_plan(0, B, H, H_kv, N, D, causal, cos_w != nullptr, seg_len);
+    const la::Plan p = plan_for(0, B, H, H_kv, N, D, dtype, causal, cos_w != nullptr, seg_len);
     st = check_common(B, H, H_kv, N, D, dtype, phi, eps, cos_w, sin_w, ws, ws_bytes, p.bytes);
     if (st != LA_OK) return st;
     la::Args a = make_args(p, B, H, H_kv, N, D, eps, cos_w, sin_w, ws);
@@ -161,6 +177,7 @@ la_status la_fwd_ex(const void *q, const void *k, const void *v, void *out, int 
     a.v = v;
     a.out = out;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (uses_mfma_fwd(0, dtype, causal, D)) return launch_status(la::mfma_fwd_run(a, phi, s));
     return launch_status(la::generic_run(a, dtype == LA_BF16, 0, causal != 0, phi, s));
 }
 
@@ -184,7 +201,7 @@ la_status la_bwd_ex(const void *q, const void *k, const void *v, const void *gra
     if (seg_len < 0) return fail(LA_ERR_INVALID, "seg_len must be >= 0");
     la_status st = check_shape(B, H, H_kv, N, D, dtype, phi);
     if (st != LA_OK) return st;
-    const la::Plan p = la::make_plan(1, B, H, H_kv, N, D, causal, cos_w != nullptr, seg_len);
+    const la::Plan p = plan_for(1, B, H, H_kv, N, D, dtype, causal, cos_w != nullptr, seg_len);
     st = check_common(B, H, H_kv, N, D, dtype, phi, eps, cos_w, sin_w, ws, ws_bytes, p.bytes);
     if (st != LA_OK) return st;
     la::Args a = make_args(p, B, H, H_kv, N, D, eps, cos_w, sin_w, ws);

@@ -94,11 +94,11 @@ constexpr int kSegAlign = 64;   // every chunk length divides this
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Segment count: enough (batch, head, segment) work items to give every one
-// of the 256 compute units several workgroups, but never segments shorter
-// than 4 * kSegAlign rows (the state record would outweigh the rows).
+// Segment count: about `target` workgroups over the `units` independent
+// sequences (each workgroup runs one segment of one unit), but never segments
+// shorter than 4 * kSegAlign rows (the state record would outweigh the rows).
 inline Plan make_plan(int op_bwd, int B, int H, int Hkv, int N, int D, int causal,
-                      int has_cos, int seg_len) {
+                      int has_cos, int seg_len, long long units, long long target) {
     Plan p{};
     p.F = has_cos ? 2 * D : D;
     p.SD = (size_t)p.F * D + p.F;
@@ -106,9 +106,7 @@ inline Plan make_plan(int op_bwd, int B, int H, int Hkv, int N, int D, int causa
     if (seg_len > 0) {
         L = (int)align_up((size_t)seg_len, kSegAlign);
     } else {
-        const long long target = 1024;
-        long long heads = (long long)B * H;
-        long long nseg = (target + heads - 1) / heads;
+        long long nseg = (target + units - 1) / units;
         L = (int)align_up((size_t)((N + nseg - 1) / nseg), kSegAlign);
         if (L < 4 * kSegAlign) L = 4 * kSegAlign;
     }

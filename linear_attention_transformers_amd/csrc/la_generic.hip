@@ -790,6 +790,12 @@ hipError_t by_shape(const Args &a, int bwd, int causal, int phi, hipStream_t s) 
 
 }  // namespace
 
+hipError_t scan_state(float *ws, int nseg, size_t SD, unsigned n_units, hipStream_t s) {
+    hipLaunchKernelGGL(k_scan_S, dim3((unsigned)((SD + kNT - 1) / kNT), n_units), dim3(kNT), 0, s,
+                       ws, nseg, SD, (size_t)n_units);
+    return hipGetLastError();
+}
+
 hipError_t generic_run(const Args &a, int bf16, int bwd, int causal, int phi, hipStream_t s) {
     return bf16 ? by_shape<bf16_t>(a, bwd, causal, phi, s) : by_shape<float>(a, bwd, causal, phi, s);
 }

@@ -10,4 +10,12 @@ namespace la {
 // Float32 vector-ALU path: every dtype / D / mode / feature map.
 hipError_t generic_run(const Args &a, int bf16, int bwd, int causal, int phi, hipStream_t s);
 
+// In-place exclusive prefix over segments of per-segment state records
+// ([n_units][nseg + 1][SD] floats; slot nseg receives the total).
+hipError_t scan_state(float *ws, int nseg, size_t SD, unsigned n_units, hipStream_t s);
+
+// bf16 matrix-core causal forward (one workgroup per batch, KV head, segment).
+bool mfma_fwd_serves(int bf16, int causal, int D);
+hipError_t mfma_fwd_run(const Args &a, int phi, hipStream_t s);
+
 }  // namespace la

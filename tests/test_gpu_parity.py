@@ -204,3 +204,25 @@ def test_binding_errors_on_gpu():
     q = torch.zeros(1, 2, 16, 32, device="cuda")
     with pytest.raises(ValueError):
         la.fwd(q, q, q, cos_weight=torch.ones(16, device="cuda"))
+
+
+def test_kernel_family_per_case():
+    """bf16 causal forward runs on the matrix-core kernels; float32 on the
+    vector-ALU kernels (checked through the library's launch timing)."""
+    torch, la = gpu_or_skip()
+    t = make(1, 4, 2, 256, 128, "bf16", scale=0.5, seed=1)
+    la.timing_enable(True)
+    try:
+        run_gpu(la, t, True, "elu+1", backward=False)
+        names = set(la.timing_collect())
+    finally:
+        la.timing_enable(False)
+    assert "k_fwd_mfma" in names and "k_state_mfma" in names, names
+    t = make(1, 4, 2, 256, 128, "f32", seed=1)
+    la.timing_enable(True)
+    try:
+        run_gpu(la, t, True, "elu+1", backward=False)
+        names = set(la.timing_collect())
+    finally:
+        la.timing_enable(False)
+    assert "k_fwd_causal" in names, names
