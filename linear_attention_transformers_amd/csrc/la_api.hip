@@ -95,13 +95,14 @@ la_status check_common(int B, int H, int H_kv, int N, int D, int dtype, int phi,
 // The kernels that serve a call decide how the sequence is split: the
 // matrix-core forward runs one workgroup per (batch, KV head, segment), the
 // float32 kernels one per (batch, query head, segment).
-bool uses_mfma_fwd(int op_bwd, int dtype, int causal, int D) {
-    return !op_bwd && la::mfma_fwd_serves(dtype == LA_BF16, causal != 0, D);
+bool uses_mfma(int op_bwd, int dtype, int causal, int D, int has_cos) {
+    if (op_bwd) return la::mfma_bwd_serves(dtype == LA_BF16, causal != 0, D, has_cos != 0);
+    return la::mfma_fwd_serves(dtype == LA_BF16, causal != 0, D);
 }
 
 la::Plan plan_for(int op_bwd, int B, int H, int H_kv, int N, int D, int dtype, int causal,
                   int has_cos, int seg_len) {
-    if (uses_mfma_fwd(op_bwd, dtype, causal, D))
+    if (uses_mfma(op_bwd, dtype, causal, D, has_cos))
         return la::make_plan(op_bwd, B, H, H_kv, N, D, causal, has_cos, seg_len,
                              (long long)B * H_kv, 512);
     return la::make_plan(op_bwd, B, H, H_kv, N, D, causal, has_cos, seg_len, (long long)B * H,
@@ -177,7 +178,8 @@ la_status la_fwd_ex(const void *q, const void *k, const void *v, void *out, int 
     a.v = v;
     a.out = out;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (uses_mfma_fwd(0, dtype, causal, D)) return launch_status(la::mfma_fwd_run(a, phi, s));
+    if (uses_mfma(0, dtype, causal, D, cos_w != nullptr))
+        return launch_status(la::mfma_fwd_run(a, phi, s));
     return launch_status(la::generic_run(a, dtype == LA_BF16, 0, causal != 0, phi, s));
 }
 
@@ -213,6 +215,8 @@ la_status la_bwd_ex(const void *q, const void *k, const void *v, const void *gra
     a.dk = dk;
     a.dv = dv;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (uses_mfma(1, dtype, causal, D, cos_w != nullptr))
+        return launch_status(la::mfma_bwd_run(a, phi, s));
     return launch_status(la::generic_run(a, dtype == LA_BF16, 1, causal != 0, phi, s));
 }
 

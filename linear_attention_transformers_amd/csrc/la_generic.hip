@@ -796,6 +796,13 @@ hipError_t scan_state(float *ws, int nseg, size_t SD, unsigned n_units, hipStrea
     return hipGetLastError();
 }
 
+hipError_t scan_suffix(const float *Rp, float *Rs, int nseg, size_t SD, int H, int Hkv, int nrep,
+                       unsigned n_units, hipStream_t s) {
+    hipLaunchKernelGGL(k_scan_R, dim3((unsigned)((SD + kNT - 1) / kNT), n_units), dim3(kNT), 0, s,
+                       Rp, Rs, nseg, SD, H, Hkv, nrep, (size_t)n_units);
+    return hipGetLastError();
+}
+
 hipError_t generic_run(const Args &a, int bf16, int bwd, int causal, int phi, hipStream_t s) {
     return bf16 ? by_shape<bf16_t>(a, bwd, causal, phi, s) : by_shape<float>(a, bwd, causal, phi, s);
 }

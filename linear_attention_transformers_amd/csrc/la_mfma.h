@@ -21,6 +21,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "la_common.h"
+
 namespace la {
 namespace mf {
 
@@ -71,6 +73,69 @@ __device__ __forceinline__ bf16x8 acc_op(const f32x16 &acc, int s) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (__bf16)acc[8 * s + e];
     return o;
+}
+
+constexpr int kC = 64;   // chunk length (rows)
+
+// phi for values that are rounded to bf16 right after: the hardware exp
+// (__expf, a few ulp) is far below bf16 resolution.
+template <int PHI>
+__device__ __forceinline__ float phi_fast(float x) {
+    if constexpr (PHI == kElu1) return x > 0.f ? x + 1.f : __expf(x);
+    else return phi_f<PHI>(x);
+}
+
+__device__ __forceinline__ float bf2f(u16 x) { return __uint_as_float((uint32_t)x << 16); }
+
+__device__ __forceinline__ u16 f2bf(float x) {
+    const __bf16 b = (__bf16)x;
+    return __builtin_bit_cast(u16, b);
+}
+
+// Stage rows [c0, c0 + kC) of one head's [N][D] bf16 tensor into an LDS tile
+// [kC][LD] (rows >= N are zeros).  FEAT: apply phi, and with COS write
+// [cos_t phi, sin_t phi] (width 2D); otherwise copy.
+template <int D, int LD, int NT, bool FEAT, int PHI, bool COS>
+__device__ __forceinline__ void stage(u16 *dst, const u16 *src, int c0, int N, const float *cw,
+                                      const float *sw) {
+    constexpr int V8 = D / 8;   // 16-byte vectors per row
+    for (int v = threadIdx.x; v < kC * V8; v += NT) {
+        const int r = v / V8, c8 = (v % V8) * 8, t = c0 + r;
+        uint4 raw = make_uint4(0, 0, 0, 0);
+        if (t < N) raw = *reinterpret_cast<const uint4 *>(src + (size_t)t * D + c8);
+        if constexpr (!FEAT) {
+            *reinterpret_cast<uint4 *>(dst + r * LD + c8) = raw;
+        } else {
+            const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[2 * e] = t < N ? phi_fast<PHI>(__uint_as_float(w4[e] << 16)) : 0.f;
+                f[2 * e + 1] = t < N ? phi_fast<PHI>(__uint_as_float(w4[e] & 0xffff0000u)) : 0.f;
+            }
+            const float m0 = COS ? (t < N ? cw[t] : 0.f) : 1.f;
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[e] = (uint32_t)f2bf(m0 * f[2 * e]) | ((uint32_t)f2bf(m0 * f[2 * e + 1]) << 16);
+            *reinterpret_cast<uint4 *>(dst + r * LD + c8) = make_uint4(o[0], o[1], o[2], o[3]);
+            if constexpr (COS) {
+                const float m1 = t < N ? sw[t] : 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o[e] = (uint32_t)f2bf(m1 * f[2 * e]) | ((uint32_t)f2bf(m1 * f[2 * e + 1]) << 16);
+                *reinterpret_cast<uint4 *>(dst + r * LD + D + c8) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+    }
+}
+
+// Lane address for a transposed 4-row read of tile X (row stride LD): rows
+// k0 .. k0+3, this lane's operand index (lane % 32) mapped to columns
+// col0 .. col0+31.
+__device__ __forceinline__ const u16 *tr_addr(const u16 *X, int LD, int k0, int col0) {
+    const int l = threadIdx.x & 63, gi = l >> 4, i16 = l & 15;
+    return X + (k0 + (i16 >> 2)) * LD + col0 + 16 * (gi & 1) + 4 * (i16 & 3);
 }
 
 }  // namespace mf

@@ -31,61 +31,6 @@ namespace {
 
 using namespace mf;
 
-constexpr int kC = 64;   // chunk length (rows)
-
-__device__ __forceinline__ float bf2f(u16 x) { return __uint_as_float((uint32_t)x << 16); }
-
-__device__ __forceinline__ u16 f2bf(float x) {
-    const __bf16 b = (__bf16)x;
-    return __builtin_bit_cast(u16, b);
-}
-
-// Stage rows [c0, c0 + kC) of one head's [N][D] bf16 tensor into an LDS tile
-// [kC][LD] (rows >= N are zeros).  FEAT: apply phi, and with COS write
-// [cos_t phi, sin_t phi] (width 2D); otherwise copy.
-template <int D, int LD, int NT, bool FEAT, int PHI, bool COS>
-__device__ __forceinline__ void stage(u16 *dst, const u16 *src, int c0, int N, const float *cw,
-                                      const float *sw) {
-    constexpr int V8 = D / 8;   // 16-byte vectors per row
-    for (int v = threadIdx.x; v < kC * V8; v += NT) {
-        const int r = v / V8, c8 = (v % V8) * 8, t = c0 + r;
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (t < N) raw = *reinterpret_cast<const uint4 *>(src + (size_t)t * D + c8);
-        if constexpr (!FEAT) {
-            *reinterpret_cast<uint4 *>(dst + r * LD + c8) = raw;
-        } else {
-            const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-            float f[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                f[2 * e] = t < N ? phi_f<PHI>(__uint_as_float(w4[e] << 16)) : 0.f;
-                f[2 * e + 1] = t < N ? phi_f<PHI>(__uint_as_float(w4[e] & 0xffff0000u)) : 0.f;
-            }
-            const float m0 = COS ? (t < N ? cw[t] : 0.f) : 1.f;
-            uint32_t o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                o[e] = (uint32_t)f2bf(m0 * f[2 * e]) | ((uint32_t)f2bf(m0 * f[2 * e + 1]) << 16);
-            *reinterpret_cast<uint4 *>(dst + r * LD + c8) = make_uint4(o[0], o[1], o[2], o[3]);
-            if constexpr (COS) {
-                const float m1 = t < N ? sw[t] : 0.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    o[e] = (uint32_t)f2bf(m1 * f[2 * e]) | ((uint32_t)f2bf(m1 * f[2 * e + 1]) << 16);
-                *reinterpret_cast<uint4 *>(dst + r * LD + D + c8) = make_uint4(o[0], o[1], o[2], o[3]);
-            }
-        }
-    }
-}
-
-// Lane address for a transposed 4-row read of tile X (row stride LD): rows
-// k0 .. k0+3, this lane's operand index (lane % 32) mapped to columns
-// col0 .. col0+31.
-__device__ __forceinline__ const u16 *tr_addr(const u16 *X, int LD, int k0, int col0) {
-    const int l = threadIdx.x & 63, gi = l >> 4, i16 = l & 15;
-    return X + (k0 + (i16 >> 2)) * LD + col0 + 16 * (gi & 1) + 4 * (i16 & 3);
-}
-
 // S[fb] += Phi(K)^T V over the 64 rows of the staged chunk, for this wave's
 // value columns (natural k order: lane half h holds rows 16s + 8h .. +7).
 template <int F, int LDF, int LDV>
@@ -291,34 +236,46 @@ __global__ __launch_bounds__(D * 2) void k_fwd_mfma(Args a) {
 }
 
 template <int D, int F, int PHI, bool COS>
-hipError_t run(const Args &a, hipStream_t s) {
+hipError_t run_state(const Args &a, hipStream_t s) {
     constexpr int NT = D * 2;
     const unsigned n_units = (unsigned)(a.B * a.Hkv);
-    const size_t SD = (size_t)F * D + F;
     {
         TimedLaunch tl("k_state_mfma", s);
         hipLaunchKernelGGL((k_state_mfma<D, F, PHI, COS>), dim3(n_units * a.nseg), dim3(NT), 0, s, a);
     }
-    {
-        TimedLaunch tl("k_scan_S", s);
-        hipError_t e = scan_state(a.ws_S, a.nseg, SD, n_units, s);
-        if (e != hipSuccess) return e;
-    }
+    TimedLaunch tl("k_scan_S", s);
+    return scan_state(a.ws_S, a.nseg, (size_t)F * D + F, n_units, s);
+}
+
+template <int D, int F, int PHI, bool COS>
+hipError_t run(const Args &a, hipStream_t s) {
+    constexpr int NT = D * 2;
+    hipError_t e = run_state<D, F, PHI, COS>(a, s);
+    if (e != hipSuccess) return e;
     {
         TimedLaunch tl("k_fwd_mfma", s);
-        hipLaunchKernelGGL((k_fwd_mfma<D, F, PHI, COS>), dim3(n_units * a.nseg), dim3(NT), 0, s, a);
+        hipLaunchKernelGGL((k_fwd_mfma<D, F, PHI, COS>), dim3((unsigned)(a.B * a.Hkv * a.nseg)),
+                           dim3(NT), 0, s, a);
     }
     return hipGetLastError();
 }
 
 template <int D, bool COS>
-hipError_t by_phi(const Args &a, int phi, hipStream_t s) {
+hipError_t by_phi(const Args &a, int phi, bool state_only, hipStream_t s) {
     constexpr int F = COS ? 2 * D : D;
     switch (phi) {
-        case kElu1: return run<D, F, kElu1, COS>(a, s);
-        case kRelu: return run<D, F, kRelu, COS>(a, s);
-        default: return run<D, F, kIdentity, COS>(a, s);
+        case kElu1: return state_only ? run_state<D, F, kElu1, COS>(a, s) : run<D, F, kElu1, COS>(a, s);
+        case kRelu: return state_only ? run_state<D, F, kRelu, COS>(a, s) : run<D, F, kRelu, COS>(a, s);
+        default:
+            return state_only ? run_state<D, F, kIdentity, COS>(a, s) : run<D, F, kIdentity, COS>(a, s);
     }
+}
+
+hipError_t dispatch(const Args &a, int phi, bool state_only, hipStream_t s) {
+    const bool cos = a.F == 2 * a.D;
+    if (a.D == 64)
+        return cos ? by_phi<64, true>(a, phi, state_only, s) : by_phi<64, false>(a, phi, state_only, s);
+    return cos ? by_phi<128, true>(a, phi, state_only, s) : by_phi<128, false>(a, phi, state_only, s);
 }
 
 }  // namespace
@@ -327,10 +284,8 @@ bool mfma_fwd_serves(int bf16, int causal, int D) {
     return bf16 && causal && (D == 64 || D == 128);
 }
 
-hipError_t mfma_fwd_run(const Args &a, int phi, hipStream_t s) {
-    const bool cos = a.F == 2 * a.D;
-    if (a.D == 64) return cos ? by_phi<64, true>(a, phi, s) : by_phi<64, false>(a, phi, s);
-    return cos ? by_phi<128, true>(a, phi, s) : by_phi<128, false>(a, phi, s);
-}
+hipError_t mfma_fwd_run(const Args &a, int phi, hipStream_t s) { return dispatch(a, phi, false, s); }
+
+hipError_t mfma_state_run(const Args &a, int phi, hipStream_t s) { return dispatch(a, phi, true, s); }
 
 }  // namespace la
