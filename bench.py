@@ -49,8 +49,13 @@ def kernel_bytes(name, w, s):
         "bwd_kv_causal": 2 * qb + 4 * kvb + 2 * rows,     # q, g, den, c, k, v -> dk, dv
         "bwd_kv_bidir": 4 * kvb,                          # k, v -> dk, dv
     }
+    # matrix-core kernels compute the same parts of the method
+    alias = {"k_state_mfma": "state", "k_fwd_mfma": "fwd_causal", "k_bwd_q_mfma": "bwd_q_causal",
+             "k_bwd_kv_mfma": "bwd_kv_causal"}
+    if name in alias:
+        return table[alias[name]]
     for key, val in table.items():
-        if name.endswith(key) or ("_" + key) in name:
+        if name.endswith(key):
             return val
     return None
 

@@ -15,7 +15,7 @@
 
 #include <vector>
 
-#include "../../include/linattn.h"
+#include "linattn.h"
 #include "la_common.h"
 #include "la_kernels.h"
 #include "la_timing.h"

@@ -67,6 +67,13 @@ __device__ __forceinline__ bf16x8 tr8(const u16 *p_lo, const u16 *p_hi) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
+__device__ __forceinline__ bf16x8 ones8() {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (__bf16)1.0f;
+    return o;
+}
+
 // Registers 8s .. 8s+7 of an accumulator as a bf16 operand (round to nearest even).
 __device__ __forceinline__ bf16x8 acc_op(const f32x16 &acc, int s) {
     bf16x8 o;
@@ -129,6 +136,81 @@ __device__ __forceinline__ void stage(u16 *dst, const u16 *src, int c0, int N, c
         }
     }
 }
+
+// Rows [c0, c0 + C) of one head's [N][D] bf16 tensor held in registers as
+// 16-byte vectors (rows >= N read as zeros), so the global loads of the next
+// chunk can be in flight while the current one is computed.  Vector k of
+// thread t is element-row (t + k*NT) / (D/8), columns 8*((t + k*NT) % (D/8)).
+template <int D, int NT, int C = kC>
+struct RawTile {
+    static constexpr int V8 = D / 8;
+    static constexpr int NV = C * V8 / NT;
+    static_assert(NV * NT == C * V8, "tile must split evenly over the threads");
+    uint4 v[NV];
+
+    __device__ __forceinline__ void load(const u16 *src, int c0, int N) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int idx = threadIdx.x + k * NT, r = idx / V8, c8 = (idx % V8) * 8;
+            v[k] = make_uint4(0, 0, 0, 0);
+            if (c0 + r < N) v[k] = *reinterpret_cast<const uint4 *>(src + (size_t)(c0 + r) * D + c8);
+        }
+    }
+
+    __device__ __forceinline__ void store(u16 *dst, int LD) const {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int idx = threadIdx.x + k * NT, r = idx / V8, c8 = (idx % V8) * 8;
+            *reinterpret_cast<uint4 *>(dst + r * LD + c8) = v[k];
+        }
+    }
+
+    // Features: phi, then with COS [cos_t phi, sin_t phi] (row width 2D),
+    // rounded to bf16.  With sz != nullptr, also sQZ[r] = Phi(x_r) . z over
+    // the rounded features (fixed-order shuffle reduction across the V8
+    // threads of a row).
+    template <int PHI, bool COS>
+    __device__ __forceinline__ void store_feat(u16 *dst, int LD, int c0, int N, const float *cw,
+                                               const float *sw, const float *sz,
+                                               float *sQZ) const {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int idx = threadIdx.x + k * NT, r = idx / V8, c8 = (idx % V8) * 8, t = c0 + r;
+            const uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[2 * e] = t < N ? phi_fast<PHI>(__uint_as_float(w4[e] << 16)) : 0.f;
+                f[2 * e + 1] = t < N ? phi_fast<PHI>(__uint_as_float(w4[e] & 0xffff0000u)) : 0.f;
+            }
+            const float m0 = COS ? (t < N ? cw[t] : 0.f) : 1.f;
+            float qz = 0.f;
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const u16 lo = f2bf(m0 * f[2 * e]), hi = f2bf(m0 * f[2 * e + 1]);
+                o[e] = (uint32_t)lo | ((uint32_t)hi << 16);
+                if (sz) qz += bf2f(lo) * sz[c8 + 2 * e] + bf2f(hi) * sz[c8 + 2 * e + 1];
+            }
+            *reinterpret_cast<uint4 *>(dst + r * LD + c8) = make_uint4(o[0], o[1], o[2], o[3]);
+            if constexpr (COS) {
+                const float m1 = t < N ? sw[t] : 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const u16 lo = f2bf(m1 * f[2 * e]), hi = f2bf(m1 * f[2 * e + 1]);
+                    o[e] = (uint32_t)lo | ((uint32_t)hi << 16);
+                    if (sz) qz += bf2f(lo) * sz[D + c8 + 2 * e] + bf2f(hi) * sz[D + c8 + 2 * e + 1];
+                }
+                *reinterpret_cast<uint4 *>(dst + r * LD + D + c8) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+            if (sz) {
+#pragma unroll
+                for (int o2 = 1; o2 < V8; o2 <<= 1) qz += __shfl_xor(qz, o2);
+                if (idx % V8 == 0) sQZ[r] = qz;
+            }
+        }
+    }
+};
 
 // Lane address for a transposed 4-row read of tile X (row stride LD): rows
 // k0 .. k0+3, this lane's operand index (lane % 32) mapped to columns

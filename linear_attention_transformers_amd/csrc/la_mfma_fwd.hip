@@ -51,7 +51,8 @@ __device__ __forceinline__ void state_update(f32x16 *S, const u16 *sK, const u16
 // ---------------------------------------------------------------------------
 // k_state_mfma: per (batch, KV head, segment) the segment sums
 // dS = sum_j Phi(k_j) v_j^T (F x D) and dz = sum_j Phi(k_j), written as fp32
-// to the workspace record of the segment.
+// to the workspace record of the segment.  The next chunk's loads are issued
+// before the current chunk's products.
 // ---------------------------------------------------------------------------
 template <int D, int F, int PHI, bool COS>
 __global__ __launch_bounds__(D * 2) void k_state_mfma(Args a) {
@@ -67,11 +68,18 @@ __global__ __launch_bounds__(D * 2) void k_state_mfma(Args a) {
     for (int fb = 0; fb < FB; ++fb) S[fb] = zero16();
     float z = 0.f;
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
+    RawTile<D, NT> rK, rV;
+    rK.load(kh, row0, a.N);
+    rV.load(vh, row0, a.N);
     for (int c0 = row0; c0 < row1; c0 += kC) {
         __syncthreads();
-        stage<D, LDF, NT, true, PHI, COS>(sK, kh, c0, a.N, a.cw, a.sw);
-        stage<D, LDV, NT, false, PHI, COS>(sV, vh, c0, a.N, a.cw, a.sw);
+        rK.template store_feat<PHI, COS>(sK, LDF, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rV.store(sV, LDV);
         __syncthreads();
+        if (c0 + kC < row1) {
+            rK.load(kh, c0 + kC, a.N);
+            rV.load(vh, c0 + kC, a.N);
+        }
         state_update<F, LDF, LDV>(S, sK, sV, w);
         if (t < F)
             for (int j = 0; j < kC; ++j) z += bf2f(sK[j * LDF + t]);
@@ -87,27 +95,54 @@ __global__ __launch_bounds__(D * 2) void k_state_mfma(Args a) {
     if (t < F) out[(size_t)F * D + t] = z;
 }
 
+// Store one 32-query block of out: lane holds query row `row` and value
+// columns 32w + 8q + 4h + 0..3 (q = 0..3) of the num^T accumulator.
+template <int D>
+__device__ __forceinline__ void store_out(u16 *oh, const f32x16 &Nt, int row, int N, float inv,
+                                          int w, int h) {
+    if (row >= N) return;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+        const uint32_t lo = (uint32_t)f2bf(Nt[4 * q4] * inv) | ((uint32_t)f2bf(Nt[4 * q4 + 1] * inv) << 16);
+        const uint32_t hi =
+            (uint32_t)f2bf(Nt[4 * q4 + 2] * inv) | ((uint32_t)f2bf(Nt[4 * q4 + 3] * inv) << 16);
+        *reinterpret_cast<uint2 *>(oh + (size_t)row * D + 32 * w + 8 * q4 + 4 * h) = make_uint2(lo, hi);
+    }
+}
+
+constexpr int kCf = 32;   // forward chunk length: one 32x32 tile of A per head
+
 // ---------------------------------------------------------------------------
 // k_fwd_mfma: per (batch, KV head, segment): the chunk loop for all n_rep
 // query heads of the KV head, from the segment's exclusive prefix state.
+// Chunks of 32 rows keep the working set small enough for two workgroups per
+// compute unit; the global loads of the next head / chunk are issued as soon
+// as the current tiles are in LDS.  z is carried on the matrix cores too
+// (z += Phi(K)^T 1, in fp32 accumulators; wave w owns feature blocks
+// w, w + D/32, ...) and mirrored to LDS for the Phi(q).z dot of the staging.
 // ---------------------------------------------------------------------------
 template <int D, int F, int PHI, bool COS>
-__global__ __launch_bounds__(D * 2) void k_fwd_mfma(Args a) {
-    constexpr int NT = D * 2, LDF = F + 8, LDV = D + 8, FB = F / 32;
-    __shared__ __attribute__((aligned(16))) u16 sK[kC * LDF];
-    __shared__ __attribute__((aligned(16))) u16 sQ[kC * LDF];
-    __shared__ __attribute__((aligned(16))) u16 sV[kC * LDV];
-    __shared__ float sz[F];
+__global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 ? 2 : 1))) void k_fwd_mfma(Args a) {
+    constexpr int NT = D * 2, NW = D / 32, LDF = F + 8, LDV = D + 8, FB = F / 32, ZB = FB / NW;
+    __shared__ __attribute__((aligned(16))) u16 sK[kCf * LDF];
+    __shared__ __attribute__((aligned(16))) u16 sQ[kCf * LDF];
+    __shared__ __attribute__((aligned(16))) u16 sV[kCf * LDV];
+    __shared__ __attribute__((aligned(16))) float sz[F];
+    __shared__ float sQZ[kCf];
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int t = threadIdx.x, l = t & 63, w = t >> 6, h = l >> 5, l32 = l & 31;
     const size_t SD = (size_t)F * D + F;
     const u16 *kh = static_cast<const u16 *>(a.k) + (size_t)bg * a.N * D;
     const u16 *vh = static_cast<const u16 *>(a.v) + (size_t)bg * a.N * D;
+    const size_t bh0 = (size_t)b * a.H + (size_t)g * a.nrep;
+    const u16 *qbase = static_cast<const u16 *>(a.q);
+    u16 *obase = static_cast<u16 *>(a.out);
 
-    // exclusive prefix state of this segment
+    // exclusive prefix state of this segment: S (F/32 tiles of this wave's
+    // value block) and this wave's blocks of z (every column of a z tile holds z)
     const float *Sp = a.ws_S + ((size_t)bg * (a.nseg + 1) + seg) * SD;
-    f32x16 S[FB];
+    f32x16 S[FB], Z[ZB];
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
@@ -115,122 +150,90 @@ __global__ __launch_bounds__(D * 2) void k_fwd_mfma(Args a) {
             const int f = 32 * fb + 8 * (r >> 2) + 4 * h + (r & 3);
             S[fb][r] = Sp[(size_t)f * D + 32 * w + l32];
         }
+#pragma unroll
+    for (int c = 0; c < ZB; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            Z[c][r] = Sp[(size_t)F * D + 32 * (w + NW * c) + 8 * (r >> 2) + 4 * h + (r & 3)];
     for (int e = t; e < F; e += NT) sz[e] = Sp[(size_t)F * D + e];
+    const bf16x8 one = ones8();
 
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
-    for (int c0 = row0; c0 < row1; c0 += kC) {
-        __syncthreads();   // previous chunk: sK, sV, sQ reads and the z update done
-        stage<D, LDF, NT, true, PHI, COS>(sK, kh, c0, a.N, a.cw, a.sw);
-        stage<D, LDV, NT, false, PHI, COS>(sV, vh, c0, a.N, a.cw, a.sw);
+    RawTile<D, NT, kCf> rK, rV, rQ;
+    rK.load(kh, row0, a.N);
+    rV.load(vh, row0, a.N);
+    rQ.load(qbase + bh0 * a.N * D, row0, a.N);
+    for (int c0 = row0; c0 < row1; c0 += kCf) {
+        __syncthreads();   // previous chunk: every LDS read done, sz updated
+        rK.template store_feat<PHI, COS>(sK, LDF, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rV.store(sV, LDV);
         for (int rep = 0; rep < a.nrep; ++rep) {
-            const size_t bh = (size_t)b * a.H + (size_t)g * a.nrep + rep;
-            const u16 *qh = static_cast<const u16 *>(a.q) + bh * a.N * D;
-            u16 *oh = static_cast<u16 *>(a.out) + bh * a.N * D;
+            u16 *oh = obase + (bh0 + rep) * a.N * D;
             if (rep > 0) __syncthreads();   // every wave is done with the previous head's sQ
-            stage<D, LDF, NT, true, PHI, COS>(sQ, qh, c0, a.N, a.cw, a.sw);
+            rQ.template store_feat<PHI, COS>(sQ, LDF, c0, a.N, a.cw, a.sw, sz, sQZ);
             __syncthreads();
-
-            // A^T tiles (keys x queries): T00 = (j 0-31, i 0-31), T01 = (j 0-31,
-            // i 32-63), T11 = (j 32-63, i 32-63); (j 32-63, i 0-31) is masked out.
-            f32x16 T00 = zero16(), T01 = zero16(), T11 = zero16();
-#pragma unroll 4
-            for (int s = 0; s < F / 16; ++s) {
-                const int k = 16 * s + 8 * h;
-                const bf16x8 k0 = ld8(sK + l32 * LDF + k);
-                const bf16x8 k1 = ld8(sK + (32 + l32) * LDF + k);
-                const bf16x8 q0 = ld8(sQ + l32 * LDF + k);
-                const bf16x8 q1 = ld8(sQ + (32 + l32) * LDF + k);
-                T00 = mfma(k0, q0, T00);
-                T01 = mfma(k0, q1, T01);
-                T11 = mfma(k1, q1, T11);
+            if (rep + 1 < a.nrep) {
+                rQ.load(qbase + (bh0 + rep + 1) * a.N * D, c0, a.N);
+            } else if (c0 + kCf < row1) {
+                rK.load(kh, c0 + kCf, a.N);
+                rV.load(vh, c0 + kCf, a.N);
+                rQ.load(qbase + bh0 * a.N * D, c0 + kCf, a.N);
             }
-            // causal mask on the diagonal tiles, bf16 rounding (the values the
-            // A V product consumes) and the intra-chunk denominators
-            float d0 = 0.f, d1 = 0.f;
+
+            // A^T (keys x queries) of the chunk, causal mask, bf16 rounding (the
+            // values the A V product consumes) and the in-chunk denominators
+            f32x16 T = zero16();
+#pragma unroll 4
+            for (int s = 0; s < F / 16; ++s)
+                T = mfma(ld8(sK + l32 * LDF + 16 * s + 8 * h), ld8(sQ + l32 * LDF + 16 * s + 8 * h), T);
+            float dsum = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int j = 8 * (r >> 2) + 4 * h + (r & 3);
-                const float x00 = (__bf16)(j <= l32 ? T00[r] : 0.f);
-                const float x11 = (__bf16)(j <= l32 ? T11[r] : 0.f);
-                const float x01 = (__bf16)T01[r];
-                T00[r] = x00;
-                T11[r] = x11;
-                T01[r] = x01;
-                d0 += x00;
-                d1 += x01 + x11;
+                const float x = (__bf16)(j <= l32 ? T[r] : 0.f);
+                T[r] = x;
+                dsum += x;
             }
-            d0 += __shfl_xor(d0, 32);
-            d1 += __shfl_xor(d1, 32);
-            // Phi(q_i) . z for i = l32 and 32 + l32, the two lane halves splitting F
-            float qz0 = 0.f, qz1 = 0.f;
-#pragma unroll 2
-            for (int f = h * (F / 2); f < (h + 1) * (F / 2); f += 8) {
-                const bf16x8 x0 = ld8(sQ + l32 * LDF + f);
-                const bf16x8 x1 = ld8(sQ + (32 + l32) * LDF + f);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float zf = sz[f + e];
-                    qz0 += (float)x0[e] * zf;
-                    qz1 += (float)x1[e] * zf;
-                }
-            }
-            qz0 += __shfl_xor(qz0, 32);
-            qz1 += __shfl_xor(qz1, 32);
-            const float den0 = d0 + qz0 + a.eps, den1 = d1 + qz1 + a.eps;
+            dsum += __shfl_xor(dsum, 32);
+            const bf16x8 B0 = acc_op(T, 0), B1 = acc_op(T, 1);
 
-            // num^T for this wave's value columns: N0 (queries 0-31), N1 (32-63)
-            f32x16 N0 = zero16(), N1 = zero16();
+            // num^T for this wave's value columns: V^T A^T + S^T Phi(Q)^T
+            f32x16 Nt = zero16();
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {   // keys 0-31
+            for (int s = 0; s < 2; ++s) {
                 const int k0 = 16 * s + 4 * h;
                 const bf16x8 va = tr8(tr_addr(sV, LDV, k0, 32 * w), tr_addr(sV, LDV, k0 + 8, 32 * w));
-                N0 = mfma(va, acc_op(T00, s), N0);
-                N1 = mfma(va, acc_op(T01, s), N1);
+                Nt = mfma(va, s ? B1 : B0, Nt);
             }
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {   // keys 32-63
-                const int k0 = 32 + 16 * s + 4 * h;
-                const bf16x8 va = tr8(tr_addr(sV, LDV, k0, 32 * w), tr_addr(sV, LDV, k0 + 8, 32 * w));
-                N1 = mfma(va, acc_op(T11, s), N1);
-            }
-            // inter-chunk term: num^T += S^T Phi(Q)^T (S rounded to bf16)
+            const u16 *qrow = sQ + l32 * LDF;
 #pragma unroll
             for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const bf16x8 sa = acc_op(S[fb], s);
-                    const int f0 = 32 * fb + 16 * s + 4 * h;
-                    N0 = mfma(sa, ld4x2(sQ + l32 * LDF + f0), N0);
-                    N1 = mfma(sa, ld4x2(sQ + (32 + l32) * LDF + f0), N1);
-                }
-            // out[i][d] = num / den; lane holds query i (= l32 or 32 + l32) and
-            // value columns 32w + 8q + 4h + 0..3, q = 0..3
-            const float inv0 = 1.f / den0, inv1 = 1.f / den1;
+                for (int s = 0; s < 2; ++s)
+                    Nt = mfma(acc_op(S[fb], s), ld4x2(qrow + 32 * fb + 16 * s + 4 * h), Nt);
+            const float den = dsum + sQZ[l32] + a.eps;
+            store_out<D>(oh, Nt, c0 + l32, a.N, 1.f / den, w, h);
+        }
+        // carry (S, z) past this chunk: S += Phi(K)^T V, z += Phi(K)^T 1
 #pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const int row = c0 + 32 * ib + l32;
-                if (row < a.N) {
-                    const f32x16 &Nt = ib ? N1 : N0;
-                    const float inv = ib ? inv1 : inv0;
+        for (int s = 0; s < kCf / 16; ++s) {
+            const int k0 = 16 * s + 8 * h;
+            const bf16x8 vb = tr8(tr_addr(sV, LDV, k0, 32 * w), tr_addr(sV, LDV, k0 + 4, 32 * w));
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const uint32_t lo = (uint32_t)f2bf(Nt[4 * q4] * inv) |
-                                            ((uint32_t)f2bf(Nt[4 * q4 + 1] * inv) << 16);
-                        const uint32_t hi = (uint32_t)f2bf(Nt[4 * q4 + 2] * inv) |
-                                            ((uint32_t)f2bf(Nt[4 * q4 + 3] * inv) << 16);
-                        *reinterpret_cast<uint2 *>(oh + (size_t)row * D + 32 * w + 8 * q4 + 4 * h) =
-                            make_uint2(lo, hi);
-                    }
-                }
+            for (int fb = 0; fb < FB; ++fb) {
+                const bf16x8 ka = tr8(tr_addr(sK, LDF, k0, 32 * fb), tr_addr(sK, LDF, k0 + 4, 32 * fb));
+                S[fb] = mfma(ka, vb, S[fb]);
+                if (fb % NW == w) Z[fb / NW] = mfma(ka, one, Z[fb / NW]);
             }
         }
-        // carry the state past this chunk
-        state_update<F, LDF, LDV>(S, sK, sV, w);
-        __syncthreads();   // all heads have read z
-        if (t < F) {
-            float acc = 0.f;
-            for (int j = 0; j < kC; ++j) acc += bf2f(sK[j * LDF + t]);
-            sz[t] += acc;
+        // every head's staging has read sz (they all passed the barrier before
+        // their products), so it can take the new z now
+        if (l32 == 0) {
+#pragma unroll
+            for (int c = 0; c < ZB; ++c)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    sz[32 * (w + NW * c) + 8 * (r >> 2) + 4 * h + (r & 3)] = Z[c][r];
         }
     }
 }
