@@ -4,7 +4,7 @@
 // The gradient is the exact derivative of the forward (SVD_linear_Attention,
 // "Module neuralops.core.triton_kernels.linear_attn", function bwd: autograd
 // of fwd with respect to q, k, v).  With g_i = dL/dout_i, gn_i = g_i / den_i,
-// c_i = (g_i . out_i) / den_i, and per chunk (C = 64 rows, j <= i masked):
+// c_i = (g_i . out_i) / den_i, and per chunk (C = 32 rows, j <= i masked):
 //   A_ij = Phi(q_i).Phi(k_j),  T_ij = g_i.v_j,  U_i = S g_i  (S exclusive),
 //   den_i = sum_j A_ij + Phi(q_i).z + eps,
 //   c_i   = (sum_j A_ij T_ij + Phi(q_i).U_i) / den_i^2,
@@ -20,12 +20,13 @@
 // c_i and each segment's sum of (R, r); a scan forms the suffixes.
 //
 // Layout of the work: one workgroup per (batch, KV head, segment) serving the
-// n_rep query heads; wave w of the D/32 waves owns feature columns
-// 32w..32w+31 of the states (S^T in the q-kernel, R^T in the kv-kernel) and of
-// dPhi(q), dPhi(k), and value columns 32w..32w+31 of dv.  The three non-zero
-// 32x32 tiles of the chunk's C x C matrices are computed by different waves
-// and exchanged through LDS (bf16), with the column sums the denominators
-// need reduced through LDS in a fixed order.
+// n_rep query heads.  Each wave computes the chunk's 32x32 tile of A and T
+// itself (so no C x C data crosses waves) and owns a 32-wide block of the
+// feature columns of the state (S^T in the q-kernel, R^T in the kv-kernel),
+// of dPhi(q) / dPhi(k), and of the value columns of dv.  The only cross-wave
+// reduction, Phi(q_i).U_i over the feature blocks, goes through LDS in a
+// fixed order.  In the q-kernel a second set of waves accumulates the
+// segment's (R, r) so the two register-heavy states live in different waves.
 #include "la_common.h"
 #include "la_kernels.h"
 #include "la_mfma.h"
@@ -36,52 +37,7 @@ namespace {
 
 using namespace mf;
 
-constexpr int kLDP = kC + 8;   // row stride of the C x C tiles in LDS
-
-// Tile t of the lower block triangle: (key block, query block).
-__device__ __forceinline__ int tile_jb(int t) { return t == 2 ? 1 : 0; }
-__device__ __forceinline__ int tile_ib(int t) { return t == 0 ? 0 : 1; }
-
-// A^T and T^T (keys x queries) of tile t, causal mask applied, A rounded to
-// bf16.  Ks/Vs: key-side tiles, Qs/Gs: query-side tiles.
-template <int F, int D>
-__device__ __forceinline__ void tile_AT(int t, const u16 *sK, const u16 *sQ, const u16 *sV,
-                                        const u16 *sG, f32x16 &At, f32x16 &Tt) {
-    constexpr int LDF = F + 8, LDV = D + 8;
-    const int l = threadIdx.x & 63, h = l >> 5, l32 = l & 31;
-    const int jb = tile_jb(t), ib = tile_ib(t);
-    At = zero16();
-    Tt = zero16();
-#pragma unroll 4
-    for (int s = 0; s < F / 16; ++s)
-        At = mfma(ld8(sK + (32 * jb + l32) * LDF + 16 * s + 8 * h),
-                  ld8(sQ + (32 * ib + l32) * LDF + 16 * s + 8 * h), At);
-#pragma unroll 4
-    for (int s = 0; s < D / 16; ++s)
-        Tt = mfma(ld8(sV + (32 * jb + l32) * LDV + 16 * s + 8 * h),
-                  ld8(sG + (32 * ib + l32) * LDV + 16 * s + 8 * h), Tt);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int j = 8 * (r >> 2) + 4 * h + (r & 3);
-        const bool keep = jb != ib || j <= l32;
-        At[r] = keep ? (float)(__bf16)At[r] : 0.f;
-        Tt[r] = keep ? Tt[r] : 0.f;
-    }
-}
-
-// Store the 32x32 tile (keys x queries accumulator) transposed into a
-// row-major [query][key] LDS matrix, bf16.
-__device__ __forceinline__ void store_tile_qk(u16 *M, int t, const f32x16 &X) {
-    const int l = threadIdx.x & 63, h = l >> 5, l32 = l & 31;
-    const int jb = tile_jb(t), ib = tile_ib(t);
-    u16 *row = M + (32 * ib + l32) * kLDP + 32 * jb + 4 * h;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-        const uint32_t lo = (uint32_t)f2bf(X[4 * q4]) | ((uint32_t)f2bf(X[4 * q4 + 1]) << 16);
-        const uint32_t hi = (uint32_t)f2bf(X[4 * q4 + 2]) | ((uint32_t)f2bf(X[4 * q4 + 3]) << 16);
-        *reinterpret_cast<uint2 *>(row + 8 * q4) = make_uint2(lo, hi);
-    }
-}
+constexpr int kCb = 32;   // backward chunk length: one 32x32 tile per head
 
 // 4 consecutive bf16 of an LDS row as floats.
 __device__ __forceinline__ void ld4f(const u16 *p, float *o) {
@@ -98,265 +54,249 @@ __device__ __forceinline__ void st4bf(u16 *p, const float *x) {
     *reinterpret_cast<uint2 *>(p) = make_uint2(lo, hi);
 }
 
+// Accumulator row index of register r for lane half h.
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
 // ---------------------------------------------------------------------------
-// k_bwd_q_mfma: forward over the chunks of one (batch, KV head, segment).
+// k_bwd_q_mfma: forward over the 32-row chunks of one (batch, KV head,
+// segment).  Waves 0 .. D/32-1 ("state waves") hold S^T and z and produce
+// dq; waves D/32 .. 2D/32-1 ("R waves") accumulate the segment's
+// R = sum_i Phi(q_i) gn_i^T (feature block w - D/32 x all value blocks) and
+// r = sum_i c_i Phi(q_i), summed over the group's query heads.
 // ---------------------------------------------------------------------------
 template <int D, int PHI>
-__global__ __launch_bounds__(D * 2) void k_bwd_q_mfma(Args a) {
-    constexpr int F = D, NW = D / 32, NT = 2 * D, LDF = F + 8, LDV = D + 8;
-    __shared__ __attribute__((aligned(16))) u16 sK[kC * LDF];
-    __shared__ __attribute__((aligned(16))) u16 sV[kC * LDV];
-    __shared__ __attribute__((aligned(16))) u16 sQ[kC * LDF];
-    __shared__ __attribute__((aligned(16))) u16 sG[kC * LDV];
-    __shared__ __attribute__((aligned(16))) u16 sQr[kC * LDV];
-    __shared__ __attribute__((aligned(16))) u16 sP[kC * kLDP];
-    __shared__ float sz[F];
-    __shared__ float sDenP[3][32], sAtP[3][32];
-    __shared__ float sQU[NW][kC];
-    __shared__ float sQZ[kC], sDen[kC], sCc[kC];
+__global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2)))
+void k_bwd_q_mfma(Args a) {
+    constexpr int F = D, NW = D / 32, NT = 4 * D, LDF = F + 8, LDV = D + 8;
+    __shared__ __attribute__((aligned(16))) u16 sK[kCb * LDF];
+    __shared__ __attribute__((aligned(16))) u16 sV[kCb * LDV];
+    __shared__ __attribute__((aligned(16))) u16 sQ[kCb * LDF];
+    __shared__ __attribute__((aligned(16))) u16 sQr[kCb * LDV];
+    __shared__ __attribute__((aligned(16))) u16 sG[kCb * LDV];
+    __shared__ __attribute__((aligned(16))) float sz[F];
+    __shared__ __attribute__((aligned(16))) float sInv[kCb];
+    __shared__ float sQZ[kCb], sCc[kCb], sQU[NW][kCb];
 
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int t = threadIdx.x, l = t & 63, w = t >> 6, h = l >> 5, l32 = l & 31;
+    const bool state_wave = w < NW;
+    const int wr = w - NW;   // feature block of an R wave
     const size_t SD = (size_t)F * D + F;
     const u16 *kh = static_cast<const u16 *>(a.k) + (size_t)bg * a.N * D;
     const u16 *vh = static_cast<const u16 *>(a.v) + (size_t)bg * a.N * D;
+    const size_t bh0 = (size_t)b * a.H + (size_t)g * a.nrep;
+    const u16 *qbase = static_cast<const u16 *>(a.q);
+    const u16 *gbase = static_cast<const u16 *>(a.g);
+    u16 *dqbase = static_cast<u16 *>(a.dq);
 
-    // S^T tiles (value block db x this wave's feature block), fp32
+    // state waves: S^T tiles (value block db x feature block w), z tile (block w)
+    // R waves: R tiles (feature block wr x value block db)
     const float *Sp = a.ws_S + ((size_t)bg * (a.nseg + 1) + seg) * SD;
-    f32x16 St[NW], dR[NW];
+    f32x16 X[NW], Z = zero16();
+    if (state_wave) {
 #pragma unroll
-    for (int db = 0; db < NW; ++db) {
+        for (int db = 0; db < NW; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            St[db][r] = Sp[(size_t)(32 * w + l32) * D + 32 * db + 8 * (r >> 2) + 4 * h + (r & 3)];
-        dR[db] = zero16();
+            for (int r = 0; r < 16; ++r)
+                X[db][r] = Sp[(size_t)(32 * w + l32) * D + 32 * db + acc_row(r, h)];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Z[r] = Sp[(size_t)F * D + 32 * w + acc_row(r, h)];
+    } else {
+#pragma unroll
+        for (int db = 0; db < NW; ++db) X[db] = zero16();
     }
     for (int e = t; e < F; e += NT) sz[e] = Sp[(size_t)F * D + e];
-    float rr = 0.f;
+    float rr = 0.f;   // R waves: thread t - NW*64 < F owns r[feature]
+    const bf16x8 one = ones8();
 
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
-    for (int c0 = row0; c0 < row1; c0 += kC) {
+    RawTile<D, NT, kCb> rK, rV, rQ, rG;
+    rK.load(kh, row0, a.N);
+    rV.load(vh, row0, a.N);
+    rQ.load(qbase + bh0 * a.N * D, row0, a.N);
+    rG.load(gbase + bh0 * a.N * D, row0, a.N);
+    for (int c0 = row0; c0 < row1; c0 += kCb) {
         __syncthreads();
-        stage<D, LDF, NT, true, PHI, false>(sK, kh, c0, a.N, a.cw, a.sw);
-        stage<D, LDV, NT, false, PHI, false>(sV, vh, c0, a.N, a.cw, a.sw);
+        rK.template store_feat<PHI, false>(sK, LDF, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rV.store(sV, LDV);
         for (int rep = 0; rep < a.nrep; ++rep) {
-            const size_t bh = (size_t)b * a.H + (size_t)g * a.nrep + rep;
-            const u16 *qh = static_cast<const u16 *>(a.q) + bh * a.N * D;
-            const u16 *gh = static_cast<const u16 *>(a.g) + bh * a.N * D;
-            u16 *dqh = static_cast<u16 *>(a.dq) + bh * a.N * D;
+            const size_t bh = bh0 + rep;
             if (rep > 0) __syncthreads();
-            stage<D, LDF, NT, true, PHI, false>(sQ, qh, c0, a.N, a.cw, a.sw);
-            stage<D, LDV, NT, false, PHI, false>(sQr, qh, c0, a.N, a.cw, a.sw);
-            stage<D, LDV, NT, false, PHI, false>(sG, gh, c0, a.N, a.cw, a.sw);
+            rQ.template store_feat<PHI, false>(sQ, LDF, c0, a.N, a.cw, a.sw, sz, sQZ);
+            rQ.store(sQr, LDV);
+            rG.store(sG, LDV);
             __syncthreads();
-
-            // tiles of A^T, T^T: tile t on wave t % NW
-            f32x16 At[2], Tt[2];
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int tt = w + k * NW;
-                if (tt < 3) {
-                    tile_AT<F, D>(tt, sK, sQ, sV, sG, At[k], Tt[k]);
-                    float dA = 0.f, aT = 0.f;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        dA += At[k][r];
-                        aT += At[k][r] * Tt[k][r];
-                    }
-                    dA += __shfl_xor(dA, 32);
-                    aT += __shfl_xor(aT, 32);
-                    if (h == 0) {
-                        sDenP[tt][l32] = dA;
-                        sAtP[tt][l32] = aT;
-                    }
-                }
+            if (rep + 1 < a.nrep) {
+                rQ.load(qbase + (bh + 1) * a.N * D, c0, a.N);
+                rG.load(gbase + (bh + 1) * a.N * D, c0, a.N);
+            } else if (c0 + kCb < row1) {
+                rK.load(kh, c0 + kCb, a.N);
+                rV.load(vh, c0 + kCb, a.N);
+                rQ.load(qbase + bh0 * a.N * D, c0 + kCb, a.N);
+                rG.load(gbase + bh0 * a.N * D, c0 + kCb, a.N);
             }
-            // U^T = S g for this wave's feature block, both query blocks
-            f32x16 U0 = zero16(), U1 = zero16();
+            const bool ok = c0 + l32 < a.N;   // this lane's query row exists
+            f32x16 Tt, U;
+            float den = 1.f, aT = 0.f;
+            if (state_wave) {
+                // A^T, T^T (keys x queries), causal mask, A rounded to bf16
+                f32x16 At = zero16();
+                Tt = zero16();
+#pragma unroll 4
+                for (int s = 0; s < F / 16; ++s)
+                    At = mfma(ld8(sK + l32 * LDF + 16 * s + 8 * h), ld8(sQ + l32 * LDF + 16 * s + 8 * h), At);
+#pragma unroll 4
+                for (int s = 0; s < D / 16; ++s)
+                    Tt = mfma(ld8(sV + l32 * LDV + 16 * s + 8 * h), ld8(sG + l32 * LDV + 16 * s + 8 * h), Tt);
+                float dA = 0.f;
 #pragma unroll
-            for (int db = 0; db < NW; ++db)
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const bf16x8 sa = acc_op(St[db], s);
-                    const int d0 = 32 * db + 16 * s + 4 * h;
-                    U0 = mfma(sa, ld4x2(sG + l32 * LDV + d0), U0);
-                    U1 = mfma(sa, ld4x2(sG + (32 + l32) * LDV + d0), U1);
+                for (int r = 0; r < 16; ++r) {
+                    const bool keep = acc_row(r, h) <= l32;
+                    const float x = keep ? (float)(__bf16)At[r] : 0.f;
+                    Tt[r] = keep ? Tt[r] : 0.f;
+                    dA += x;
+                    aT += x * Tt[r];
                 }
-            {   // partial Phi(q_i) . U_i over this wave's features
-                float qu0 = 0.f, qu1 = 0.f, x[4];
+                dA += __shfl_xor(dA, 32);
+                aT += __shfl_xor(aT, 32);
+                den = ok ? dA + sQZ[l32] + a.eps : 1.f;
+                // U^T = S g (this feature block x the chunk's queries)
+                U = zero16();
+#pragma unroll
+                for (int db = 0; db < NW; ++db)
+#pragma unroll
+                    for (int s = 0; s < 2; ++s)
+                        U = mfma(acc_op(X[db], s), ld4x2(sG + l32 * LDV + 32 * db + 16 * s + 4 * h), U);
+                float qu = 0.f, x4[4];
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
-                    const int f0 = 32 * w + 8 * q4 + 4 * h;
-                    ld4f(sQ + l32 * LDF + f0, x);
+                    ld4f(sQ + l32 * LDF + 32 * w + 8 * q4 + 4 * h, x4);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) qu0 += x[e] * U0[4 * q4 + e];
-                    ld4f(sQ + (32 + l32) * LDF + f0, x);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) qu1 += x[e] * U1[4 * q4 + e];
+                    for (int e = 0; e < 4; ++e) qu += x4[e] * U[4 * q4 + e];
                 }
-                qu0 += __shfl_xor(qu0, 32);
-                qu1 += __shfl_xor(qu1, 32);
+                qu += __shfl_xor(qu, 32);
                 if (h == 0) {
-                    sQU[w][l32] = qu0;
-                    sQU[w][32 + l32] = qu1;
+                    sQU[w][l32] = qu;
+                    if (w == 0) sInv[l32] = 1.f / den;
                 }
-            }
-            if (w == NW - 1) {   // Phi(q_i) . z for every row of the chunk
-                float acc = 0.f;
-                for (int f = 0; f < F; f += 8) {
-                    const bf16x8 xq = ld8(sQ + l * LDF + f);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc += (float)xq[e] * sz[f + e];
-                }
-                sQZ[l] = acc;
             }
             __syncthreads();
-
-            // den and c of rows l32 and 32 + l32 (rows past N: neutral)
-            float den[2], cc[2];
+            if (state_wave) {
+                float gsum = aT;
 #pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const int i = 32 * ib + l32;
-                float dsum = ib ? sDenP[1][l32] + sDenP[2][l32] : sDenP[0][l32];
-                float gsum = ib ? sAtP[1][l32] + sAtP[2][l32] : sAtP[0][l32];
-#pragma unroll
-                for (int ww = 0; ww < NW; ++ww) gsum += sQU[ww][i];
-                const bool ok = c0 + i < a.N;
-                den[ib] = ok ? dsum + sQZ[i] + a.eps : 1.f;
-                cc[ib] = ok ? gsum / (den[ib] * den[ib]) : 0.f;
+                for (int ww = 0; ww < NW; ++ww) gsum += sQU[ww][l32];
+                const float inv = 1.f / den;
+                const float c = ok ? gsum * inv * inv : 0.f;
                 if (w == 0 && h == 0) {
-                    sDen[i] = den[ib];
-                    sCc[i] = cc[ib];
+                    sCc[l32] = c;
                     if (ok) {
-                        a.ws_den[bh * a.N + c0 + i] = den[ib];
-                        a.ws_c[bh * a.N + c0 + i] = cc[ib];
+                        a.ws_den[bh * a.N + c0 + l32] = den;
+                        a.ws_c[bh * a.N + c0 + l32] = c;
                     }
                 }
-            }
-            // P tiles into sP as [query][key]
+                // P^T = T^T / den - c (masked), then dPhi(q)^T = Phi(K)^T P^T + U^T / den - z c
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int tt = w + k * NW;
-                if (tt < 3) {
-                    const int ib = tile_ib(tt), jb = tile_jb(tt);
-                    const float inv = 1.f / den[ib], c = cc[ib];
+                for (int r = 0; r < 16; ++r)
+                    Tt[r] = acc_row(r, h) <= l32 ? Tt[r] * inv - c : 0.f;
+                f32x16 Qd = zero16();
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int j = 8 * (r >> 2) + 4 * h + (r & 3);
-                        const bool keep = jb != ib || j <= l32;
-                        Tt[k][r] = keep ? Tt[k][r] * inv - c : 0.f;
-                    }
-                    store_tile_qk(sP, tt, Tt[k]);
+                for (int s = 0; s < 2; ++s) {
+                    const int k0 = 16 * s + 4 * h;
+                    const bf16x8 ka = tr8(tr_addr(sK, LDF, k0, 32 * w), tr_addr(sK, LDF, k0 + 8, 32 * w));
+                    Qd = mfma(ka, acc_op(Tt, s), Qd);
                 }
-            }
-            __syncthreads();
-            // G -> gn = G / den, in place (bf16)
-            for (int v = t; v < kC * D / 8; v += NT) {
-                const int i = v / (D / 8), c8 = (v % (D / 8)) * 8;
-                const float inv = 1.f / sDen[i];
-                uint4 *p = reinterpret_cast<uint4 *>(sG + i * LDV + c8);
-                uint4 u = *p;
-                uint32_t wds[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float lo = __uint_as_float(wds[e] << 16) * inv;
-                    const float hi = __uint_as_float(wds[e] & 0xffff0000u) * inv;
-                    wds[e] = (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
-                }
-                *p = make_uint4(wds[0], wds[1], wds[2], wds[3]);
-            }
-            if (t < F) {   // r partial: sum_i c_i Phi(q_i)
-                float acc = 0.f;
-                for (int i = 0; i < kC; ++i) acc += sCc[i] * bf2f(sQ[i * LDF + t]);
-                rr += acc;
-            }
-            __syncthreads();
-
-            // dPhi(q)^T for this wave's feature block
-            f32x16 Q0 = zero16(), Q1 = zero16();
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int k0 = 16 * s + 8 * h;
-                const bf16x8 ka = tr8(tr_addr(sK, LDF, k0, 32 * w), tr_addr(sK, LDF, k0 + 4, 32 * w));
-                if (s < 2) Q0 = mfma(ka, ld8(sP + l32 * kLDP + 16 * s + 8 * h), Q0);
-                Q1 = mfma(ka, ld8(sP + (32 + l32) * kLDP + 16 * s + 8 * h), Q1);
-            }
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                f32x16 &Qt = ib ? Q1 : Q0;
-                const f32x16 &Ut = ib ? U1 : U0;
-                const float inv = 1.f / den[ib], c = cc[ib];
-                const int row = c0 + 32 * ib + l32;
+                const int row = c0 + l32;
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int f0 = 32 * w + 8 * q4 + 4 * h;
                     float qr[4], o[4];
-                    ld4f(sQr + (32 * ib + l32) * LDV + f0, qr);
+                    ld4f(sQr + l32 * LDV + f0, qr);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float dphi = Qt[4 * q4 + e] + Ut[4 * q4 + e] * inv - sz[f0 + e] * c;
-                        o[e] = phi_d<PHI>(qr[e]) * dphi;
-                    }
-                    if (row < a.N) st4bf(dqh + (size_t)row * D + f0, o);
+                    for (int e = 0; e < 4; ++e)
+                        o[e] = phi_d<PHI>(qr[e]) * (Qd[4 * q4 + e] + U[4 * q4 + e] * inv - sz[f0 + e] * c);
+                    if (row < a.N) st4bf(dqbase + bh * a.N * D + (size_t)row * D + f0, o);
                 }
             }
-            // segment partial R += Phi(Q)^T gn (this wave's feature block x all value blocks)
+            __syncthreads();   // sCc and sInv are complete
+            if (!state_wave) {
+                // R (feature block wr x every value block) += (Phi(Q) / den)^T G
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+                for (int s = 0; s < kCb / 16; ++s) {
+                    const int k0 = 16 * s + 8 * h;
+                    bf16x8 qa = tr8(tr_addr(sQ, LDF, k0, 32 * wr), tr_addr(sQ, LDF, k0 + 4, 32 * wr));
+                    const float4 i0 = *reinterpret_cast<const float4 *>(sInv + k0);
+                    const float4 i1 = *reinterpret_cast<const float4 *>(sInv + k0 + 4);
+                    const float sc[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) qa[e] = (__bf16)((float)qa[e] * sc[e]);
+#pragma unroll
+                    for (int db = 0; db < NW; ++db) {
+                        const bf16x8 gb = tr8(tr_addr(sG, LDV, k0, 32 * db), tr_addr(sG, LDV, k0 + 4, 32 * db));
+                        X[db] = mfma(qa, gb, X[db]);
+                    }
+                }
+                const int tf = t - NW * 64;
+                if (tf < F) {
+                    float acc = 0.f;
+#pragma unroll 8
+                    for (int i = 0; i < kCb; ++i) acc += sCc[i] * bf2f(sQ[i * LDF + tf]);
+                    rr += acc;
+                }
+            }
+        }
+        if (state_wave) {
+            // carry (S^T, z) past this chunk
+#pragma unroll
+            for (int s = 0; s < kCb / 16; ++s) {
                 const int k0 = 16 * s + 8 * h;
-                const bf16x8 qa = tr8(tr_addr(sQ, LDF, k0, 32 * w), tr_addr(sQ, LDF, k0 + 4, 32 * w));
+                const bf16x8 kb = tr8(tr_addr(sK, LDF, k0, 32 * w), tr_addr(sK, LDF, k0 + 4, 32 * w));
+                Z = mfma(kb, one, Z);
 #pragma unroll
                 for (int db = 0; db < NW; ++db) {
-                    const bf16x8 gb = tr8(tr_addr(sG, LDV, k0, 32 * db), tr_addr(sG, LDV, k0 + 4, 32 * db));
-                    dR[db] = mfma(qa, gb, dR[db]);
+                    const bf16x8 va = tr8(tr_addr(sV, LDV, k0, 32 * db), tr_addr(sV, LDV, k0 + 4, 32 * db));
+                    X[db] = mfma(va, kb, X[db]);
                 }
             }
-        }
-        // carry S^T past this chunk: S^T += V^T Phi(K)
+            // every staging of this chunk has read sz (each preceded a barrier
+            // this wave has passed), so it can take the new z now
+            if (l32 == 0) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int k0 = 16 * s + 8 * h;
-            const bf16x8 kb = tr8(tr_addr(sK, LDF, k0, 32 * w), tr_addr(sK, LDF, k0 + 4, 32 * w));
-#pragma unroll
-            for (int db = 0; db < NW; ++db) {
-                const bf16x8 va = tr8(tr_addr(sV, LDV, k0, 32 * db), tr_addr(sV, LDV, k0 + 4, 32 * db));
-                St[db] = mfma(va, kb, St[db]);
+                for (int r = 0; r < 16; ++r) sz[32 * w + acc_row(r, h)] = Z[r];
             }
         }
-        __syncthreads();
-        if (t < F) {
-            float acc = 0.f;
-            for (int j = 0; j < kC; ++j) acc += bf2f(sK[j * LDF + t]);
-            sz[t] += acc;
-        }
     }
-    // this segment's (R, r), summed over the group's query heads
-    float *Ro = a.ws_Rp + ((size_t)bg * a.nseg + seg) * SD;
+    if (!state_wave) {
+        // this segment's (R, r), summed over the group's query heads
+        float *Ro = a.ws_Rp + ((size_t)bg * a.nseg + seg) * SD;
 #pragma unroll
-    for (int db = 0; db < NW; ++db)
+        for (int db = 0; db < NW; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            Ro[(size_t)(32 * w + 8 * (r >> 2) + 4 * h + (r & 3)) * D + 32 * db + l32] = dR[db][r];
-    if (t < F) Ro[(size_t)F * D + t] = rr;
+            for (int r = 0; r < 16; ++r)
+                Ro[(size_t)(32 * wr + acc_row(r, h)) * D + 32 * db + l32] = X[db][r];
+        const int tf = t - NW * 64;
+        if (tf < F) Ro[(size_t)F * D + tf] = rr;
+    }
 }
 
 // ---------------------------------------------------------------------------
-// k_bwd_kv_mfma: backward over the chunks of one (batch, KV head, segment),
-// from the exclusive suffix (R, r) of the segment.
+// k_bwd_kv_mfma: backward over the 32-row chunks of one (batch, KV head,
+// segment), from the exclusive suffix (R, r) of the segment.  Wave w holds
+// R^T (every value block x feature block w) and produces dk for feature
+// block w and dv for value block w.
 // ---------------------------------------------------------------------------
 template <int D, int PHI>
-__global__ __launch_bounds__(D * 2) void k_bwd_kv_mfma(Args a) {
+__global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2)))
+void k_bwd_kv_mfma(Args a) {
     constexpr int F = D, NW = D / 32, NT = 2 * D, LDF = F + 8, LDV = D + 8;
-    __shared__ __attribute__((aligned(16))) u16 sK[kC * LDF];
-    __shared__ __attribute__((aligned(16))) u16 sV[kC * LDV];
-    __shared__ __attribute__((aligned(16))) u16 sKr[kC * LDV];
-    __shared__ __attribute__((aligned(16))) u16 sQ[kC * LDF];
-    __shared__ __attribute__((aligned(16))) u16 sG[kC * LDV];
-    __shared__ __attribute__((aligned(16))) u16 sA[kC * kLDP];
-    __shared__ __attribute__((aligned(16))) u16 sP[kC * kLDP];
+    __shared__ __attribute__((aligned(16))) u16 sK[kCb * LDF];
+    __shared__ __attribute__((aligned(16))) u16 sV[kCb * LDV];
+    __shared__ __attribute__((aligned(16))) u16 sKr[kCb * LDV];
+    __shared__ __attribute__((aligned(16))) u16 sQ[kCb * LDF];
+    __shared__ __attribute__((aligned(16))) u16 sG[kCb * LDV];
     __shared__ __attribute__((aligned(16))) u16 sR[F * LDV];
-    __shared__ float sr[F], sCc[kC];
+    __shared__ __attribute__((aligned(16))) float sCc[kCb];
+    __shared__ float sr[F];
 
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
@@ -366,25 +306,34 @@ __global__ __launch_bounds__(D * 2) void k_bwd_kv_mfma(Args a) {
     const u16 *vh = static_cast<const u16 *>(a.v) + (size_t)bg * a.N * D;
     u16 *dkh = static_cast<u16 *>(a.dk) + (size_t)bg * a.N * D;
     u16 *dvh = static_cast<u16 *>(a.dv) + (size_t)bg * a.N * D;
+    const size_t bh0 = (size_t)b * a.H + (size_t)g * a.nrep;
+    const u16 *qbase = static_cast<const u16 *>(a.q);
+    const u16 *gbase = static_cast<const u16 *>(a.g);
 
-    // R^T tiles (value block db x this wave's feature block), fp32
     const float *Rp = a.ws_Rs + ((size_t)bg * (a.nseg + 1) + seg) * SD;
     f32x16 Rt[NW];
 #pragma unroll
     for (int db = 0; db < NW; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            Rt[db][r] = Rp[(size_t)(32 * w + l32) * D + 32 * db + 8 * (r >> 2) + 4 * h + (r & 3)];
+        for (int r = 0; r < 16; ++r) Rt[db][r] = Rp[(size_t)(32 * w + l32) * D + 32 * db + acc_row(r, h)];
     for (int e = t; e < F; e += NT) sr[e] = Rp[(size_t)F * D + e];
 
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
-    const int nch = (row1 - row0 + kC - 1) / kC;
+    const int nch = (row1 - row0 + kCb - 1) / kCb;
+    RawTile<D, NT, kCb> rK, rV, rQ, rG;
+    {
+        const int c0 = row0 + (nch - 1) * kCb;
+        rK.load(kh, c0, a.N);
+        rV.load(vh, c0, a.N);
+        rQ.load(qbase + bh0 * a.N * D, c0, a.N);
+        rG.load(gbase + bh0 * a.N * D, c0, a.N);
+    }
     for (int ci = nch - 1; ci >= 0; --ci) {
-        const int c0 = row0 + ci * kC;
+        const int c0 = row0 + ci * kCb;
         __syncthreads();
-        stage<D, LDF, NT, true, PHI, false>(sK, kh, c0, a.N, a.cw, a.sw);
-        stage<D, LDV, NT, false, PHI, false>(sV, vh, c0, a.N, a.cw, a.sw);
-        stage<D, LDV, NT, false, PHI, false>(sKr, kh, c0, a.N, a.cw, a.sw);
+        rK.template store_feat<PHI, false>(sK, LDF, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rK.store(sKr, LDV);
+        rV.store(sV, LDV);
         // R (bf16, [feature][value]) for the value-gradient's state term
 #pragma unroll
         for (int db = 0; db < NW; ++db)
@@ -398,43 +347,32 @@ __global__ __launch_bounds__(D * 2) void k_bwd_kv_mfma(Args a) {
         __syncthreads();
 
         // state terms: dPhi(k)^T = R V^T - r, dv^T = R^T Phi(K)^T
-        f32x16 dK[2] = {zero16(), zero16()}, dV[2] = {zero16(), zero16()};
+        f32x16 dK = zero16(), dV = zero16();
 #pragma unroll
         for (int db = 0; db < NW; ++db)
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const bf16x8 ra = acc_op(Rt[db], s);
-                const int d0 = 32 * db + 16 * s + 4 * h;
-                dK[0] = mfma(ra, ld4x2(sV + l32 * LDV + d0), dK[0]);
-                dK[1] = mfma(ra, ld4x2(sV + (32 + l32) * LDV + d0), dK[1]);
-            }
+            for (int s = 0; s < 2; ++s)
+                dK = mfma(acc_op(Rt[db], s), ld4x2(sV + l32 * LDV + 32 * db + 16 * s + 4 * h), dK);
 #pragma unroll 4
         for (int s = 0; s < F / 16; ++s) {
             const int k0 = 16 * s + 8 * h;
-            const bf16x8 ra = tr8(tr_addr(sR, LDV, k0, 32 * w), tr_addr(sR, LDV, k0 + 4, 32 * w));
-            dV[0] = mfma(ra, ld8(sK + l32 * LDF + 16 * s + 8 * h), dV[0]);
-            dV[1] = mfma(ra, ld8(sK + (32 + l32) * LDF + 16 * s + 8 * h), dV[1]);
+            dV = mfma(tr8(tr_addr(sR, LDV, k0, 32 * w), tr_addr(sR, LDV, k0 + 4, 32 * w)),
+                      ld8(sK + l32 * LDF + 16 * s + 8 * h), dV);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float rf = sr[32 * w + 8 * (r >> 2) + 4 * h + (r & 3)];
-            dK[0][r] -= rf;
-            dK[1][r] -= rf;
-        }
+        for (int r = 0; r < 16; ++r) dK[r] -= sr[32 * w + acc_row(r, h)];
 
         for (int rep = 0; rep < a.nrep; ++rep) {
-            const size_t bh = (size_t)b * a.H + (size_t)g * a.nrep + rep;
-            const u16 *qh = static_cast<const u16 *>(a.q) + bh * a.N * D;
-            const u16 *gh = static_cast<const u16 *>(a.g) + bh * a.N * D;
-            __syncthreads();   // previous head's tiles and the state-term reads of r are done
-            stage<D, LDF, NT, true, PHI, false>(sQ, qh, c0, a.N, a.cw, a.sw);
-            // gn = g / den (rows past N: zeros)
-            for (int v = t; v < kC * D / 8; v += NT) {
-                const int i = v / (D / 8), c8 = (v % (D / 8)) * 8, row = c0 + i;
-                uint4 u = make_uint4(0, 0, 0, 0);
-                if (row < a.N) {
-                    const float inv = 1.f / a.ws_den[bh * a.N + row];
-                    u = *reinterpret_cast<const uint4 *>(gh + (size_t)row * D + c8);
+            const size_t bh = bh0 + rep;
+            __syncthreads();   // previous head's LDS reads and every read of r are done
+            rQ.template store_feat<PHI, false>(sQ, LDF, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+            {   // gn = g / den in LDS (rows past N: zeros), and c
+                constexpr int NV = RawTile<D, NT, kCb>::NV, V8 = D / 8;
+#pragma unroll
+                for (int k = 0; k < NV; ++k) {
+                    const int idx = t + k * NT, i = idx / V8, c8 = (idx % V8) * 8, row = c0 + i;
+                    const float inv = row < a.N ? 1.f / a.ws_den[bh * a.N + row] : 0.f;
+                    const uint4 u = rG.v[k];
                     uint32_t wds[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -442,57 +380,54 @@ __global__ __launch_bounds__(D * 2) void k_bwd_kv_mfma(Args a) {
                         const float hi = __uint_as_float(wds[e] & 0xffff0000u) * inv;
                         wds[e] = (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
                     }
-                    u = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+                    *reinterpret_cast<uint4 *>(sG + i * LDV + c8) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
                 }
-                *reinterpret_cast<uint4 *>(sG + i * LDV + c8) = u;
-            }
-            for (int i = t; i < kC; i += NT) sCc[i] = c0 + i < a.N ? a.ws_c[bh * a.N + c0 + i] : 0.f;
-            __syncthreads();
-
-            // tiles: A (bf16) and P = gn.v - c, stored [query][key]
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int tt = w + k * NW;
-                if (tt < 3) {
-                    f32x16 At, Tt;
-                    tile_AT<F, D>(tt, sK, sQ, sV, sG, At, Tt);
-                    const int ib = tile_ib(tt), jb = tile_jb(tt);
-                    const float c = sCc[32 * ib + l32];
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int j = 8 * (r >> 2) + 4 * h + (r & 3);
-                        const bool keep = jb != ib || j <= l32;
-                        Tt[r] = keep ? Tt[r] - c : 0.f;
-                    }
-                    store_tile_qk(sA, tt, At);
-                    store_tile_qk(sP, tt, Tt);
-                }
-            }
-            if (t < F) {
-                float acc = 0.f;
-                for (int i = 0; i < kC; ++i) acc += sCc[i] * bf2f(sQ[i * LDF + t]);
-                sr[t] += acc;
+                for (int i = t; i < kCb; i += NT) sCc[i] = c0 + i < a.N ? a.ws_c[bh * a.N + c0 + i] : 0.f;
             }
             __syncthreads();
+            if (rep + 1 < a.nrep) {
+                rQ.load(qbase + (bh + 1) * a.N * D, c0, a.N);
+                rG.load(gbase + (bh + 1) * a.N * D, c0, a.N);
+            } else if (ci > 0) {
+                const int cn = c0 - kCb;
+                rK.load(kh, cn, a.N);
+                rV.load(vh, cn, a.N);
+                rQ.load(qbase + bh0 * a.N * D, cn, a.N);
+                rG.load(gbase + bh0 * a.N * D, cn, a.N);
+            }
 
-            // in-chunk terms
+            // A = Phi(Q) Phi(K)^T and P = gn V^T - c (queries x keys), i >= j
+            f32x16 A = zero16(), P = zero16();
+#pragma unroll 4
+            for (int s = 0; s < F / 16; ++s)
+                A = mfma(ld8(sQ + l32 * LDF + 16 * s + 8 * h), ld8(sK + l32 * LDF + 16 * s + 8 * h), A);
+#pragma unroll 4
+            for (int s = 0; s < D / 16; ++s)
+                P = mfma(ld8(sG + l32 * LDV + 16 * s + 8 * h), ld8(sV + l32 * LDV + 16 * s + 8 * h), P);
+            {
+                const float4 c0v = *reinterpret_cast<const float4 *>(sCc + 4 * h);
+                const float4 c1v = *reinterpret_cast<const float4 *>(sCc + 8 + 4 * h);
+                const float4 c2v = *reinterpret_cast<const float4 *>(sCc + 16 + 4 * h);
+                const float4 c3v = *reinterpret_cast<const float4 *>(sCc + 24 + 4 * h);
+                const float cr[16] = {c0v.x, c0v.y, c0v.z, c0v.w, c1v.x, c1v.y, c1v.z, c1v.w,
+                                      c2v.x, c2v.y, c2v.z, c2v.w, c3v.x, c3v.y, c3v.z, c3v.w};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int k0 = 16 * s + 8 * h;
-                const bf16x8 qa = tr8(tr_addr(sQ, LDF, k0, 32 * w), tr_addr(sQ, LDF, k0 + 4, 32 * w));
-                const bf16x8 ga = tr8(tr_addr(sG, LDV, k0, 32 * w), tr_addr(sG, LDV, k0 + 4, 32 * w));
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb) {
-                    if (jb == 1 && s < 2) continue;   // queries before key block 1 see none of it
-                    const bf16x8 pb = tr8(tr_addr(sP, kLDP, k0, 32 * jb), tr_addr(sP, kLDP, k0 + 4, 32 * jb));
-                    const bf16x8 ab = tr8(tr_addr(sA, kLDP, k0, 32 * jb), tr_addr(sA, kLDP, k0 + 4, 32 * jb));
-                    dK[jb] = mfma(qa, pb, dK[jb]);
-                    dV[jb] = mfma(ga, ab, dV[jb]);
+                for (int r = 0; r < 16; ++r) {
+                    const bool keep = acc_row(r, h) >= l32;
+                    A[r] = keep ? (float)(__bf16)A[r] : 0.f;
+                    P[r] = keep ? P[r] - cr[r] : 0.f;
                 }
             }
-            // R^T += gn^T Phi(Q) for the rows of this chunk
+            // in-chunk terms: dPhi(k)^T += Phi(Q)^T P, dv^T += gn^T A
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+            for (int s = 0; s < 2; ++s) {
+                const int k0 = 16 * s + 4 * h;
+                dK = mfma(tr8(tr_addr(sQ, LDF, k0, 32 * w), tr_addr(sQ, LDF, k0 + 8, 32 * w)), acc_op(P, s), dK);
+                dV = mfma(tr8(tr_addr(sG, LDV, k0, 32 * w), tr_addr(sG, LDV, k0 + 8, 32 * w)), acc_op(A, s), dV);
+            }
+            // R^T += gn^T Phi(Q) for the rows of this chunk; r += Phi(Q)^T c
+#pragma unroll
+            for (int s = 0; s < kCb / 16; ++s) {
                 const int k0 = 16 * s + 8 * h;
                 const bf16x8 qb = tr8(tr_addr(sQ, LDF, k0, 32 * w), tr_addr(sQ, LDF, k0 + 4, 32 * w));
 #pragma unroll
@@ -501,21 +436,25 @@ __global__ __launch_bounds__(D * 2) void k_bwd_kv_mfma(Args a) {
                     Rt[db] = mfma(ga, qb, Rt[db]);
                 }
             }
+            if (t < F) {
+                float acc = 0.f;
+#pragma unroll 8
+                for (int i = 0; i < kCb; ++i) acc += sCc[i] * bf2f(sQ[i * LDF + t]);
+                sr[t] += acc;
+            }
         }
-        // dk = phi'(k) dPhi(k), dv; lane holds key j and columns 32w + 8q + 4h + 0..3
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-            const int row = c0 + 32 * jb + l32;
-            if (row >= a.N) continue;
+        // dk = phi'(k) dPhi(k), dv; lane holds key l32 and columns 32w + 8q + 4h + 0..3
+        const int row = c0 + l32;
+        if (row < a.N) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int f0 = 32 * w + 8 * q4 + 4 * h;
                 float kr[4], ok[4], ov[4];
-                ld4f(sKr + (32 * jb + l32) * LDV + f0, kr);
+                ld4f(sKr + l32 * LDV + f0, kr);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    ok[e] = phi_d<PHI>(kr[e]) * dK[jb][4 * q4 + e];
-                    ov[e] = dV[jb][4 * q4 + e];
+                    ok[e] = phi_d<PHI>(kr[e]) * dK[4 * q4 + e];
+                    ov[e] = dV[4 * q4 + e];
                 }
                 st4bf(dkh + (size_t)row * D + f0, ok);
                 st4bf(dvh + (size_t)row * D + f0, ov);
@@ -526,14 +465,14 @@ __global__ __launch_bounds__(D * 2) void k_bwd_kv_mfma(Args a) {
 
 template <int D, int PHI>
 hipError_t run(const Args &a, hipStream_t s) {
-    constexpr int NT = D * 2, F = D;
+    constexpr int F = D;
     const unsigned n_units = (unsigned)(a.B * a.Hkv);
     const size_t SD = (size_t)F * D + F;
     hipError_t e = mfma_state_run(a, PHI, s);
     if (e != hipSuccess) return e;
     {
         TimedLaunch tl("k_bwd_q_mfma", s);
-        hipLaunchKernelGGL((k_bwd_q_mfma<D, PHI>), dim3(n_units * a.nseg), dim3(NT), 0, s, a);
+        hipLaunchKernelGGL((k_bwd_q_mfma<D, PHI>), dim3(n_units * a.nseg), dim3(4 * D), 0, s, a);
     }
     {
         TimedLaunch tl("k_scan_R", s);
@@ -543,7 +482,7 @@ hipError_t run(const Args &a, hipStream_t s) {
     }
     {
         TimedLaunch tl("k_bwd_kv_mfma", s);
-        hipLaunchKernelGGL((k_bwd_kv_mfma<D, PHI>), dim3(n_units * a.nseg), dim3(NT), 0, s, a);
+        hipLaunchKernelGGL((k_bwd_kv_mfma<D, PHI>), dim3(n_units * a.nseg), dim3(2 * D), 0, s, a);
     }
     return hipGetLastError();
 }
