@@ -60,6 +60,36 @@ def kernel_bytes(name, w, s):
     return None
 
 
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary
+    (FETCH_SIZE / WRITE_SIZE scaled by a plain copy of known size), or None
+    when there is no summary or a kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "counters_%s.md" % workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    srcdir = os.path.join(ROOT, "linear_attention_transformers_amd", "csrc")
+    for line in text.splitlines():
+        if line.startswith("Kernel sources (sha256 prefix):"):
+            for item in line.split(":", 1)[1].split(","):
+                name, digest = item.strip().split("=")
+                cur = hashlib.sha256(open(os.path.join(srcdir, name), "rb").read()).hexdigest()
+                if not cur.startswith(digest):
+                    return None
+    scale, rows = None, {}
+    for line in text.splitlines():
+        parts = line.split()
+        if len(parts) == 4 and parts[0] == "fetch_scale":
+            scale = (float(parts[1]), float(parts[3]))
+        elif len(parts) == 3 and parts[0].startswith("k_"):
+            rows[parts[0]] = (float(parts[1]), float(parts[2]))
+    if scale is None or kernel not in rows:
+        return None
+    fetch, write = rows[kernel]
+    return (fetch * scale[0] + write * scale[1]) * 1024.0
+
+
 def step_roofline(w, s, causal):
     """Time of one fwd+bwd step at the roofline: algorithmic bytes at HBM peak
     vs algorithmic flops at the bf16 matrix peak (state updates and reads,
@@ -123,6 +153,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="before warmup, copy a buffer of this many MiB once (a plain "
+                         "device copy of known size, to scale HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -165,6 +198,16 @@ def main():
             la.bwd(t["q"], t["k"], t["v"], t["grad_out"], is_causal=causal, phi=w.phi,
                    eps=w.eps, cos_weight=cw, sin_weight=sw, workspace=ws_b, grads=grads)
 
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("bench: calibration copy of %d MiB done" % args.calibration_copy_mib)
+
     log("bench: %d warmup steps" % args.warmup)
     for _ in range(args.warmup):
         step()
@@ -191,7 +234,7 @@ def main():
     avg_s = total_ms / launches / 1e3
     nbytes = kernel_bytes(dom_name, w, s)
     roof = {"bound": "hbm", "kernel": dom_name, "achieved": None, "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": None, "traffic": None,
+            "unit": "GB/s", "frac": None, "traffic": measured_traffic(name, dom_name),
             "avg_launch_ms": avg_s * 1e3, "algorithmic_bytes_per_launch": nbytes}
     if nbytes is not None:
         ach = nbytes / avg_s / 1e9
