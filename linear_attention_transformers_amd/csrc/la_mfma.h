@@ -220,5 +220,38 @@ __device__ __forceinline__ const u16 *tr_addr(const u16 *X, int LD, int k0, int 
     return X + (k0 + (i16 >> 2)) * LD + col0 + 16 * (gi & 1) + 4 * (i16 & 3);
 }
 
+// Output rows go through LDS so global stores are whole rows, 16 bytes per
+// lane, instead of 8-byte pieces spread over 32 rows per instruction.
+// stage_out: this lane's accumulator values for row `lane % 32` and columns
+// col0 + 8q + 4h + 0..3 (q = 0..3), scaled by `scale`, into sO[32][LDO].
+__device__ __forceinline__ void stage_out(u16 *sO, int LDO, const f32x16 &acc, float scale,
+                                          int col0) {
+    const int l = threadIdx.x & 63, h = l >> 5, l32 = l & 31;
+    u16 *row = sO + l32 * LDO + col0 + 4 * h;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+        const uint32_t lo = (uint32_t)f2bf(acc[4 * q4] * scale) | ((uint32_t)f2bf(acc[4 * q4 + 1] * scale) << 16);
+        const uint32_t hi =
+            (uint32_t)f2bf(acc[4 * q4 + 2] * scale) | ((uint32_t)f2bf(acc[4 * q4 + 3] * scale) << 16);
+        *reinterpret_cast<uint2 *>(row + 8 * q4) = make_uint2(lo, hi);
+    }
+}
+
+// store_rows: rows 0..31 of sO (row r -> global row c0 + r of a [N][D]
+// tensor, rows >= N skipped), NT threads (numbered tid, default the thread
+// index) storing 16-byte pieces.  Call after a barrier that follows the
+// stage_out of every wave.
+template <int D, int NT>
+__device__ __forceinline__ void store_rows(u16 *dst, const u16 *sO, int LDO, int c0, int N,
+                                           int tid = -1) {
+    constexpr int V8 = D / 8;
+    for (int v = tid < 0 ? (int)threadIdx.x : tid; v < 32 * V8; v += NT) {
+        const int r = v / V8, c8 = (v % V8) * 8;
+        if (c0 + r < N)
+            *reinterpret_cast<uint4 *>(dst + (size_t)(c0 + r) * D + c8) =
+                *reinterpret_cast<const uint4 *>(sO + r * LDO + c8);
+    }
+}
+
 }  // namespace mf
 }  // namespace la

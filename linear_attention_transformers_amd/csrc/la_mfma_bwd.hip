@@ -206,16 +206,23 @@ void k_bwd_q_mfma(Args a) {
                     const bf16x8 ka = tr8(tr_addr(sK, LDF, k0, 32 * w), tr_addr(sK, LDF, k0 + 8, 32 * w));
                     Qd = mfma(ka, acc_op(Tt, s), Qd);
                 }
-                const int row = c0 + l32;
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int f0 = 32 * w + 8 * q4 + 4 * h;
-                    float qr[4], o[4];
+                    float qr[4];
                     ld4f(sQr + l32 * LDV + f0, qr);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        o[e] = phi_d<PHI>(qr[e]) * (Qd[4 * q4 + e] + U[4 * q4 + e] * inv - sz[f0 + e] * c);
-                    if (row < a.N) st4bf(dqbase + bh * a.N * D + (size_t)row * D + f0, o);
+                        Qd[4 * q4 + e] = phi_d<PHI>(qr[e]) *
+                                         (Qd[4 * q4 + e] + U[4 * q4 + e] * inv - sz[f0 + e] * c);
+                }
+                const int row = c0 + l32;
+                if (row < a.N) {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const float o[4] = {Qd[4 * q4], Qd[4 * q4 + 1], Qd[4 * q4 + 2], Qd[4 * q4 + 3]};
+                        st4bf(dqbase + bh * a.N * D + (size_t)row * D + 32 * w + 8 * q4 + 4 * h, o);
+                    }
                 }
             }
             __syncthreads();   // sCc and sInv are complete
@@ -328,9 +335,14 @@ void k_bwd_kv_mfma(Args a) {
         rQ.load(qbase + bh0 * a.N * D, c0, a.N);
         rG.load(gbase + bh0 * a.N * D, c0, a.N);
     }
+    int pend_c0 = -1;   // dk, dv rows of the previous chunk staged in sQ, sG
     for (int ci = nch - 1; ci >= 0; --ci) {
         const int c0 = row0 + ci * kCb;
         __syncthreads();
+        if (pend_c0 >= 0) {
+            store_rows<D, NT>(dkh, sQ, LDF, pend_c0, a.N);
+            store_rows<D, NT>(dvh, sG, LDV, pend_c0, a.N);
+        }
         rK.template store_feat<PHI, false>(sK, LDF, c0, a.N, a.cw, a.sw, nullptr, nullptr);
         rK.store(sKr, LDV);
         rV.store(sV, LDV);
@@ -396,34 +408,43 @@ void k_bwd_kv_mfma(Args a) {
                 rG.load(gbase + bh0 * a.N * D, cn, a.N);
             }
 
-            // A = Phi(Q) Phi(K)^T and P = gn V^T - c (queries x keys), i >= j
-            f32x16 A = zero16(), P = zero16();
-#pragma unroll 4
-            for (int s = 0; s < F / 16; ++s)
-                A = mfma(ld8(sQ + l32 * LDF + 16 * s + 8 * h), ld8(sK + l32 * LDF + 16 * s + 8 * h), A);
-#pragma unroll 4
-            for (int s = 0; s < D / 16; ++s)
-                P = mfma(ld8(sG + l32 * LDV + 16 * s + 8 * h), ld8(sV + l32 * LDV + 16 * s + 8 * h), P);
+            // A = Phi(Q) Phi(K)^T and P = gn V^T - c (queries x keys), i >= j;
+            // each is turned into bf16 operands as soon as it is complete
+            bf16x8 Aop[2], Pop[2];
             {
-                const float4 c0v = *reinterpret_cast<const float4 *>(sCc + 4 * h);
-                const float4 c1v = *reinterpret_cast<const float4 *>(sCc + 8 + 4 * h);
-                const float4 c2v = *reinterpret_cast<const float4 *>(sCc + 16 + 4 * h);
-                const float4 c3v = *reinterpret_cast<const float4 *>(sCc + 24 + 4 * h);
-                const float cr[16] = {c0v.x, c0v.y, c0v.z, c0v.w, c1v.x, c1v.y, c1v.z, c1v.w,
-                                      c2v.x, c2v.y, c2v.z, c2v.w, c3v.x, c3v.y, c3v.z, c3v.w};
+                f32x16 A = zero16();
+#pragma unroll 4
+                for (int s = 0; s < F / 16; ++s)
+                    A = mfma(ld8(sQ + l32 * LDF + 16 * s + 8 * h), ld8(sK + l32 * LDF + 16 * s + 8 * h), A);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const bool keep = acc_row(r, h) >= l32;
-                    A[r] = keep ? (float)(__bf16)A[r] : 0.f;
-                    P[r] = keep ? P[r] - cr[r] : 0.f;
+                for (int r = 0; r < 16; ++r) A[r] = acc_row(r, h) >= l32 ? A[r] : 0.f;
+                Aop[0] = acc_op(A, 0);
+                Aop[1] = acc_op(A, 1);
+            }
+            {
+                f32x16 P = zero16();
+#pragma unroll 4
+                for (int s = 0; s < D / 16; ++s)
+                    P = mfma(ld8(sG + l32 * LDV + 16 * s + 8 * h), ld8(sV + l32 * LDV + 16 * s + 8 * h), P);
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const float4 cv = *reinterpret_cast<const float4 *>(sCc + 8 * q4 + 4 * h);
+                    const float cr[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * q4 + e;
+                        P[r] = acc_row(r, h) >= l32 ? P[r] - cr[e] : 0.f;
+                    }
                 }
+                Pop[0] = acc_op(P, 0);
+                Pop[1] = acc_op(P, 1);
             }
             // in-chunk terms: dPhi(k)^T += Phi(Q)^T P, dv^T += gn^T A
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const int k0 = 16 * s + 4 * h;
-                dK = mfma(tr8(tr_addr(sQ, LDF, k0, 32 * w), tr_addr(sQ, LDF, k0 + 8, 32 * w)), acc_op(P, s), dK);
-                dV = mfma(tr8(tr_addr(sG, LDV, k0, 32 * w), tr_addr(sG, LDV, k0 + 8, 32 * w)), acc_op(A, s), dV);
+                dK = mfma(tr8(tr_addr(sQ, LDF, k0, 32 * w), tr_addr(sQ, LDF, k0 + 8, 32 * w)), Pop[s], dK);
+                dV = mfma(tr8(tr_addr(sG, LDV, k0, 32 * w), tr_addr(sG, LDV, k0 + 8, 32 * w)), Aop[s], dV);
             }
             // R^T += gn^T Phi(Q) for the rows of this chunk; r += Phi(Q)^T c
 #pragma unroll
@@ -443,23 +464,25 @@ void k_bwd_kv_mfma(Args a) {
                 sr[t] += acc;
             }
         }
-        // dk = phi'(k) dPhi(k), dv; lane holds key l32 and columns 32w + 8q + 4h + 0..3
-        const int row = c0 + l32;
-        if (row < a.N) {
+        // dk = phi'(k) dPhi(k), dv; lane holds key l32 and columns 32w + 8q + 4h + 0..3.
+        // The last head's reads of sQ and sG must be over before they take the rows.
+        __syncthreads();
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int f0 = 32 * w + 8 * q4 + 4 * h;
-                float kr[4], ok[4], ov[4];
-                ld4f(sKr + l32 * LDV + f0, kr);
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int f0 = 32 * w + 8 * q4 + 4 * h;
+            float kr[4];
+            ld4f(sKr + l32 * LDV + f0, kr);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    ok[e] = phi_d<PHI>(kr[e]) * dK[4 * q4 + e];
-                    ov[e] = dV[4 * q4 + e];
-                }
-                st4bf(dkh + (size_t)row * D + f0, ok);
-                st4bf(dvh + (size_t)row * D + f0, ov);
-            }
+            for (int e = 0; e < 4; ++e) dK[4 * q4 + e] *= phi_d<PHI>(kr[e]);
         }
+        stage_out(sQ, LDF, dK, 1.f, 32 * w);
+        stage_out(sG, LDV, dV, 1.f, 32 * w);
+        pend_c0 = c0;
+    }
+    __syncthreads();
+    if (pend_c0 >= 0) {
+        store_rows<D, NT>(dkh, sQ, LDF, pend_c0, a.N);
+        store_rows<D, NT>(dvh, sG, LDV, pend_c0, a.N);
     }
 }
 

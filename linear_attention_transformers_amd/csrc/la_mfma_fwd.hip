@@ -95,21 +95,6 @@ __global__ __launch_bounds__(D * 2) void k_state_mfma(Args a) {
     if (t < F) out[(size_t)F * D + t] = z;
 }
 
-// Store one 32-query block of out: lane holds query row `row` and value
-// columns 32w + 8q + 4h + 0..3 (q = 0..3) of the num^T accumulator.
-template <int D>
-__device__ __forceinline__ void store_out(u16 *oh, const f32x16 &Nt, int row, int N, float inv,
-                                          int w, int h) {
-    if (row >= N) return;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-        const uint32_t lo = (uint32_t)f2bf(Nt[4 * q4] * inv) | ((uint32_t)f2bf(Nt[4 * q4 + 1] * inv) << 16);
-        const uint32_t hi =
-            (uint32_t)f2bf(Nt[4 * q4 + 2] * inv) | ((uint32_t)f2bf(Nt[4 * q4 + 3] * inv) << 16);
-        *reinterpret_cast<uint2 *>(oh + (size_t)row * D + 32 * w + 8 * q4 + 4 * h) = make_uint2(lo, hi);
-    }
-}
-
 constexpr int kCf = 32;   // forward chunk length: one 32x32 tile of A per head
 
 // ---------------------------------------------------------------------------
@@ -127,6 +112,7 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
     __shared__ __attribute__((aligned(16))) u16 sK[kCf * LDF];
     __shared__ __attribute__((aligned(16))) u16 sQ[kCf * LDF];
     __shared__ __attribute__((aligned(16))) u16 sV[kCf * LDV];
+    __shared__ __attribute__((aligned(16))) u16 sO[kCf * LDV];   // output rows of one head
     __shared__ __attribute__((aligned(16))) float sz[F];
     __shared__ float sQZ[kCf];
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
@@ -163,13 +149,20 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
     rK.load(kh, row0, a.N);
     rV.load(vh, row0, a.N);
     rQ.load(qbase + bh0 * a.N * D, row0, a.N);
+    // rows staged in sO wait for the next barrier to be stored (pend_* = where)
+    u16 *pend_oh = nullptr;
+    int pend_c0 = 0;
     for (int c0 = row0; c0 < row1; c0 += kCf) {
-        __syncthreads();   // previous chunk: every LDS read done, sz updated
+        __syncthreads();   // previous chunk: every LDS read done, sz updated, sO complete
+        if (pend_oh) store_rows<D, NT>(pend_oh, sO, LDV, pend_c0, a.N);
         rK.template store_feat<PHI, COS>(sK, LDF, c0, a.N, a.cw, a.sw, nullptr, nullptr);
         rV.store(sV, LDV);
         for (int rep = 0; rep < a.nrep; ++rep) {
             u16 *oh = obase + (bh0 + rep) * a.N * D;
-            if (rep > 0) __syncthreads();   // every wave is done with the previous head's sQ
+            if (rep > 0) {
+                __syncthreads();   // every wave is done with the previous head's sQ; sO complete
+                store_rows<D, NT>(pend_oh, sO, LDV, pend_c0, a.N);
+            }
             rQ.template store_feat<PHI, COS>(sQ, LDF, c0, a.N, a.cw, a.sw, sz, sQZ);
             __syncthreads();
             if (rep + 1 < a.nrep) {
@@ -212,7 +205,9 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
                 for (int s = 0; s < 2; ++s)
                     Nt = mfma(acc_op(S[fb], s), ld4x2(qrow + 32 * fb + 16 * s + 4 * h), Nt);
             const float den = dsum + sQZ[l32] + a.eps;
-            store_out<D>(oh, Nt, c0 + l32, a.N, 1.f / den, w, h);
+            stage_out(sO, LDV, Nt, 1.f / den, 32 * w);
+            pend_oh = oh;
+            pend_c0 = c0;
         }
         // carry (S, z) past this chunk: S += Phi(K)^T V, z += Phi(K)^T 1
 #pragma unroll
@@ -236,6 +231,8 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
                     sz[32 * (w + NW * c) + 8 * (r >> 2) + 4 * h + (r & 3)] = Z[c][r];
         }
     }
+    __syncthreads();
+    if (pend_oh) store_rows<D, NT>(pend_oh, sO, LDV, pend_c0, a.N);
 }
 
 template <int D, int F, int PHI, bool COS>
