@@ -28,12 +28,50 @@ namespace mf {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16;
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kC = 64;   // chunk length (rows)
+
+// LDS tile layouts.  A tile with RL bf16 elements per row keeps element
+// (r, c) at index L::at(r, c), L::ld elements per row.  The LDS has 64 banks
+// of 4 bytes; 16-byte accesses are served 16 lanes at a time and 8-byte ones
+// 32 lanes at a time.  Every address below is a lane term plus a compile-time
+// constant, so a tile costs one or two base registers however many columns
+// are read.
+//
+// Pad<RL>: rows padded by 8 elements (16 bytes, one bank quad): reads of one
+// 16-byte column over 16 consecutive rows are conflict-free, transposed reads
+// of 4 consecutive rows collide up to 4-way.
+template <int RL>
+struct Pad {
+    static constexpr int ld = RL + 8;
+    static __device__ __forceinline__ int at(int r, int c) { return r * ld + c; }
+};
+
+// PadI<RL>: Pad with the rows of every aligned 16-row block permuted:
+// logical row 16b + x is stored at physical row 16b + rev(x), rev reversing
+// the four bits of x.  Four consecutive logical rows from a multiple of 4 (one
+// transposed read, in the natural order or in an accumulator's k order) then
+// sit 4 or 8 physical rows apart, on four disjoint bank groups, so every
+// transposed read is conflict-free; 16 consecutive aligned rows are one
+// permuted block (conflict-free 16-row reads); two adjacent rows of a 64-wide
+// tile are 8 physical rows apart (conflict-free row writes); and the physical
+// row is a constant plus a lane term, so addresses stay additive.  Tiles with
+// this layout have a multiple of 16 rows.
+template <int RL>
+struct PadI {
+    static constexpr int ld = RL + 8;
+    static __device__ __forceinline__ int at(int r, int c) {
+        const int rev = ((r & 1) << 3) | ((r & 2) << 1) | ((r & 4) >> 1) | ((r & 8) >> 3);
+        return ((r & ~15) | rev) * ld + c;
+    }
+};
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -46,14 +84,19 @@ __device__ __forceinline__ f32x16 zero16() {
     return z;
 }
 
-// 16-byte operand: 8 consecutive elements of an LDS row.
-__device__ __forceinline__ bf16x8 ld8(const u16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
-
-// Operand in the permuted k order of an accumulator: elements p[0..3], p[8..11].
-__device__ __forceinline__ bf16x8 ld4x2(const u16 *p) {
-    const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(p);
-    const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(p + 8);
+// Operand in the permuted k order of an accumulator: elements (r, c .. c+3)
+// and (r, c+8 .. c+11) of a tile with layout L (c a multiple of 4).
+template <class L>
+__device__ __forceinline__ bf16x8 ld4x2(const u16 *X, int r, int c) {
+    const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(X + L::at(r, c));
+    const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(X + L::at(r, c + 8));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// 16-byte operand: elements (r, c .. c+7) of a tile with layout L (c a multiple of 8).
+template <class L>
+__device__ __forceinline__ bf16x8 ld8(const u16 *X, int r, int c) {
+    return *reinterpret_cast<const bf16x8 *>(X + L::at(r, c));
 }
 
 // Transposed 4-row read (see header comment); p = this lane's address.
@@ -82,8 +125,6 @@ __device__ __forceinline__ bf16x8 acc_op(const f32x16 &acc, int s) {
     return o;
 }
 
-constexpr int kC = 64;   // chunk length (rows)
-
 // phi for values that are rounded to bf16 right after: the hardware exp
 // (__expf, a few ulp) is far below bf16 resolution.
 template <int PHI>
@@ -92,6 +133,10 @@ __device__ __forceinline__ float phi_fast(float x) {
     else return phi_f<PHI>(x);
 }
 
+// 1 / x by the hardware reciprocal (1 ulp); the quotients it feeds are
+// rounded to bf16 or scale bf16 operands.
+__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
 __device__ __forceinline__ float bf2f(u16 x) { return __uint_as_float((uint32_t)x << 16); }
 
 __device__ __forceinline__ u16 f2bf(float x) {
@@ -99,42 +144,23 @@ __device__ __forceinline__ u16 f2bf(float x) {
     return __builtin_bit_cast(u16, b);
 }
 
-// Stage rows [c0, c0 + kC) of one head's [N][D] bf16 tensor into an LDS tile
-// [kC][LD] (rows >= N are zeros).  FEAT: apply phi, and with COS write
-// [cos_t phi, sin_t phi] (width 2D); otherwise copy.
-template <int D, int LD, int NT, bool FEAT, int PHI, bool COS>
-__device__ __forceinline__ void stage(u16 *dst, const u16 *src, int c0, int N, const float *cw,
-                                      const float *sw) {
-    constexpr int V8 = D / 8;   // 16-byte vectors per row
-    for (int v = threadIdx.x; v < kC * V8; v += NT) {
-        const int r = v / V8, c8 = (v % V8) * 8, t = c0 + r;
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (t < N) raw = *reinterpret_cast<const uint4 *>(src + (size_t)t * D + c8);
-        if constexpr (!FEAT) {
-            *reinterpret_cast<uint4 *>(dst + r * LD + c8) = raw;
-        } else {
-            const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-            float f[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                f[2 * e] = t < N ? phi_fast<PHI>(__uint_as_float(w4[e] << 16)) : 0.f;
-                f[2 * e + 1] = t < N ? phi_fast<PHI>(__uint_as_float(w4[e] & 0xffff0000u)) : 0.f;
-            }
-            const float m0 = COS ? (t < N ? cw[t] : 0.f) : 1.f;
-            uint32_t o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                o[e] = (uint32_t)f2bf(m0 * f[2 * e]) | ((uint32_t)f2bf(m0 * f[2 * e + 1]) << 16);
-            *reinterpret_cast<uint4 *>(dst + r * LD + c8) = make_uint4(o[0], o[1], o[2], o[3]);
-            if constexpr (COS) {
-                const float m1 = t < N ? sw[t] : 0.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    o[e] = (uint32_t)f2bf(m1 * f[2 * e]) | ((uint32_t)f2bf(m1 * f[2 * e + 1]) << 16);
-                *reinterpret_cast<uint4 *>(dst + r * LD + D + c8) = make_uint4(o[0], o[1], o[2], o[3]);
-            }
-        }
-    }
+// Two floats rounded to bf16 (nearest even) and packed low, high into one
+// word: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pk2(float lo, float hi) {
+    bf16x2 v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// phi'(x) from the bf16 feature p = phi(x) of a bf16 input x.  relu: p > 0
+// exactly when x > 0; elu+1: p = x + 1 >= 1 for x > 0 and p = exp(x) <= 1
+// otherwise, so phi' = min(p, 1) (exp(x) to bf16 precision); identity: 1.
+template <int PHI>
+__device__ __forceinline__ float phi_d_feat(float p) {
+    if constexpr (PHI == kElu1) return fminf(p, 1.f);
+    else if constexpr (PHI == kRelu) return p > 0.f ? 1.f : 0.f;
+    else return 1.f;
 }
 
 // Rows [c0, c0 + C) of one head's [N][D] bf16 tensor held in registers as
@@ -149,6 +175,14 @@ struct RawTile {
     uint4 v[NV];
 
     __device__ __forceinline__ void load(const u16 *src, int c0, int N) {
+        if (c0 + C <= N) {   // whole tile in range (uniform): no per-row checks
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const int idx = threadIdx.x + k * NT, r = idx / V8, c8 = (idx % V8) * 8;
+                v[k] = *reinterpret_cast<const uint4 *>(src + (size_t)(c0 + r) * D + c8);
+            }
+            return;
+        }
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int idx = threadIdx.x + k * NT, r = idx / V8, c8 = (idx % V8) * 8;
@@ -157,11 +191,12 @@ struct RawTile {
         }
     }
 
-    __device__ __forceinline__ void store(u16 *dst, int LD) const {
+    template <class L>
+    __device__ __forceinline__ void store(u16 *dst) const {
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int idx = threadIdx.x + k * NT, r = idx / V8, c8 = (idx % V8) * 8;
-            *reinterpret_cast<uint4 *>(dst + r * LD + c8) = v[k];
+            *reinterpret_cast<uint4 *>(dst + L::at(r, c8)) = v[k];
         }
     }
 
@@ -169,8 +204,8 @@ struct RawTile {
     // rounded to bf16.  With sz != nullptr, also sQZ[r] = Phi(x_r) . z over
     // the rounded features (fixed-order shuffle reduction across the V8
     // threads of a row).
-    template <int PHI, bool COS>
-    __device__ __forceinline__ void store_feat(u16 *dst, int LD, int c0, int N, const float *cw,
+    template <int PHI, bool COS, class L>
+    __device__ __forceinline__ void store_feat(u16 *dst, int c0, int N, const float *cw,
                                                const float *sw, const float *sz,
                                                float *sQZ) const {
 #pragma unroll
@@ -188,20 +223,22 @@ struct RawTile {
             uint32_t o[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const u16 lo = f2bf(m0 * f[2 * e]), hi = f2bf(m0 * f[2 * e + 1]);
-                o[e] = (uint32_t)lo | ((uint32_t)hi << 16);
-                if (sz) qz += bf2f(lo) * sz[c8 + 2 * e] + bf2f(hi) * sz[c8 + 2 * e + 1];
+                o[e] = pk2(m0 * f[2 * e], m0 * f[2 * e + 1]);
+                if (sz)
+                    qz += __uint_as_float(o[e] << 16) * sz[c8 + 2 * e] +
+                          __uint_as_float(o[e] & 0xffff0000u) * sz[c8 + 2 * e + 1];
             }
-            *reinterpret_cast<uint4 *>(dst + r * LD + c8) = make_uint4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<uint4 *>(dst + L::at(r, c8)) = make_uint4(o[0], o[1], o[2], o[3]);
             if constexpr (COS) {
                 const float m1 = t < N ? sw[t] : 0.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const u16 lo = f2bf(m1 * f[2 * e]), hi = f2bf(m1 * f[2 * e + 1]);
-                    o[e] = (uint32_t)lo | ((uint32_t)hi << 16);
-                    if (sz) qz += bf2f(lo) * sz[D + c8 + 2 * e] + bf2f(hi) * sz[D + c8 + 2 * e + 1];
+                    o[e] = pk2(m1 * f[2 * e], m1 * f[2 * e + 1]);
+                    if (sz)
+                        qz += __uint_as_float(o[e] << 16) * sz[D + c8 + 2 * e] +
+                              __uint_as_float(o[e] & 0xffff0000u) * sz[D + c8 + 2 * e + 1];
                 }
-                *reinterpret_cast<uint4 *>(dst + r * LD + D + c8) = make_uint4(o[0], o[1], o[2], o[3]);
+                *reinterpret_cast<uint4 *>(dst + L::at(r, D + c8)) = make_uint4(o[0], o[1], o[2], o[3]);
             }
             if (sz) {
 #pragma unroll
@@ -212,44 +249,41 @@ struct RawTile {
     }
 };
 
-// Lane address for a transposed 4-row read of tile X (row stride LD): rows
-// k0 .. k0+3, this lane's operand index (lane % 32) mapped to columns
-// col0 .. col0+31.
-__device__ __forceinline__ const u16 *tr_addr(const u16 *X, int LD, int k0, int col0) {
+// Lane address for a transposed 4-row read of tile X: rows k0 .. k0+3, this
+// lane's operand index (lane % 32) mapped to columns col0 .. col0+31
+// (col0 a multiple of 32).
+template <class L>
+__device__ __forceinline__ const u16 *tr_addr(const u16 *X, int k0, int col0) {
     const int l = threadIdx.x & 63, gi = l >> 4, i16 = l & 15;
-    return X + (k0 + (i16 >> 2)) * LD + col0 + 16 * (gi & 1) + 4 * (i16 & 3);
+    return X + L::at(k0 + (i16 >> 2), col0 + 16 * (gi & 1) + 4 * (i16 & 3));
 }
 
 // Output rows go through LDS so global stores are whole rows, 16 bytes per
 // lane, instead of 8-byte pieces spread over 32 rows per instruction.
 // stage_out: this lane's accumulator values for row `lane % 32` and columns
-// col0 + 8q + 4h + 0..3 (q = 0..3), scaled by `scale`, into sO[32][LDO].
-__device__ __forceinline__ void stage_out(u16 *sO, int LDO, const f32x16 &acc, float scale,
-                                          int col0) {
+// col0 + 8q + 4h + 0..3 (q = 0..3), scaled by `scale`, into the 32-row tile sO.
+template <class L>
+__device__ __forceinline__ void stage_out(u16 *sO, const f32x16 &acc, float scale, int col0) {
     const int l = threadIdx.x & 63, h = l >> 5, l32 = l & 31;
-    u16 *row = sO + l32 * LDO + col0 + 4 * h;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-        const uint32_t lo = (uint32_t)f2bf(acc[4 * q4] * scale) | ((uint32_t)f2bf(acc[4 * q4 + 1] * scale) << 16);
-        const uint32_t hi =
-            (uint32_t)f2bf(acc[4 * q4 + 2] * scale) | ((uint32_t)f2bf(acc[4 * q4 + 3] * scale) << 16);
-        *reinterpret_cast<uint2 *>(row + 8 * q4) = make_uint2(lo, hi);
+        const uint32_t lo = pk2(acc[4 * q4] * scale, acc[4 * q4 + 1] * scale);
+        const uint32_t hi = pk2(acc[4 * q4 + 2] * scale, acc[4 * q4 + 3] * scale);
+        *reinterpret_cast<uint2 *>(sO + L::at(l32, col0 + 8 * q4 + 4 * h)) = make_uint2(lo, hi);
     }
 }
 
-// store_rows: rows 0..31 of sO (row r -> global row c0 + r of a [N][D]
-// tensor, rows >= N skipped), NT threads (numbered tid, default the thread
-// index) storing 16-byte pieces.  Call after a barrier that follows the
-// stage_out of every wave.
-template <int D, int NT>
-__device__ __forceinline__ void store_rows(u16 *dst, const u16 *sO, int LDO, int c0, int N,
-                                           int tid = -1) {
+// store_rows: rows 0..31 of the tile sO (row r -> global row c0 + r of a
+// [N][D] tensor, rows >= N skipped; layout L), NT threads storing 16-byte pieces.  Call
+// after a barrier that follows the stage_out of every wave.
+template <int D, int NT, class L>
+__device__ __forceinline__ void store_rows(u16 *dst, const u16 *sO, int c0, int N) {
     constexpr int V8 = D / 8;
-    for (int v = tid < 0 ? (int)threadIdx.x : tid; v < 32 * V8; v += NT) {
+    for (int v = threadIdx.x; v < 32 * V8; v += NT) {
         const int r = v / V8, c8 = (v % V8) * 8;
         if (c0 + r < N)
             *reinterpret_cast<uint4 *>(dst + (size_t)(c0 + r) * D + c8) =
-                *reinterpret_cast<const uint4 *>(sO + r * LDO + c8);
+                *reinterpret_cast<const uint4 *>(sO + L::at(r, c8));
     }
 }
 

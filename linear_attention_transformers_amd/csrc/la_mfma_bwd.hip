@@ -17,7 +17,12 @@
 //   dPhi(k_j) = sum_i P_ij Phi(q_i) + R v_j - r,
 //   dv_j      = sum_i A_ij gn_i + R^T Phi(k_j)
 // (k_bwd_kv_mfma, backward over chunks).  k_bwd_q_mfma also writes den_i,
-// c_i and each segment's sum of (R, r); a scan forms the suffixes.
+// c_i and each segment's sum of (R, r); a scan forms the suffixes.  The
+// chain rule through phi takes phi' from the staged bf16 features
+// (phi_d_feat), so the raw q and k rows are not kept.
+//
+// LDS tiles use the padded layout: in these kernels the permuted layout's
+// extra address arithmetic costs more than its bank conflicts save.
 //
 // Layout of the work: one workgroup per (batch, KV head, segment) serving the
 // n_rep query heads.  Each wave computes the chunk's 32x32 tile of A and T
@@ -49,9 +54,7 @@ __device__ __forceinline__ void ld4f(const u16 *p, float *o) {
 }
 
 __device__ __forceinline__ void st4bf(u16 *p, const float *x) {
-    const uint32_t lo = (uint32_t)f2bf(x[0]) | ((uint32_t)f2bf(x[1]) << 16);
-    const uint32_t hi = (uint32_t)f2bf(x[2]) | ((uint32_t)f2bf(x[3]) << 16);
-    *reinterpret_cast<uint2 *>(p) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2 *>(p) = make_uint2(pk2(x[0], x[1]), pk2(x[2], x[3]));
 }
 
 // Accumulator row index of register r for lane half h.
@@ -67,12 +70,13 @@ __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 *
 template <int D, int PHI>
 __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bwd_q_mfma(Args a) {
-    constexpr int F = D, NW = D / 32, NT = 4 * D, LDF = F + 8, LDV = D + 8;
-    __shared__ __attribute__((aligned(16))) u16 sK[kCb * LDF];
-    __shared__ __attribute__((aligned(16))) u16 sV[kCb * LDV];
-    __shared__ __attribute__((aligned(16))) u16 sQ[kCb * LDF];
-    __shared__ __attribute__((aligned(16))) u16 sQr[kCb * LDV];
-    __shared__ __attribute__((aligned(16))) u16 sG[kCb * LDV];
+    constexpr int F = D, NW = D / 32, NT = 4 * D;
+    using TF = Pad<F>;
+    using TD = Pad<D>;
+    __shared__ __attribute__((aligned(16))) u16 sK[kCb * TF::ld];
+    __shared__ __attribute__((aligned(16))) u16 sV[kCb * TD::ld];
+    __shared__ __attribute__((aligned(16))) u16 sQ[kCb * TF::ld];
+    __shared__ __attribute__((aligned(16))) u16 sG[kCb * TD::ld];
     __shared__ __attribute__((aligned(16))) float sz[F];
     __shared__ __attribute__((aligned(16))) float sInv[kCb];
     __shared__ float sQZ[kCb], sCc[kCb], sQU[NW][kCb];
@@ -118,14 +122,13 @@ void k_bwd_q_mfma(Args a) {
     rG.load(gbase + bh0 * a.N * D, row0, a.N);
     for (int c0 = row0; c0 < row1; c0 += kCb) {
         __syncthreads();
-        rK.template store_feat<PHI, false>(sK, LDF, c0, a.N, a.cw, a.sw, nullptr, nullptr);
-        rV.store(sV, LDV);
+        rK.template store_feat<PHI, false, TF>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rV.template store<TD>(sV);
         for (int rep = 0; rep < a.nrep; ++rep) {
             const size_t bh = bh0 + rep;
             if (rep > 0) __syncthreads();
-            rQ.template store_feat<PHI, false>(sQ, LDF, c0, a.N, a.cw, a.sw, sz, sQZ);
-            rQ.store(sQr, LDV);
-            rG.store(sG, LDV);
+            rQ.template store_feat<PHI, false, TF>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+            rG.template store<TD>(sG);
             __syncthreads();
             if (rep + 1 < a.nrep) {
                 rQ.load(qbase + (bh + 1) * a.N * D, c0, a.N);
@@ -145,16 +148,15 @@ void k_bwd_q_mfma(Args a) {
                 Tt = zero16();
 #pragma unroll 4
                 for (int s = 0; s < F / 16; ++s)
-                    At = mfma(ld8(sK + l32 * LDF + 16 * s + 8 * h), ld8(sQ + l32 * LDF + 16 * s + 8 * h), At);
+                    At = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), At);
 #pragma unroll 4
                 for (int s = 0; s < D / 16; ++s)
-                    Tt = mfma(ld8(sV + l32 * LDV + 16 * s + 8 * h), ld8(sG + l32 * LDV + 16 * s + 8 * h), Tt);
+                    Tt = mfma(ld8<TD>(sV, l32, 16 * s + 8 * h), ld8<TD>(sG, l32, 16 * s + 8 * h), Tt);
                 float dA = 0.f;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const bool keep = acc_row(r, h) <= l32;
                     const float x = keep ? (float)(__bf16)At[r] : 0.f;
-                    Tt[r] = keep ? Tt[r] : 0.f;
                     dA += x;
                     aT += x * Tt[r];
                 }
@@ -167,18 +169,18 @@ void k_bwd_q_mfma(Args a) {
                 for (int db = 0; db < NW; ++db)
 #pragma unroll
                     for (int s = 0; s < 2; ++s)
-                        U = mfma(acc_op(X[db], s), ld4x2(sG + l32 * LDV + 32 * db + 16 * s + 4 * h), U);
+                        U = mfma(acc_op(X[db], s), ld4x2<TD>(sG, l32, 32 * db + 16 * s + 4 * h), U);
                 float qu = 0.f, x4[4];
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
-                    ld4f(sQ + l32 * LDF + 32 * w + 8 * q4 + 4 * h, x4);
+                    ld4f(sQ + TF::at(l32, 32 * w + 8 * q4 + 4 * h), x4);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) qu += x4[e] * U[4 * q4 + e];
                 }
                 qu += __shfl_xor(qu, 32);
                 if (h == 0) {
                     sQU[w][l32] = qu;
-                    if (w == 0) sInv[l32] = 1.f / den;
+                    if (w == 0) sInv[l32] = rcp(den);
                 }
             }
             __syncthreads();
@@ -186,7 +188,7 @@ void k_bwd_q_mfma(Args a) {
                 float gsum = aT;
 #pragma unroll
                 for (int ww = 0; ww < NW; ++ww) gsum += sQU[ww][l32];
-                const float inv = 1.f / den;
+                const float inv = rcp(den);
                 const float c = ok ? gsum * inv * inv : 0.f;
                 if (w == 0 && h == 0) {
                     sCc[l32] = c;
@@ -203,17 +205,17 @@ void k_bwd_q_mfma(Args a) {
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     const int k0 = 16 * s + 4 * h;
-                    const bf16x8 ka = tr8(tr_addr(sK, LDF, k0, 32 * w), tr_addr(sK, LDF, k0 + 8, 32 * w));
+                    const bf16x8 ka = tr8(tr_addr<TF>(sK, k0, 32 * w), tr_addr<TF>(sK, k0 + 8, 32 * w));
                     Qd = mfma(ka, acc_op(Tt, s), Qd);
                 }
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int f0 = 32 * w + 8 * q4 + 4 * h;
-                    float qr[4];
-                    ld4f(sQr + l32 * LDV + f0, qr);
+                    float qf[4];
+                    ld4f(sQ + TF::at(l32, f0), qf);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        Qd[4 * q4 + e] = phi_d<PHI>(qr[e]) *
+                        Qd[4 * q4 + e] = phi_d_feat<PHI>(qf[e]) *
                                          (Qd[4 * q4 + e] + U[4 * q4 + e] * inv - sz[f0 + e] * c);
                 }
                 const int row = c0 + l32;
@@ -231,7 +233,7 @@ void k_bwd_q_mfma(Args a) {
 #pragma unroll
                 for (int s = 0; s < kCb / 16; ++s) {
                     const int k0 = 16 * s + 8 * h;
-                    bf16x8 qa = tr8(tr_addr(sQ, LDF, k0, 32 * wr), tr_addr(sQ, LDF, k0 + 4, 32 * wr));
+                    bf16x8 qa = tr8(tr_addr<TF>(sQ, k0, 32 * wr), tr_addr<TF>(sQ, k0 + 4, 32 * wr));
                     const float4 i0 = *reinterpret_cast<const float4 *>(sInv + k0);
                     const float4 i1 = *reinterpret_cast<const float4 *>(sInv + k0 + 4);
                     const float sc[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
@@ -239,7 +241,7 @@ void k_bwd_q_mfma(Args a) {
                     for (int e = 0; e < 8; ++e) qa[e] = (__bf16)((float)qa[e] * sc[e]);
 #pragma unroll
                     for (int db = 0; db < NW; ++db) {
-                        const bf16x8 gb = tr8(tr_addr(sG, LDV, k0, 32 * db), tr_addr(sG, LDV, k0 + 4, 32 * db));
+                        const bf16x8 gb = tr8(tr_addr<TD>(sG, k0, 32 * db), tr_addr<TD>(sG, k0 + 4, 32 * db));
                         X[db] = mfma(qa, gb, X[db]);
                     }
                 }
@@ -247,7 +249,7 @@ void k_bwd_q_mfma(Args a) {
                 if (tf < F) {
                     float acc = 0.f;
 #pragma unroll 8
-                    for (int i = 0; i < kCb; ++i) acc += sCc[i] * bf2f(sQ[i * LDF + tf]);
+                    for (int i = 0; i < kCb; ++i) acc += sCc[i] * bf2f(sQ[TF::at(i, tf)]);
                     rr += acc;
                 }
             }
@@ -257,11 +259,11 @@ void k_bwd_q_mfma(Args a) {
 #pragma unroll
             for (int s = 0; s < kCb / 16; ++s) {
                 const int k0 = 16 * s + 8 * h;
-                const bf16x8 kb = tr8(tr_addr(sK, LDF, k0, 32 * w), tr_addr(sK, LDF, k0 + 4, 32 * w));
+                const bf16x8 kb = tr8(tr_addr<TF>(sK, k0, 32 * w), tr_addr<TF>(sK, k0 + 4, 32 * w));
                 Z = mfma(kb, one, Z);
 #pragma unroll
                 for (int db = 0; db < NW; ++db) {
-                    const bf16x8 va = tr8(tr_addr(sV, LDV, k0, 32 * db), tr_addr(sV, LDV, k0 + 4, 32 * db));
+                    const bf16x8 va = tr8(tr_addr<TD>(sV, k0, 32 * db), tr_addr<TD>(sV, k0 + 4, 32 * db));
                     X[db] = mfma(va, kb, X[db]);
                 }
             }
@@ -295,13 +297,14 @@ void k_bwd_q_mfma(Args a) {
 template <int D, int PHI>
 __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bwd_kv_mfma(Args a) {
-    constexpr int F = D, NW = D / 32, NT = 2 * D, LDF = F + 8, LDV = D + 8;
-    __shared__ __attribute__((aligned(16))) u16 sK[kCb * LDF];
-    __shared__ __attribute__((aligned(16))) u16 sV[kCb * LDV];
-    __shared__ __attribute__((aligned(16))) u16 sKr[kCb * LDV];
-    __shared__ __attribute__((aligned(16))) u16 sQ[kCb * LDF];
-    __shared__ __attribute__((aligned(16))) u16 sG[kCb * LDV];
-    __shared__ __attribute__((aligned(16))) u16 sR[F * LDV];
+    constexpr int F = D, NW = D / 32, NT = 2 * D;
+    using TF = Pad<F>;
+    using TD = Pad<D>;
+    __shared__ __attribute__((aligned(16))) u16 sK[kCb * TF::ld];
+    __shared__ __attribute__((aligned(16))) u16 sV[kCb * TD::ld];
+    __shared__ __attribute__((aligned(16))) u16 sQ[kCb * TF::ld];
+    __shared__ __attribute__((aligned(16))) u16 sG[kCb * TD::ld];
+    __shared__ __attribute__((aligned(16))) u16 sR[F * TD::ld];
     __shared__ __attribute__((aligned(16))) float sCc[kCb];
     __shared__ float sr[F];
 
@@ -340,12 +343,11 @@ void k_bwd_kv_mfma(Args a) {
         const int c0 = row0 + ci * kCb;
         __syncthreads();
         if (pend_c0 >= 0) {
-            store_rows<D, NT>(dkh, sQ, LDF, pend_c0, a.N);
-            store_rows<D, NT>(dvh, sG, LDV, pend_c0, a.N);
+            store_rows<D, NT, TD>(dkh, sQ, pend_c0, a.N);
+            store_rows<D, NT, TD>(dvh, sG, pend_c0, a.N);
         }
-        rK.template store_feat<PHI, false>(sK, LDF, c0, a.N, a.cw, a.sw, nullptr, nullptr);
-        rK.store(sKr, LDV);
-        rV.store(sV, LDV);
+        rK.template store_feat<PHI, false, TF>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rV.template store<TD>(sV);
         // R (bf16, [feature][value]) for the value-gradient's state term
 #pragma unroll
         for (int db = 0; db < NW; ++db)
@@ -354,7 +356,7 @@ void k_bwd_kv_mfma(Args a) {
                 float x[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[e] = Rt[db][4 * q4 + e];
-                st4bf(sR + (32 * w + l32) * LDV + 32 * db + 8 * q4 + 4 * h, x);
+                st4bf(sR + TD::at(32 * w + l32, 32 * db + 8 * q4 + 4 * h), x);
             }
         __syncthreads();
 
@@ -364,12 +366,12 @@ void k_bwd_kv_mfma(Args a) {
         for (int db = 0; db < NW; ++db)
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                dK = mfma(acc_op(Rt[db], s), ld4x2(sV + l32 * LDV + 32 * db + 16 * s + 4 * h), dK);
+                dK = mfma(acc_op(Rt[db], s), ld4x2<TD>(sV, l32, 32 * db + 16 * s + 4 * h), dK);
 #pragma unroll 4
         for (int s = 0; s < F / 16; ++s) {
             const int k0 = 16 * s + 8 * h;
-            dV = mfma(tr8(tr_addr(sR, LDV, k0, 32 * w), tr_addr(sR, LDV, k0 + 4, 32 * w)),
-                      ld8(sK + l32 * LDF + 16 * s + 8 * h), dV);
+            dV = mfma(tr8(tr_addr<TD>(sR, k0, 32 * w), tr_addr<TD>(sR, k0 + 4, 32 * w)),
+                      ld8<TF>(sK, l32, 16 * s + 8 * h), dV);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) dK[r] -= sr[32 * w + acc_row(r, h)];
@@ -377,22 +379,19 @@ void k_bwd_kv_mfma(Args a) {
         for (int rep = 0; rep < a.nrep; ++rep) {
             const size_t bh = bh0 + rep;
             __syncthreads();   // previous head's LDS reads and every read of r are done
-            rQ.template store_feat<PHI, false>(sQ, LDF, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+            rQ.template store_feat<PHI, false, TF>(sQ, c0, a.N, a.cw, a.sw, nullptr, nullptr);
             {   // gn = g / den in LDS (rows past N: zeros), and c
                 constexpr int NV = RawTile<D, NT, kCb>::NV, V8 = D / 8;
 #pragma unroll
                 for (int k = 0; k < NV; ++k) {
                     const int idx = t + k * NT, i = idx / V8, c8 = (idx % V8) * 8, row = c0 + i;
-                    const float inv = row < a.N ? 1.f / a.ws_den[bh * a.N + row] : 0.f;
+                    const float inv = row < a.N ? rcp(a.ws_den[bh * a.N + row]) : 0.f;
                     const uint4 u = rG.v[k];
                     uint32_t wds[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float lo = __uint_as_float(wds[e] << 16) * inv;
-                        const float hi = __uint_as_float(wds[e] & 0xffff0000u) * inv;
-                        wds[e] = (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
-                    }
-                    *reinterpret_cast<uint4 *>(sG + i * LDV + c8) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+                    for (int e = 0; e < 4; ++e)
+                        wds[e] = pk2(__uint_as_float(wds[e] << 16) * inv, __uint_as_float(wds[e] & 0xffff0000u) * inv);
+                    *reinterpret_cast<uint4 *>(sG + TD::at(i, c8)) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
                 }
                 for (int i = t; i < kCb; i += NT) sCc[i] = c0 + i < a.N ? a.ws_c[bh * a.N + c0 + i] : 0.f;
             }
@@ -415,7 +414,7 @@ void k_bwd_kv_mfma(Args a) {
                 f32x16 A = zero16();
 #pragma unroll 4
                 for (int s = 0; s < F / 16; ++s)
-                    A = mfma(ld8(sQ + l32 * LDF + 16 * s + 8 * h), ld8(sK + l32 * LDF + 16 * s + 8 * h), A);
+                    A = mfma(ld8<TF>(sQ, l32, 16 * s + 8 * h), ld8<TF>(sK, l32, 16 * s + 8 * h), A);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) A[r] = acc_row(r, h) >= l32 ? A[r] : 0.f;
                 Aop[0] = acc_op(A, 0);
@@ -425,7 +424,7 @@ void k_bwd_kv_mfma(Args a) {
                 f32x16 P = zero16();
 #pragma unroll 4
                 for (int s = 0; s < D / 16; ++s)
-                    P = mfma(ld8(sG + l32 * LDV + 16 * s + 8 * h), ld8(sV + l32 * LDV + 16 * s + 8 * h), P);
+                    P = mfma(ld8<TD>(sG, l32, 16 * s + 8 * h), ld8<TD>(sV, l32, 16 * s + 8 * h), P);
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const float4 cv = *reinterpret_cast<const float4 *>(sCc + 8 * q4 + 4 * h);
@@ -443,24 +442,24 @@ void k_bwd_kv_mfma(Args a) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const int k0 = 16 * s + 4 * h;
-                dK = mfma(tr8(tr_addr(sQ, LDF, k0, 32 * w), tr_addr(sQ, LDF, k0 + 8, 32 * w)), Pop[s], dK);
-                dV = mfma(tr8(tr_addr(sG, LDV, k0, 32 * w), tr_addr(sG, LDV, k0 + 8, 32 * w)), Aop[s], dV);
+                dK = mfma(tr8(tr_addr<TF>(sQ, k0, 32 * w), tr_addr<TF>(sQ, k0 + 8, 32 * w)), Pop[s], dK);
+                dV = mfma(tr8(tr_addr<TD>(sG, k0, 32 * w), tr_addr<TD>(sG, k0 + 8, 32 * w)), Aop[s], dV);
             }
             // R^T += gn^T Phi(Q) for the rows of this chunk; r += Phi(Q)^T c
 #pragma unroll
             for (int s = 0; s < kCb / 16; ++s) {
                 const int k0 = 16 * s + 8 * h;
-                const bf16x8 qb = tr8(tr_addr(sQ, LDF, k0, 32 * w), tr_addr(sQ, LDF, k0 + 4, 32 * w));
+                const bf16x8 qb = tr8(tr_addr<TF>(sQ, k0, 32 * w), tr_addr<TF>(sQ, k0 + 4, 32 * w));
 #pragma unroll
                 for (int db = 0; db < NW; ++db) {
-                    const bf16x8 ga = tr8(tr_addr(sG, LDV, k0, 32 * db), tr_addr(sG, LDV, k0 + 4, 32 * db));
+                    const bf16x8 ga = tr8(tr_addr<TD>(sG, k0, 32 * db), tr_addr<TD>(sG, k0 + 4, 32 * db));
                     Rt[db] = mfma(ga, qb, Rt[db]);
                 }
             }
             if (t < F) {
                 float acc = 0.f;
 #pragma unroll 8
-                for (int i = 0; i < kCb; ++i) acc += sCc[i] * bf2f(sQ[i * LDF + t]);
+                for (int i = 0; i < kCb; ++i) acc += sCc[i] * bf2f(sQ[TF::at(i, t)]);
                 sr[t] += acc;
             }
         }
@@ -470,19 +469,19 @@ void k_bwd_kv_mfma(Args a) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const int f0 = 32 * w + 8 * q4 + 4 * h;
-            float kr[4];
-            ld4f(sKr + l32 * LDV + f0, kr);
+            float kf[4];
+            ld4f(sK + TF::at(l32, f0), kf);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dK[4 * q4 + e] *= phi_d<PHI>(kr[e]);
+            for (int e = 0; e < 4; ++e) dK[4 * q4 + e] *= phi_d_feat<PHI>(kf[e]);
         }
-        stage_out(sQ, LDF, dK, 1.f, 32 * w);
-        stage_out(sG, LDV, dV, 1.f, 32 * w);
+        stage_out<TF>(sQ, dK, 1.f, 32 * w);
+        stage_out<TD>(sG, dV, 1.f, 32 * w);
         pend_c0 = c0;
     }
     __syncthreads();
     if (pend_c0 >= 0) {
-        store_rows<D, NT>(dkh, sQ, LDF, pend_c0, a.N);
-        store_rows<D, NT>(dvh, sG, LDV, pend_c0, a.N);
+        store_rows<D, NT, TD>(dkh, sQ, pend_c0, a.N);
+        store_rows<D, NT, TD>(dvh, sG, pend_c0, a.N);
     }
 }
 

@@ -21,6 +21,8 @@
 // tiles of A^T (keys x queries) itself, so no C x C data crosses waves.
 // Operands come from LDS tiles stored row-major; contractions over the row
 // (token) index read them with ds_read_b64_tr_b16.
+#include <type_traits>
+
 #include "la_common.h"
 #include "la_kernels.h"
 #include "la_mfma.h"
@@ -31,19 +33,33 @@ namespace {
 
 using namespace mf;
 
+// LDS layout of the forward's tiles: the row-permuted padded layout, under
+// which every transposed read and every 16-row read is conflict-free.
+template <int D, int F>
+struct FwdTiles {
+    using TF = PadI<F>;
+    using TD = PadI<D>;
+};
+
 // S[fb] += Phi(K)^T V over the 64 rows of the staged chunk, for this wave's
-// value columns (natural k order: lane half h holds rows 16s + 8h .. +7).
-template <int F, int LDF, int LDV>
-__device__ __forceinline__ void state_update(f32x16 *S, const u16 *sK, const u16 *sV, int w) {
+// value columns (natural k order: lane half h holds rows 16s + 8h .. +7), and
+// z += Phi(K)^T 1 for the feature blocks fb = w (mod D/32) into Z[fb / (D/32)].
+template <int D, int F>
+__device__ __forceinline__ void state_update(f32x16 *S, f32x16 *Z, const u16 *sK, const u16 *sV, int w) {
+    using TF = typename FwdTiles<D, F>::TF;
+    using TD = typename FwdTiles<D, F>::TD;
+    constexpr int NW = D / 32;
     const int h = (threadIdx.x & 63) >> 5;
+    const bf16x8 one = ones8();
 #pragma unroll
     for (int s = 0; s < kC / 16; ++s) {
         const int k0 = 16 * s + 8 * h;
-        const bf16x8 vb = tr8(tr_addr(sV, LDV, k0, 32 * w), tr_addr(sV, LDV, k0 + 4, 32 * w));
+        const bf16x8 vb = tr8(tr_addr<TD>(sV, k0, 32 * w), tr_addr<TD>(sV, k0 + 4, 32 * w));
 #pragma unroll
         for (int fb = 0; fb < F / 32; ++fb) {
-            const bf16x8 ka = tr8(tr_addr(sK, LDF, k0, 32 * fb), tr_addr(sK, LDF, k0 + 4, 32 * fb));
+            const bf16x8 ka = tr8(tr_addr<TF>(sK, k0, 32 * fb), tr_addr<TF>(sK, k0 + 4, 32 * fb));
             S[fb] = mfma(ka, vb, S[fb]);
+            if (fb % NW == w) Z[fb / NW] = mfma(ka, one, Z[fb / NW]);
         }
     }
 }
@@ -55,34 +71,35 @@ __device__ __forceinline__ void state_update(f32x16 *S, const u16 *sK, const u16
 // before the current chunk's products.
 // ---------------------------------------------------------------------------
 template <int D, int F, int PHI, bool COS>
-__global__ __launch_bounds__(D * 2) void k_state_mfma(Args a) {
-    constexpr int NT = D * 2, LDF = F + 8, LDV = D + 8, FB = F / 32;
-    __shared__ __attribute__((aligned(16))) u16 sK[kC * LDF];
-    __shared__ __attribute__((aligned(16))) u16 sV[kC * LDV];
+__global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 ? 2 : 1))) void k_state_mfma(Args a) {
+    using TF = typename FwdTiles<D, F>::TF;
+    using TD = typename FwdTiles<D, F>::TD;
+    constexpr int NT = D * 2, NW = D / 32, FB = F / 32, ZB = FB / NW;
+    __shared__ __attribute__((aligned(16))) u16 sK[kC * TF::ld];
+    __shared__ __attribute__((aligned(16))) u16 sV[kC * TD::ld];
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
     const int t = threadIdx.x, l = t & 63, w = t >> 6, h = l >> 5, l32 = l & 31;
     const u16 *kh = static_cast<const u16 *>(a.k) + (size_t)bg * a.N * D;
     const u16 *vh = static_cast<const u16 *>(a.v) + (size_t)bg * a.N * D;
-    f32x16 S[FB];
+    f32x16 S[FB], Z[ZB];
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb) S[fb] = zero16();
-    float z = 0.f;
+#pragma unroll
+    for (int c = 0; c < ZB; ++c) Z[c] = zero16();
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
     RawTile<D, NT> rK, rV;
     rK.load(kh, row0, a.N);
     rV.load(vh, row0, a.N);
     for (int c0 = row0; c0 < row1; c0 += kC) {
         __syncthreads();
-        rK.template store_feat<PHI, COS>(sK, LDF, c0, a.N, a.cw, a.sw, nullptr, nullptr);
-        rV.store(sV, LDV);
+        rK.template store_feat<PHI, COS, TF>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rV.template store<TD>(sV);
         __syncthreads();
         if (c0 + kC < row1) {
             rK.load(kh, c0 + kC, a.N);
             rV.load(vh, c0 + kC, a.N);
         }
-        state_update<F, LDF, LDV>(S, sK, sV, w);
-        if (t < F)
-            for (int j = 0; j < kC; ++j) z += bf2f(sK[j * LDF + t]);
+        state_update<D, F>(S, Z, sK, sV, w);
     }
     float *out = a.ws_S + ((size_t)bg * (a.nseg + 1) + seg) * ((size_t)F * D + F);
 #pragma unroll
@@ -92,7 +109,14 @@ __global__ __launch_bounds__(D * 2) void k_state_mfma(Args a) {
             const int f = 32 * fb + 8 * (r >> 2) + 4 * h + (r & 3);
             out[(size_t)f * D + 32 * w + l32] = S[fb][r];
         }
-    if (t < F) out[(size_t)F * D + t] = z;
+    // every column of a z tile holds z: lane 0 of each half writes its rows
+    if (l32 == 0) {
+#pragma unroll
+        for (int c = 0; c < ZB; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                out[(size_t)F * D + 32 * (w + NW * c) + 8 * (r >> 2) + 4 * h + (r & 3)] = Z[c][r];
+    }
 }
 
 constexpr int kCf = 32;   // forward chunk length: one 32x32 tile of A per head
@@ -108,11 +132,13 @@ constexpr int kCf = 32;   // forward chunk length: one 32x32 tile of A per head
 // ---------------------------------------------------------------------------
 template <int D, int F, int PHI, bool COS>
 __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 ? 2 : 1))) void k_fwd_mfma(Args a) {
-    constexpr int NT = D * 2, NW = D / 32, LDF = F + 8, LDV = D + 8, FB = F / 32, ZB = FB / NW;
-    __shared__ __attribute__((aligned(16))) u16 sK[kCf * LDF];
-    __shared__ __attribute__((aligned(16))) u16 sQ[kCf * LDF];
-    __shared__ __attribute__((aligned(16))) u16 sV[kCf * LDV];
-    __shared__ __attribute__((aligned(16))) u16 sO[kCf * LDV];   // output rows of one head
+    using TF = typename FwdTiles<D, F>::TF;
+    using TD = typename FwdTiles<D, F>::TD;
+    constexpr int NT = D * 2, NW = D / 32, FB = F / 32, ZB = FB / NW;
+    __shared__ __attribute__((aligned(16))) u16 sK[kCf * TF::ld];
+    __shared__ __attribute__((aligned(16))) u16 sQ[kCf * TF::ld];
+    __shared__ __attribute__((aligned(16))) u16 sV[kCf * TD::ld];
+    __shared__ __attribute__((aligned(16))) u16 sO[kCf * TD::ld];   // output rows of one head
     __shared__ __attribute__((aligned(16))) float sz[F];
     __shared__ float sQZ[kCf];
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
@@ -154,16 +180,16 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
     int pend_c0 = 0;
     for (int c0 = row0; c0 < row1; c0 += kCf) {
         __syncthreads();   // previous chunk: every LDS read done, sz updated, sO complete
-        if (pend_oh) store_rows<D, NT>(pend_oh, sO, LDV, pend_c0, a.N);
-        rK.template store_feat<PHI, COS>(sK, LDF, c0, a.N, a.cw, a.sw, nullptr, nullptr);
-        rV.store(sV, LDV);
+        if (pend_oh) store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
+        rK.template store_feat<PHI, COS, TF>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rV.template store<TD>(sV);
         for (int rep = 0; rep < a.nrep; ++rep) {
             u16 *oh = obase + (bh0 + rep) * a.N * D;
             if (rep > 0) {
                 __syncthreads();   // every wave is done with the previous head's sQ; sO complete
-                store_rows<D, NT>(pend_oh, sO, LDV, pend_c0, a.N);
+                store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
             }
-            rQ.template store_feat<PHI, COS>(sQ, LDF, c0, a.N, a.cw, a.sw, sz, sQZ);
+            rQ.template store_feat<PHI, COS, TF>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
             __syncthreads();
             if (rep + 1 < a.nrep) {
                 rQ.load(qbase + (bh0 + rep + 1) * a.N * D, c0, a.N);
@@ -178,7 +204,7 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
             f32x16 T = zero16();
 #pragma unroll 4
             for (int s = 0; s < F / 16; ++s)
-                T = mfma(ld8(sK + l32 * LDF + 16 * s + 8 * h), ld8(sQ + l32 * LDF + 16 * s + 8 * h), T);
+                T = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), T);
             float dsum = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -195,17 +221,16 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const int k0 = 16 * s + 4 * h;
-                const bf16x8 va = tr8(tr_addr(sV, LDV, k0, 32 * w), tr_addr(sV, LDV, k0 + 8, 32 * w));
+                const bf16x8 va = tr8(tr_addr<TD>(sV, k0, 32 * w), tr_addr<TD>(sV, k0 + 8, 32 * w));
                 Nt = mfma(va, s ? B1 : B0, Nt);
             }
-            const u16 *qrow = sQ + l32 * LDF;
 #pragma unroll
             for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
-                    Nt = mfma(acc_op(S[fb], s), ld4x2(qrow + 32 * fb + 16 * s + 4 * h), Nt);
+                    Nt = mfma(acc_op(S[fb], s), ld4x2<TF>(sQ, l32, 32 * fb + 16 * s + 4 * h), Nt);
             const float den = dsum + sQZ[l32] + a.eps;
-            stage_out(sO, LDV, Nt, 1.f / den, 32 * w);
+            stage_out<TD>(sO, Nt, rcp(den), 32 * w);
             pend_oh = oh;
             pend_c0 = c0;
         }
@@ -213,10 +238,10 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
 #pragma unroll
         for (int s = 0; s < kCf / 16; ++s) {
             const int k0 = 16 * s + 8 * h;
-            const bf16x8 vb = tr8(tr_addr(sV, LDV, k0, 32 * w), tr_addr(sV, LDV, k0 + 4, 32 * w));
+            const bf16x8 vb = tr8(tr_addr<TD>(sV, k0, 32 * w), tr_addr<TD>(sV, k0 + 4, 32 * w));
 #pragma unroll
             for (int fb = 0; fb < FB; ++fb) {
-                const bf16x8 ka = tr8(tr_addr(sK, LDF, k0, 32 * fb), tr_addr(sK, LDF, k0 + 4, 32 * fb));
+                const bf16x8 ka = tr8(tr_addr<TF>(sK, k0, 32 * fb), tr_addr<TF>(sK, k0 + 4, 32 * fb));
                 S[fb] = mfma(ka, vb, S[fb]);
                 if (fb % NW == w) Z[fb / NW] = mfma(ka, one, Z[fb / NW]);
             }
@@ -232,7 +257,7 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
         }
     }
     __syncthreads();
-    if (pend_oh) store_rows<D, NT>(pend_oh, sO, LDV, pend_c0, a.N);
+    if (pend_oh) store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
 }
 
 template <int D, int F, int PHI, bool COS>
