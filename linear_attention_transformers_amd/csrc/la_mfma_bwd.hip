@@ -57,6 +57,30 @@ __device__ __forceinline__ void st4bf(u16 *p, const float *x) {
     *reinterpret_cast<uint2 *>(p) = make_uint2(pk2(x[0], x[1]), pk2(x[2], x[3]));
 }
 
+// An accumulator tile through LDS in its register layout: register 4q + e of
+// lane l at float (64q + l) * 4 + e, so each 16-byte access of a wave is
+// contiguous.
+__device__ __forceinline__ void put_acc(float *dst, const f32x16 &x) {
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4 *>(dst + (64 * q + l) * 4) = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+}
+
+__device__ __forceinline__ f32x16 get_acc(const float *src) {
+    const int l = threadIdx.x & 63;
+    f32x16 x;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4 *>(src + (64 * q + l) * 4);
+        x[4 * q] = v.x;
+        x[4 * q + 1] = v.y;
+        x[4 * q + 2] = v.z;
+        x[4 * q + 3] = v.w;
+    }
+    return x;
+}
+
 // Accumulator row index of register r for lane half h.
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
@@ -65,7 +89,10 @@ __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 *
 // segment).  Waves 0 .. D/32-1 ("state waves") hold S^T and z and produce
 // dq; waves D/32 .. 2D/32-1 ("R waves") accumulate the segment's
 // R = sum_i Phi(q_i) gn_i^T (feature block w - D/32 x all value blocks) and
-// r = sum_i c_i Phi(q_i), summed over the group's query heads.
+// r = sum_i c_i Phi(q_i), summed over the group's query heads.  Per chunk and
+// head the first two R waves also compute the 32x32 tiles A^T (with the
+// denominators) and T^T and pass them to the state waves through LDS, which
+// meanwhile form U = S g: the state waves' chain is the kernel's critical path.
 // ---------------------------------------------------------------------------
 template <int D, int PHI>
 __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2)))
@@ -79,7 +106,8 @@ void k_bwd_q_mfma(Args a) {
     __shared__ __attribute__((aligned(16))) u16 sG[kCb * TD::ld];
     __shared__ __attribute__((aligned(16))) float sz[F];
     __shared__ __attribute__((aligned(16))) float sInv[kCb];
-    __shared__ float sQZ[kCb], sCc[kCb], sQU[NW][kCb];
+    __shared__ __attribute__((aligned(16))) float sAt[64 * 16], sTt[64 * 16];   // accumulator tiles
+    __shared__ float sQZ[kCb], sCc[kCb], sDen[kCb], sQU[NW][kCb];
 
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
@@ -111,7 +139,7 @@ void k_bwd_q_mfma(Args a) {
         for (int db = 0; db < NW; ++db) X[db] = zero16();
     }
     for (int e = t; e < F; e += NT) sz[e] = Sp[(size_t)F * D + e];
-    float rr = 0.f;   // R waves: thread t - NW*64 < F owns r[feature]
+    float rr = 0.f;   // thread NT - F + f owns r[f]
     const bf16x8 one = ones8();
 
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
@@ -140,29 +168,8 @@ void k_bwd_q_mfma(Args a) {
                 rG.load(gbase + bh0 * a.N * D, c0 + kCb, a.N);
             }
             const bool ok = c0 + l32 < a.N;   // this lane's query row exists
-            f32x16 Tt, U;
-            float den = 1.f, aT = 0.f;
+            f32x16 U;
             if (state_wave) {
-                // A^T, T^T (keys x queries), causal mask, A rounded to bf16
-                f32x16 At = zero16();
-                Tt = zero16();
-#pragma unroll 4
-                for (int s = 0; s < F / 16; ++s)
-                    At = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), At);
-#pragma unroll 4
-                for (int s = 0; s < D / 16; ++s)
-                    Tt = mfma(ld8<TD>(sV, l32, 16 * s + 8 * h), ld8<TD>(sG, l32, 16 * s + 8 * h), Tt);
-                float dA = 0.f;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const bool keep = acc_row(r, h) <= l32;
-                    const float x = keep ? (float)(__bf16)At[r] : 0.f;
-                    dA += x;
-                    aT += x * Tt[r];
-                }
-                dA += __shfl_xor(dA, 32);
-                aT += __shfl_xor(aT, 32);
-                den = ok ? dA + sQZ[l32] + a.eps : 1.f;
                 // U^T = S g (this feature block x the chunk's queries)
                 U = zero16();
 #pragma unroll
@@ -178,22 +185,53 @@ void k_bwd_q_mfma(Args a) {
                     for (int e = 0; e < 4; ++e) qu += x4[e] * U[4 * q4 + e];
                 }
                 qu += __shfl_xor(qu, 32);
-                if (h == 0) {
-                    sQU[w][l32] = qu;
-                    if (w == 0) sInv[l32] = rcp(den);
+                if (h == 0) sQU[w][l32] = qu;
+            } else if (w == NW) {
+                // A^T (keys x queries), causal mask, rounded to bf16 (the
+                // forward's A), the denominators, and the tile for the state waves
+                f32x16 At = zero16();
+#pragma unroll 4
+                for (int s = 0; s < F / 16; ++s)
+                    At = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), At);
+                float dA = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    At[r] = acc_row(r, h) <= l32 ? (float)(__bf16)At[r] : 0.f;
+                    dA += At[r];
                 }
+                dA += __shfl_xor(dA, 32);
+                put_acc(sAt, At);
+                if (h == 0) {
+                    const float den = ok ? dA + sQZ[l32] + a.eps : 1.f;
+                    sDen[l32] = den;
+                    sInv[l32] = rcp(den);
+                }
+            } else if (w == NW + 1) {
+                // T^T = V G^T (keys x queries), unmasked: the state waves mask
+                f32x16 Tt = zero16();
+#pragma unroll 4
+                for (int s = 0; s < D / 16; ++s)
+                    Tt = mfma(ld8<TD>(sV, l32, 16 * s + 8 * h), ld8<TD>(sG, l32, 16 * s + 8 * h), Tt);
+                put_acc(sTt, Tt);
             }
             __syncthreads();
             if (state_wave) {
+                // c = (sum_j A_ij T_ij + Phi(q_i).U_i) / den_i^2
+                f32x16 Tt = get_acc(sTt);
+                const f32x16 At = get_acc(sAt);
+                float aT = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) aT += At[r] * Tt[r];
+                aT += __shfl_xor(aT, 32);
                 float gsum = aT;
 #pragma unroll
                 for (int ww = 0; ww < NW; ++ww) gsum += sQU[ww][l32];
-                const float inv = rcp(den);
+                const float inv = sInv[l32];
                 const float c = ok ? gsum * inv * inv : 0.f;
                 if (w == 0 && h == 0) {
                     sCc[l32] = c;
                     if (ok) {
-                        a.ws_den[bh * a.N + c0 + l32] = den;
+                        a.ws_den[bh * a.N + c0 + l32] = sDen[l32];
                         a.ws_c[bh * a.N + c0 + l32] = c;
                     }
                 }
@@ -245,8 +283,8 @@ void k_bwd_q_mfma(Args a) {
                         X[db] = mfma(qa, gb, X[db]);
                     }
                 }
-                const int tf = t - NW * 64;
-                if (tf < F) {
+                const int tf = t - (NT - F);   // r: the last F threads
+                if (tf >= 0) {
                     float acc = 0.f;
 #pragma unroll 8
                     for (int i = 0; i < kCb; ++i) acc += sCc[i] * bf2f(sQ[TF::at(i, tf)]);
@@ -283,8 +321,8 @@ void k_bwd_q_mfma(Args a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 Ro[(size_t)(32 * wr + acc_row(r, h)) * D + 32 * db + l32] = X[db][r];
-        const int tf = t - NW * 64;
-        if (tf < F) Ro[(size_t)F * D + tf] = rr;
+        const int tf = t - (NT - F);
+        if (tf >= 0) Ro[(size_t)F * D + tf] = rr;
     }
 }
 
