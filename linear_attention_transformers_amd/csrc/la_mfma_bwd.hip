@@ -93,6 +93,8 @@ __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 *
 // head the first two R waves also compute the 32x32 tiles A^T (with the
 // denominators) and T^T and pass them to the state waves through LDS, which
 // meanwhile form U = S g: the state waves' chain is the kernel's critical path.
+// After that exchange (one barrier) the two wave kinds run independently: the
+// R update needs only 1/den, and the waves that own r recompute c.
 // ---------------------------------------------------------------------------
 template <int D, int PHI>
 __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2)))
@@ -107,7 +109,7 @@ void k_bwd_q_mfma(Args a) {
     __shared__ __attribute__((aligned(16))) float sz[F];
     __shared__ __attribute__((aligned(16))) float sInv[kCb];
     __shared__ __attribute__((aligned(16))) float sAt[64 * 16], sTt[64 * 16];   // accumulator tiles
-    __shared__ float sQZ[kCb], sCc[kCb], sDen[kCb], sQU[NW][kCb];
+    __shared__ float sQZ[kCb], sDen[kCb], sQU[NW][kCb];
 
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
@@ -228,12 +230,9 @@ void k_bwd_q_mfma(Args a) {
                 for (int ww = 0; ww < NW; ++ww) gsum += sQU[ww][l32];
                 const float inv = sInv[l32];
                 const float c = ok ? gsum * inv * inv : 0.f;
-                if (w == 0 && h == 0) {
-                    sCc[l32] = c;
-                    if (ok) {
-                        a.ws_den[bh * a.N + c0 + l32] = sDen[l32];
-                        a.ws_c[bh * a.N + c0 + l32] = c;
-                    }
+                if (w == 0 && h == 0 && ok) {
+                    a.ws_den[bh * a.N + c0 + l32] = sDen[l32];
+                    a.ws_c[bh * a.N + c0 + l32] = c;
                 }
                 // P^T = T^T / den - c (masked), then dPhi(q)^T = Phi(K)^T P^T + U^T / den - z c
 #pragma unroll
@@ -265,7 +264,6 @@ void k_bwd_q_mfma(Args a) {
                     }
                 }
             }
-            __syncthreads();   // sCc and sInv are complete
             if (!state_wave) {
                 // R (feature block wr x every value block) += (Phi(Q) / den)^T G
 #pragma unroll
@@ -283,11 +281,25 @@ void k_bwd_q_mfma(Args a) {
                         X[db] = mfma(qa, gb, X[db]);
                     }
                 }
-                const int tf = t - (NT - F);   // r: the last F threads
-                if (tf >= 0) {
+                if (w >= (NT - F) / 64) {
+                    // r += Phi(Q)^T c: these waves form c_i themselves, in the
+                    // state waves' order (same bits), rather than wait for them
+                    const f32x16 At = get_acc(sAt), Tt = get_acc(sTt);
+                    float aT = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) aT += At[r] * Tt[r];
+                    aT += __shfl_xor(aT, 32);
+                    float gsum = aT;
+#pragma unroll
+                    for (int ww = 0; ww < NW; ++ww) gsum += sQU[ww][l32];
+                    const float inv = sInv[l32];
+                    const float cq = ok ? gsum * inv * inv : 0.f;   // c of query l32
+                    const int tf = t - (NT - F);
                     float acc = 0.f;
-#pragma unroll 8
-                    for (int i = 0; i < kCb; ++i) acc += sCc[i] * bf2f(sQ[TF::at(i, tf)]);
+#pragma unroll
+                    for (int i = 0; i < kCb; ++i)
+                        acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cq), i)) *
+                               bf2f(sQ[TF::at(i, tf)]);
                     rr += acc;
                 }
             }
