@@ -203,22 +203,27 @@ struct RawTile {
     // Features: phi, then with COS [cos_t phi, sin_t phi] (row width 2D),
     // rounded to bf16.  With sz != nullptr, also sQZ[r] = Phi(x_r) . z over
     // the rounded features (fixed-order shuffle reduction across the V8
-    // threads of a row).
+    // threads of a row).  Branch-free: rows >= N hold zeros (load), phi of
+    // them is finite, and a 0/1 row factor folded into the weight zeroes it.
     template <int PHI, bool COS, class L>
     __device__ __forceinline__ void store_feat(u16 *dst, int c0, int N, const float *cw,
                                                const float *sw, const float *sz,
                                                float *sQZ) const {
+        const bool full = c0 + C <= N;
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int idx = threadIdx.x + k * NT, r = idx / V8, c8 = (idx % V8) * 8, t = c0 + r;
+            const bool valid = full || t < N;
+            const int tc = valid ? t : 0;   // an in-range index for the weights
             const uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
             float f[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                f[2 * e] = t < N ? phi_fast<PHI>(__uint_as_float(w4[e] << 16)) : 0.f;
-                f[2 * e + 1] = t < N ? phi_fast<PHI>(__uint_as_float(w4[e] & 0xffff0000u)) : 0.f;
+                f[2 * e] = phi_fast<PHI>(__uint_as_float(w4[e] << 16));
+                f[2 * e + 1] = phi_fast<PHI>(__uint_as_float(w4[e] & 0xffff0000u));
             }
-            const float m0 = COS ? (t < N ? cw[t] : 0.f) : 1.f;
+            const float vf = valid ? 1.f : 0.f;
+            const float m0 = COS ? vf * cw[tc] : vf;
             float qz = 0.f;
             uint32_t o[4];
 #pragma unroll
@@ -230,7 +235,7 @@ struct RawTile {
             }
             *reinterpret_cast<uint4 *>(dst + L::at(r, c8)) = make_uint4(o[0], o[1], o[2], o[3]);
             if constexpr (COS) {
-                const float m1 = t < N ? sw[t] : 0.f;
+                const float m1 = vf * sw[tc];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     o[e] = pk2(m1 * f[2 * e], m1 * f[2 * e + 1]);

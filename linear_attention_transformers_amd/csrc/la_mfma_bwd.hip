@@ -435,7 +435,8 @@ void k_bwd_kv_mfma(Args a) {
 #pragma unroll
                 for (int k = 0; k < NV; ++k) {
                     const int idx = t + k * NT, i = idx / V8, c8 = (idx % V8) * 8, row = c0 + i;
-                    const float inv = row < a.N ? rcp(a.ws_den[bh * a.N + row]) : 0.f;
+                    // rows past N: zeros (their g rows are zeros; den read in range)
+                    const float inv = rcp(a.ws_den[bh * a.N + min(row, a.N - 1)]);
                     const uint4 u = rG.v[k];
                     uint32_t wds[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
