@@ -174,20 +174,20 @@ struct RawTile {
     static_assert(NV * NT == C * V8, "tile must split evenly over the threads");
     uint4 v[NV];
 
+    // One load per vector from a clamped (in-range) row, then rows >= N
+    // zeroed behind a uniform branch: a single straight path (N >= 1).
     __device__ __forceinline__ void load(const u16 *src, int c0, int N) {
-        if (c0 + C <= N) {   // whole tile in range (uniform): no per-row checks
-#pragma unroll
-            for (int k = 0; k < NV; ++k) {
-                const int idx = threadIdx.x + k * NT, r = idx / V8, c8 = (idx % V8) * 8;
-                v[k] = *reinterpret_cast<const uint4 *>(src + (size_t)(c0 + r) * D + c8);
-            }
-            return;
-        }
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int idx = threadIdx.x + k * NT, r = idx / V8, c8 = (idx % V8) * 8;
-            v[k] = make_uint4(0, 0, 0, 0);
-            if (c0 + r < N) v[k] = *reinterpret_cast<const uint4 *>(src + (size_t)(c0 + r) * D + c8);
+            v[k] = *reinterpret_cast<const uint4 *>(src + (size_t)min(c0 + r, N - 1) * D + c8);
+        }
+        if (c0 + C > N) {
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const int r = (threadIdx.x + k * NT) / V8;
+                if (c0 + r >= N) v[k] = make_uint4(0, 0, 0, 0);
+            }
         }
     }
 
@@ -201,11 +201,11 @@ struct RawTile {
     }
 
     // Features: phi, then with COS [cos_t phi, sin_t phi] (row width 2D),
-    // rounded to bf16.  With sz != nullptr, also sQZ[r] = Phi(x_r) . z over
+    // rounded to bf16.  With QZ, also sQZ[r] = Phi(x_r) . z over
     // the rounded features (fixed-order shuffle reduction across the V8
     // threads of a row).  Branch-free: rows >= N hold zeros (load), phi of
     // them is finite, and a 0/1 row factor folded into the weight zeroes it.
-    template <int PHI, bool COS, class L>
+    template <int PHI, bool COS, class L, bool QZ>
     __device__ __forceinline__ void store_feat(u16 *dst, int c0, int N, const float *cw,
                                                const float *sw, const float *sz,
                                                float *sQZ) const {
@@ -229,7 +229,7 @@ struct RawTile {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 o[e] = pk2(m0 * f[2 * e], m0 * f[2 * e + 1]);
-                if (sz)
+                if constexpr (QZ)
                     qz += __uint_as_float(o[e] << 16) * sz[c8 + 2 * e] +
                           __uint_as_float(o[e] & 0xffff0000u) * sz[c8 + 2 * e + 1];
             }
@@ -239,13 +239,13 @@ struct RawTile {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     o[e] = pk2(m1 * f[2 * e], m1 * f[2 * e + 1]);
-                    if (sz)
+                    if constexpr (QZ)
                         qz += __uint_as_float(o[e] << 16) * sz[D + c8 + 2 * e] +
                               __uint_as_float(o[e] & 0xffff0000u) * sz[D + c8 + 2 * e + 1];
                 }
                 *reinterpret_cast<uint4 *>(dst + L::at(r, D + c8)) = make_uint4(o[0], o[1], o[2], o[3]);
             }
-            if (sz) {
+            if constexpr (QZ) {
 #pragma unroll
                 for (int o2 = 1; o2 < V8; o2 <<= 1) qz += __shfl_xor(qz, o2);
                 if (idx % V8 == 0) sQZ[r] = qz;

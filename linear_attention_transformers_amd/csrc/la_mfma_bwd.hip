@@ -113,6 +113,8 @@ void k_bwd_q_mfma(Args a) {
 
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
+    // w is left per-lane: declared uniform, the wave-role branches keep both
+    // roles' registers live and the kernel spills
     const int t = threadIdx.x, l = t & 63, w = t >> 6, h = l >> 5, l32 = l & 31;
     const bool state_wave = w < NW;
     const int wr = w - NW;   // feature block of an R wave
@@ -152,22 +154,24 @@ void k_bwd_q_mfma(Args a) {
     rG.load(gbase + bh0 * a.N * D, row0, a.N);
     for (int c0 = row0; c0 < row1; c0 += kCb) {
         __syncthreads();
-        rK.template store_feat<PHI, false, TF>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rK.template store_feat<PHI, false, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
         rV.template store<TD>(sV);
+        // the next chunk's K, V (unconditional: rows past the segment are
+        // loaded clamped and never used, and no register copies are needed)
+        rK.load(kh, c0 + kCb, a.N);
+        rV.load(vh, c0 + kCb, a.N);
         for (int rep = 0; rep < a.nrep; ++rep) {
             const size_t bh = bh0 + rep;
             if (rep > 0) __syncthreads();
-            rQ.template store_feat<PHI, false, TF>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+            rQ.template store_feat<PHI, false, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
             rG.template store<TD>(sG);
             __syncthreads();
-            if (rep + 1 < a.nrep) {
-                rQ.load(qbase + (bh + 1) * a.N * D, c0, a.N);
-                rG.load(gbase + (bh + 1) * a.N * D, c0, a.N);
-            } else if (c0 + kCb < row1) {
-                rK.load(kh, c0 + kCb, a.N);
-                rV.load(vh, c0 + kCb, a.N);
-                rQ.load(qbase + bh0 * a.N * D, c0 + kCb, a.N);
-                rG.load(gbase + bh0 * a.N * D, c0 + kCb, a.N);
+            {   // Q, G rows of the next head, or of the first head at the next chunk
+                const bool last = rep + 1 == a.nrep;
+                const size_t hn = bh0 + (last ? 0 : rep + 1);
+                const int cn = last ? c0 + kCb : c0;
+                rQ.load(qbase + hn * a.N * D, cn, a.N);
+                rG.load(gbase + hn * a.N * D, cn, a.N);
             }
             const bool ok = c0 + l32 < a.N;   // this lane's query row exists
             f32x16 U;
@@ -360,7 +364,8 @@ void k_bwd_kv_mfma(Args a) {
 
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
-    const int t = threadIdx.x, l = t & 63, w = t >> 6, h = l >> 5, l32 = l & 31;
+    const int t = threadIdx.x, l = t & 63, h = l >> 5, l32 = l & 31;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index, uniform
     const size_t SD = (size_t)F * D + F;
     const u16 *kh = static_cast<const u16 *>(a.k) + (size_t)bg * a.N * D;
     const u16 *vh = static_cast<const u16 *>(a.v) + (size_t)bg * a.N * D;
@@ -381,12 +386,21 @@ void k_bwd_kv_mfma(Args a) {
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
     const int nch = (row1 - row0 + kCb - 1) / kCb;
     RawTile<D, NT, kCb> rK, rV, rQ, rG;
+    constexpr int NV = RawTile<D, NT, kCb>::NV, V8 = D / 8;
+    float pden[NV], pc;   // den of this thread's G rows and c of query t % 32, prefetched
+    auto load_dc = [&](size_t hh, int cc) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+            pden[k] = a.ws_den[hh * a.N + min(cc + (t + k * NT) / V8, a.N - 1)];
+        pc = a.ws_c[hh * a.N + min(cc + (t & (kCb - 1)), a.N - 1)];
+    };
     {
         const int c0 = row0 + (nch - 1) * kCb;
         rK.load(kh, c0, a.N);
         rV.load(vh, c0, a.N);
         rQ.load(qbase + bh0 * a.N * D, c0, a.N);
         rG.load(gbase + bh0 * a.N * D, c0, a.N);
+        load_dc(bh0, c0);
     }
     int pend_c0 = -1;   // dk, dv rows of the previous chunk staged in sQ, sG
     for (int ci = nch - 1; ci >= 0; --ci) {
@@ -396,8 +410,11 @@ void k_bwd_kv_mfma(Args a) {
             store_rows<D, NT, TD>(dkh, sQ, pend_c0, a.N);
             store_rows<D, NT, TD>(dvh, sG, pend_c0, a.N);
         }
-        rK.template store_feat<PHI, false, TF>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rK.template store_feat<PHI, false, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
         rV.template store<TD>(sV);
+        const int cn = ci > 0 ? c0 - kCb : c0;   // next chunk (none: reload this one)
+        rK.load(kh, cn, a.N);
+        rV.load(vh, cn, a.N);
         // R (bf16, [feature][value]) for the value-gradient's state term
 #pragma unroll
         for (int db = 0; db < NW; ++db)
@@ -427,16 +444,13 @@ void k_bwd_kv_mfma(Args a) {
         for (int r = 0; r < 16; ++r) dK[r] -= sr[32 * w + acc_row(r, h)];
 
         for (int rep = 0; rep < a.nrep; ++rep) {
-            const size_t bh = bh0 + rep;
             __syncthreads();   // previous head's LDS reads and every read of r are done
-            rQ.template store_feat<PHI, false, TF>(sQ, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+            rQ.template store_feat<PHI, false, TF, false>(sQ, c0, a.N, a.cw, a.sw, nullptr, nullptr);
             {   // gn = g / den in LDS (rows past N: zeros), and c
-                constexpr int NV = RawTile<D, NT, kCb>::NV, V8 = D / 8;
 #pragma unroll
                 for (int k = 0; k < NV; ++k) {
                     const int idx = t + k * NT, i = idx / V8, c8 = (idx % V8) * 8, row = c0 + i;
-                    // rows past N: zeros (their g rows are zeros; den read in range)
-                    const float inv = rcp(a.ws_den[bh * a.N + min(row, a.N - 1)]);
+                    const float inv = row < a.N ? rcp(pden[k]) : 0.f;
                     const uint4 u = rG.v[k];
                     uint32_t wds[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -444,18 +458,16 @@ void k_bwd_kv_mfma(Args a) {
                         wds[e] = pk2(__uint_as_float(wds[e] << 16) * inv, __uint_as_float(wds[e] & 0xffff0000u) * inv);
                     *reinterpret_cast<uint4 *>(sG + TD::at(i, c8)) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
                 }
-                for (int i = t; i < kCb; i += NT) sCc[i] = c0 + i < a.N ? a.ws_c[bh * a.N + c0 + i] : 0.f;
+                if (t < kCb) sCc[t] = c0 + t < a.N ? pc : 0.f;
             }
             __syncthreads();
-            if (rep + 1 < a.nrep) {
-                rQ.load(qbase + (bh + 1) * a.N * D, c0, a.N);
-                rG.load(gbase + (bh + 1) * a.N * D, c0, a.N);
-            } else if (ci > 0) {
-                const int cn = c0 - kCb;
-                rK.load(kh, cn, a.N);
-                rV.load(vh, cn, a.N);
-                rQ.load(qbase + bh0 * a.N * D, cn, a.N);
-                rG.load(gbase + bh0 * a.N * D, cn, a.N);
+            {   // Q, G, den, c of the next head, or of the first head at the next chunk
+                const bool last = rep + 1 == a.nrep;
+                const size_t hn = bh0 + (last ? 0 : rep + 1);
+                const int cq = last ? cn : c0;
+                rQ.load(qbase + hn * a.N * D, cq, a.N);
+                rG.load(gbase + hn * a.N * D, cq, a.N);
+                load_dc(hn, cq);
             }
 
             // A = Phi(Q) Phi(K)^T and P = gn V^T - c (queries x keys), i >= j;

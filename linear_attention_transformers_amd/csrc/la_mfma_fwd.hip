@@ -78,7 +78,8 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
     __shared__ __attribute__((aligned(16))) u16 sK[kC * TF::ld];
     __shared__ __attribute__((aligned(16))) u16 sV[kC * TD::ld];
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
-    const int t = threadIdx.x, l = t & 63, w = t >> 6, h = l >> 5, l32 = l & 31;
+    const int t = threadIdx.x, l = t & 63, h = l >> 5, l32 = l & 31;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index, uniform
     const u16 *kh = static_cast<const u16 *>(a.k) + (size_t)bg * a.N * D;
     const u16 *vh = static_cast<const u16 *>(a.v) + (size_t)bg * a.N * D;
     f32x16 S[FB], Z[ZB];
@@ -92,13 +93,11 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
     rV.load(vh, row0, a.N);
     for (int c0 = row0; c0 < row1; c0 += kC) {
         __syncthreads();
-        rK.template store_feat<PHI, COS, TF>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rK.template store_feat<PHI, COS, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
         rV.template store<TD>(sV);
         __syncthreads();
-        if (c0 + kC < row1) {
-            rK.load(kh, c0 + kC, a.N);
-            rV.load(vh, c0 + kC, a.N);
-        }
+        rK.load(kh, c0 + kC, a.N);   // next chunk (past the segment: unused)
+        rV.load(vh, c0 + kC, a.N);
         state_update<D, F>(S, Z, sK, sV, w);
     }
     float *out = a.ws_S + ((size_t)bg * (a.nseg + 1) + seg) * ((size_t)F * D + F);
@@ -143,7 +142,8 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
     __shared__ float sQZ[kCf];
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
-    const int t = threadIdx.x, l = t & 63, w = t >> 6, h = l >> 5, l32 = l & 31;
+    const int t = threadIdx.x, l = t & 63, h = l >> 5, l32 = l & 31;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index, uniform
     const size_t SD = (size_t)F * D + F;
     const u16 *kh = static_cast<const u16 *>(a.k) + (size_t)bg * a.N * D;
     const u16 *vh = static_cast<const u16 *>(a.v) + (size_t)bg * a.N * D;
@@ -181,22 +181,23 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
     for (int c0 = row0; c0 < row1; c0 += kCf) {
         __syncthreads();   // previous chunk: every LDS read done, sz updated, sO complete
         if (pend_oh) store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
-        rK.template store_feat<PHI, COS, TF>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rK.template store_feat<PHI, COS, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
         rV.template store<TD>(sV);
+        // the next chunk's K, V (unconditional: rows past the segment are
+        // loaded clamped and never used, and no register copies are needed)
+        rK.load(kh, c0 + kCf, a.N);
+        rV.load(vh, c0 + kCf, a.N);
         for (int rep = 0; rep < a.nrep; ++rep) {
             u16 *oh = obase + (bh0 + rep) * a.N * D;
             if (rep > 0) {
                 __syncthreads();   // every wave is done with the previous head's sQ; sO complete
                 store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
             }
-            rQ.template store_feat<PHI, COS, TF>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+            rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
             __syncthreads();
-            if (rep + 1 < a.nrep) {
-                rQ.load(qbase + (bh0 + rep + 1) * a.N * D, c0, a.N);
-            } else if (c0 + kCf < row1) {
-                rK.load(kh, c0 + kCf, a.N);
-                rV.load(vh, c0 + kCf, a.N);
-                rQ.load(qbase + bh0 * a.N * D, c0 + kCf, a.N);
+            {   // Q rows of the next head, or of the first head at the next chunk
+                const bool last = rep + 1 == a.nrep;
+                rQ.load(qbase + (bh0 + (last ? 0 : rep + 1)) * a.N * D, last ? c0 + kCf : c0, a.N);
             }
 
             // A^T (keys x queries) of the chunk, causal mask, bf16 rounding (the
