@@ -105,7 +105,7 @@ def step_roofline(w, s, causal):
     return max(t_bytes, t_flops), fwd_bytes + bwd_bytes, fwd_flops + bwd_flops
 
 
-def cpu_baseline(w, tensors, budget_heads=None):
+def cpu_baseline(w, tensors, budget_heads=None, min_seconds=10.0):
     """The CPU oracle, as it is, on whole (batch, KV head) groups at full N,
     fwd + bwd; throughput scaled to the whole workload by group count."""
     import numpy as np
@@ -131,10 +131,15 @@ def cpu_baseline(w, tensors, budget_heads=None):
         cw, sw = si.exact_f64(tensors["cos_weight"]), si.exact_f64(tensors["sin_weight"])
     causal = "causal" in w.modes
     kw = dict(is_causal=causal, phi=w.phi, eps=w.eps, cos_weight=cw, sin_weight=sw)
-    t0 = time.perf_counter()
-    oracle.fwd(q, k, v, **kw)
-    oracle.bwd(q, k, v, g, **kw)
-    dt = time.perf_counter() - t0
+    # repeat the sample until about min_seconds of oracle time have passed
+    reps, total = 0, 0.0
+    while reps == 0 or (total < min_seconds and reps < 64):
+        t0 = time.perf_counter()
+        oracle.fwd(q, k, v, **kw)
+        oracle.bwd(q, k, v, g, **kw)
+        total += time.perf_counter() - t0
+        reps += 1
+    dt = total / reps
     t_full = dt * n_groups / take
     return {
         "value": w.B * w.N / t_full,
@@ -142,7 +147,8 @@ def cpu_baseline(w, tensors, budget_heads=None):
         "cores": min(threads, take * nrep),
         "kind": "oracle",
         "sample": "%d of %d (batch, KV head) groups (%d query heads each) at full N=%d, "
-                  "fwd+bwd in fp64, %.1f s; scaled by group count" % (take, n_groups, nrep, w.N, dt),
+                  "fwd+bwd in fp64, mean of %d runs (%.1f s in all); scaled by group count"
+                  % (take, n_groups, nrep, w.N, reps, total),
     }
 
 
