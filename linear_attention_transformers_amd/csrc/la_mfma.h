@@ -201,20 +201,20 @@ struct RawTile {
     }
 
     // Features: phi, then with COS [cos_t phi, sin_t phi] (row width 2D),
-    // rounded to bf16.  With QZ, also sQZ[r] = Phi(x_r) . z over
-    // the rounded features (fixed-order shuffle reduction across the V8
-    // threads of a row).  Branch-free: rows >= N hold zeros (load), phi of
-    // them is finite, and a 0/1 row factor folded into the weight zeroes it.
+    // rounded to bf16.  With QZ, also sQZ[r] = Phi(x_r) . z (features before
+    // rounding, fp32; fixed-order shuffle reduction across the V8 threads of
+    // a row).  Branch-free per element: rows >= N hold zeros (load) and phi
+    // of them is finite; only a ragged tile (uniform test) multiplies them
+    // by a 0/1 row factor.
     template <int PHI, bool COS, class L, bool QZ>
     __device__ __forceinline__ void store_feat(u16 *dst, int c0, int N, const float *cw,
                                                const float *sw, const float *sz,
                                                float *sQZ) const {
-        const bool full = c0 + C <= N;
+        const bool ragged = c0 + C > N;
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int idx = threadIdx.x + k * NT, r = idx / V8, c8 = (idx % V8) * 8, t = c0 + r;
-            const bool valid = full || t < N;
-            const int tc = valid ? t : 0;   // an in-range index for the weights
+            const int tc = min(t, N - 1);   // an in-range index for the weights
             const uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
             float f[8];
 #pragma unroll
@@ -222,28 +222,34 @@ struct RawTile {
                 f[2 * e] = phi_fast<PHI>(__uint_as_float(w4[e] << 16));
                 f[2 * e + 1] = phi_fast<PHI>(__uint_as_float(w4[e] & 0xffff0000u));
             }
-            const float vf = valid ? 1.f : 0.f;
-            const float m0 = COS ? vf * cw[tc] : vf;
-            float qz = 0.f;
+            if (ragged) {
+                const float vf = t < N ? 1.f : 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] *= vf;
+            }
+            const float m0 = COS ? cw[tc] : 1.f;
             uint32_t o[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                o[e] = pk2(m0 * f[2 * e], m0 * f[2 * e + 1]);
-                if constexpr (QZ)
-                    qz += __uint_as_float(o[e] << 16) * sz[c8 + 2 * e] +
-                          __uint_as_float(o[e] & 0xffff0000u) * sz[c8 + 2 * e + 1];
-            }
+            for (int e = 0; e < 4; ++e) o[e] = COS ? pk2(m0 * f[2 * e], m0 * f[2 * e + 1]) : pk2(f[2 * e], f[2 * e + 1]);
             *reinterpret_cast<uint4 *>(dst + L::at(r, c8)) = make_uint4(o[0], o[1], o[2], o[3]);
-            if constexpr (COS) {
-                const float m1 = vf * sw[tc];
+            float qz = 0.f;
+            if constexpr (QZ) {
+                float d = 0.f;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    o[e] = pk2(m1 * f[2 * e], m1 * f[2 * e + 1]);
-                    if constexpr (QZ)
-                        qz += __uint_as_float(o[e] << 16) * sz[D + c8 + 2 * e] +
-                              __uint_as_float(o[e] & 0xffff0000u) * sz[D + c8 + 2 * e + 1];
-                }
+                for (int e = 0; e < 8; ++e) d += f[e] * sz[c8 + e];
+                qz = m0 * d;
+            }
+            if constexpr (COS) {
+                const float m1 = sw[tc];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = pk2(m1 * f[2 * e], m1 * f[2 * e + 1]);
                 *reinterpret_cast<uint4 *>(dst + L::at(r, D + c8)) = make_uint4(o[0], o[1], o[2], o[3]);
+                if constexpr (QZ) {
+                    float d = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) d += f[e] * sz[D + c8 + e];
+                    qz += m1 * d;
+                }
             }
             if constexpr (QZ) {
 #pragma unroll

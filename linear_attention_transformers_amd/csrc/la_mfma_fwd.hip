@@ -70,8 +70,13 @@ __device__ __forceinline__ void state_update(f32x16 *S, f32x16 *Z, const u16 *sK
 // to the workspace record of the segment.  The next chunk's loads are issued
 // before the current chunk's products.
 // ---------------------------------------------------------------------------
+// Occupancy the state pass is built for: it streams K and V, so more waves
+// per SIMD hide more load latency (each shape's registers allow this).
+template <int D, int F>
+constexpr int state_waves() { return F == 64 ? 4 : F == 128 ? (D == 128 ? 3 : 2) : 1; }
+
 template <int D, int F, int PHI, bool COS>
-__global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 ? 2 : 1))) void k_state_mfma(Args a) {
+__global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(state_waves<D, F>()))) void k_state_mfma(Args a) {
     using TF = typename FwdTiles<D, F>::TF;
     using TD = typename FwdTiles<D, F>::TD;
     constexpr int NT = D * 2, NW = D / 32, FB = F / 32, ZB = FB / NW;
