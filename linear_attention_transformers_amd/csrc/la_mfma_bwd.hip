@@ -433,7 +433,8 @@ void k_bwd_kv_mfma(Args a) {
         for (int db = 0; db < NW; ++db)
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                dK = mfma(acc_op(Rt[db], s), ld4x2<TD>(sV, l32, 32 * db + 16 * s + 4 * h), dK);
+                dK = mfma(ld4x2<TD>(sR, 32 * w + l32, 32 * db + 16 * s + 4 * h),   // R, as staged
+                          ld4x2<TD>(sV, l32, 32 * db + 16 * s + 4 * h), dK);
 #pragma unroll 4
         for (int s = 0; s < F / 16; ++s) {
             const int k0 = 16 * s + 8 * h;
@@ -470,8 +471,8 @@ void k_bwd_kv_mfma(Args a) {
                 load_dc(hn, cq);
             }
 
-            // A = Phi(Q) Phi(K)^T and P = gn V^T - c (queries x keys), i >= j;
-            // each is turned into bf16 operands as soon as it is complete
+            // A = Phi(Q) Phi(K)^T and P = gn V^T - c (queries x keys), i >= j,
+            // masked and turned into bf16 operands
             bf16x8 Aop[2], Pop[2];
             {
                 f32x16 A = zero16();

@@ -207,20 +207,19 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
 
             // A^T (keys x queries) of the chunk, causal mask, bf16 rounding (the
             // values the A V product consumes) and the in-chunk denominators
+            // from the same rounded values
             f32x16 T = zero16();
 #pragma unroll 4
             for (int s = 0; s < F / 16; ++s)
                 T = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), T);
-            float dsum = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int j = 8 * (r >> 2) + 4 * h + (r & 3);
-                const float x = (__bf16)(j <= l32 ? T[r] : 0.f);
-                T[r] = x;
-                dsum += x;
+                T[r] = j <= l32 ? T[r] : 0.f;
             }
-            dsum += __shfl_xor(dsum, 32);
             const bf16x8 B0 = acc_op(T, 0), B1 = acc_op(T, 1);
+            // sum_j A_ij on the matrix cores: 1^T A^T, every row holds it
+            const float dsum = mfma(one, B1, mfma(one, B0, zero16()))[0];
 
             // num^T for this wave's value columns: V^T A^T + S^T Phi(Q)^T
             f32x16 Nt = zero16();
