@@ -96,8 +96,9 @@ la_status check_common(int B, int H, int H_kv, int N, int D, int dtype, int phi,
 // matrix-core forward runs one workgroup per (batch, KV head, segment), the
 // float32 kernels one per (batch, query head, segment).
 bool uses_mfma(int op_bwd, int dtype, int causal, int D, int has_cos) {
-    if (op_bwd) return la::mfma_bwd_serves(dtype == LA_BF16, causal != 0, D, has_cos != 0);
-    return la::mfma_fwd_serves(dtype == LA_BF16, causal != 0, D);
+    (void)causal;   // both modes run on the matrix cores
+    if (op_bwd) return la::mfma_bwd_serves(dtype == LA_BF16, D, has_cos != 0);
+    return la::mfma_fwd_serves(dtype == LA_BF16, D);
 }
 
 la::Plan plan_for(int op_bwd, int B, int H, int H_kv, int N, int D, int dtype, int causal,
@@ -179,7 +180,7 @@ la_status la_fwd_ex(const void *q, const void *k, const void *v, void *out, int 
     a.out = out;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (uses_mfma(0, dtype, causal, D, cos_w != nullptr))
-        return launch_status(la::mfma_fwd_run(a, phi, s));
+        return launch_status(la::mfma_fwd_run(a, phi, causal, s));
     return launch_status(la::generic_run(a, dtype == LA_BF16, 0, causal != 0, phi, s));
 }
 
@@ -216,7 +217,7 @@ la_status la_bwd_ex(const void *q, const void *k, const void *v, const void *gra
     a.dv = dv;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (uses_mfma(1, dtype, causal, D, cos_w != nullptr))
-        return launch_status(la::mfma_bwd_run(a, phi, s));
+        return launch_status(la::mfma_bwd_run(a, phi, causal, s));
     return launch_status(la::generic_run(a, dtype == LA_BF16, 1, causal != 0, phi, s));
 }
 

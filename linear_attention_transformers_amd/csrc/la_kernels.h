@@ -20,12 +20,13 @@ hipError_t scan_state(float *ws, int nseg, size_t SD, unsigned n_units, hipStrea
 hipError_t scan_suffix(const float *Rp, float *Rs, int nseg, size_t SD, int H, int Hkv, int nrep,
                        unsigned n_units, hipStream_t s);
 
-// bf16 matrix-core causal kernels (one workgroup per batch, KV head, segment).
-bool mfma_fwd_serves(int bf16, int causal, int D);
-hipError_t mfma_fwd_run(const Args &a, int phi, hipStream_t s);
-// per-segment state sums + exclusive prefix (the first two steps of both passes)
+// bf16 matrix-core kernels, causal and bidirectional (one workgroup per
+// batch, KV head, segment).
+bool mfma_fwd_serves(int bf16, int D);
+hipError_t mfma_fwd_run(const Args &a, int phi, int causal, hipStream_t s);
+// per-segment state sums + exclusive prefix and total (the first two steps of both passes)
 hipError_t mfma_state_run(const Args &a, int phi, hipStream_t s);
-bool mfma_bwd_serves(int bf16, int causal, int D, int has_cos);
-hipError_t mfma_bwd_run(const Args &a, int phi, hipStream_t s);
+bool mfma_bwd_serves(int bf16, int D, int has_cos);
+hipError_t mfma_bwd_run(const Args &a, int phi, int causal, hipStream_t s);
 
 }  // namespace la

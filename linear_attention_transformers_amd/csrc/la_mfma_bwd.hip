@@ -96,7 +96,7 @@ __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 *
 // After that exchange (one barrier) the two wave kinds run independently: the
 // R update needs only 1/den, and the waves that own r recompute c.
 // ---------------------------------------------------------------------------
-template <int D, int PHI>
+template <int D, int PHI, bool CAUSAL>
 __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bwd_q_mfma(Args a) {
     constexpr int F = D, NW = D / 32, NT = 4 * D;
@@ -126,9 +126,10 @@ void k_bwd_q_mfma(Args a) {
     const u16 *gbase = static_cast<const u16 *>(a.g);
     u16 *dqbase = static_cast<u16 *>(a.dq);
 
-    // state waves: S^T tiles (value block db x feature block w), z tile (block w)
+    // state waves: S^T tiles (value block db x feature block w), z tile (block w),
+    // the segment's exclusive prefix (causal) or the sequence total
     // R waves: R tiles (feature block wr x value block db)
-    const float *Sp = a.ws_S + ((size_t)bg * (a.nseg + 1) + seg) * SD;
+    const float *Sp = a.ws_S + ((size_t)bg * (a.nseg + 1) + (CAUSAL ? seg : a.nseg)) * SD;
     f32x16 X[NW], Z = zero16();
     if (state_wave) {
 #pragma unroll
@@ -148,18 +149,22 @@ void k_bwd_q_mfma(Args a) {
 
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
     RawTile<D, NT, kCb> rK, rV, rQ, rG;
-    rK.load(kh, row0, a.N);
-    rV.load(vh, row0, a.N);
+    if constexpr (CAUSAL) {
+        rK.load(kh, row0, a.N);
+        rV.load(vh, row0, a.N);
+    }
     rQ.load(qbase + bh0 * a.N * D, row0, a.N);
     rG.load(gbase + bh0 * a.N * D, row0, a.N);
     for (int c0 = row0; c0 < row1; c0 += kCb) {
         __syncthreads();
-        rK.template store_feat<PHI, false, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
-        rV.template store<TD>(sV);
-        // the next chunk's K, V (unconditional: rows past the segment are
-        // loaded clamped and never used, and no register copies are needed)
-        rK.load(kh, c0 + kCb, a.N);
-        rV.load(vh, c0 + kCb, a.N);
+        if constexpr (CAUSAL) {
+            rK.template store_feat<PHI, false, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+            rV.template store<TD>(sV);
+            // the next chunk's K, V (unconditional: rows past the segment are
+            // loaded clamped and never used, and no register copies are needed)
+            rK.load(kh, c0 + kCb, a.N);
+            rV.load(vh, c0 + kCb, a.N);
+        }
         for (int rep = 0; rep < a.nrep; ++rep) {
             const size_t bh = bh0 + rep;
             if (rep > 0) __syncthreads();
@@ -193,26 +198,28 @@ void k_bwd_q_mfma(Args a) {
                 qu += __shfl_xor(qu, 32);
                 if (h == 0) sQU[w][l32] = qu;
             } else if (w == NW) {
-                // A^T (keys x queries), causal mask, rounded to bf16 (the
-                // forward's A), the denominators, and the tile for the state waves
-                f32x16 At = zero16();
-#pragma unroll 4
-                for (int s = 0; s < F / 16; ++s)
-                    At = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), At);
+                // causal: A^T (keys x queries), causal mask, rounded to bf16
+                // (the forward's A), the tile for the state waves; the denominators
                 float dA = 0.f;
+                if constexpr (CAUSAL) {
+                    f32x16 At = zero16();
+#pragma unroll 4
+                    for (int s = 0; s < F / 16; ++s)
+                        At = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), At);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    At[r] = acc_row(r, h) <= l32 ? (float)(__bf16)At[r] : 0.f;
-                    dA += At[r];
+                    for (int r = 0; r < 16; ++r) {
+                        At[r] = acc_row(r, h) <= l32 ? (float)(__bf16)At[r] : 0.f;
+                        dA += At[r];
+                    }
+                    dA += __shfl_xor(dA, 32);
+                    put_acc(sAt, At);
                 }
-                dA += __shfl_xor(dA, 32);
-                put_acc(sAt, At);
                 if (h == 0) {
                     const float den = ok ? dA + sQZ[l32] + a.eps : 1.f;
                     sDen[l32] = den;
                     sInv[l32] = rcp(den);
                 }
-            } else if (w == NW + 1) {
+            } else if (CAUSAL && w == NW + 1) {
                 // T^T = V G^T (keys x queries), unmasked: the state waves mask
                 f32x16 Tt = zero16();
 #pragma unroll 4
@@ -222,32 +229,37 @@ void k_bwd_q_mfma(Args a) {
             }
             __syncthreads();
             if (state_wave) {
-                // c = (sum_j A_ij T_ij + Phi(q_i).U_i) / den_i^2
-                f32x16 Tt = get_acc(sTt);
-                const f32x16 At = get_acc(sAt);
+                // c = (sum_j A_ij T_ij + Phi(q_i).U_i) / den_i^2 (no A term: bidirectional)
+                f32x16 Tt;
                 float aT = 0.f;
+                if constexpr (CAUSAL) {
+                    Tt = get_acc(sTt);
+                    const f32x16 At = get_acc(sAt);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) aT += At[r] * Tt[r];
-                aT += __shfl_xor(aT, 32);
+                    for (int r = 0; r < 16; ++r) aT += At[r] * Tt[r];
+                    aT += __shfl_xor(aT, 32);
+                }
                 float gsum = aT;
 #pragma unroll
                 for (int ww = 0; ww < NW; ++ww) gsum += sQU[ww][l32];
                 const float inv = sInv[l32];
                 const float c = ok ? gsum * inv * inv : 0.f;
-                if (w == 0 && h == 0 && ok) {
-                    a.ws_den[bh * a.N + c0 + l32] = sDen[l32];
-                    a.ws_c[bh * a.N + c0 + l32] = c;
-                }
-                // P^T = T^T / den - c (masked), then dPhi(q)^T = Phi(K)^T P^T + U^T / den - z c
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    Tt[r] = acc_row(r, h) <= l32 ? Tt[r] * inv - c : 0.f;
                 f32x16 Qd = zero16();
+                if constexpr (CAUSAL) {
+                    if (w == 0 && h == 0 && ok) {   // for the dk/dv pass
+                        a.ws_den[bh * a.N + c0 + l32] = sDen[l32];
+                        a.ws_c[bh * a.N + c0 + l32] = c;
+                    }
+                    // P^T = T^T / den - c (masked), then dPhi(q)^T = Phi(K)^T P^T + U^T / den - z c
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const int k0 = 16 * s + 4 * h;
-                    const bf16x8 ka = tr8(tr_addr<TF>(sK, k0, 32 * w), tr_addr<TF>(sK, k0 + 8, 32 * w));
-                    Qd = mfma(ka, acc_op(Tt, s), Qd);
+                    for (int r = 0; r < 16; ++r)
+                        Tt[r] = acc_row(r, h) <= l32 ? Tt[r] * inv - c : 0.f;
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        const int k0 = 16 * s + 4 * h;
+                        const bf16x8 ka = tr8(tr_addr<TF>(sK, k0, 32 * w), tr_addr<TF>(sK, k0 + 8, 32 * w));
+                        Qd = mfma(ka, acc_op(Tt, s), Qd);
+                    }
                 }
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
@@ -288,11 +300,13 @@ void k_bwd_q_mfma(Args a) {
                 if (w >= (NT - F) / 64) {
                     // r += Phi(Q)^T c: these waves form c_i themselves, in the
                     // state waves' order (same bits), rather than wait for them
-                    const f32x16 At = get_acc(sAt), Tt = get_acc(sTt);
                     float aT = 0.f;
+                    if constexpr (CAUSAL) {
+                        const f32x16 At = get_acc(sAt), Tt = get_acc(sTt);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) aT += At[r] * Tt[r];
-                    aT += __shfl_xor(aT, 32);
+                        for (int r = 0; r < 16; ++r) aT += At[r] * Tt[r];
+                        aT += __shfl_xor(aT, 32);
+                    }
                     float gsum = aT;
 #pragma unroll
                     for (int ww = 0; ww < NW; ++ww) gsum += sQU[ww][l32];
@@ -308,7 +322,7 @@ void k_bwd_q_mfma(Args a) {
                 }
             }
         }
-        if (state_wave) {
+        if (CAUSAL && state_wave) {
             // carry (S^T, z) past this chunk
 #pragma unroll
             for (int s = 0; s < kCb / 16; ++s) {
@@ -348,7 +362,7 @@ void k_bwd_q_mfma(Args a) {
 // R^T (every value block x feature block w) and produces dk for feature
 // block w and dv for value block w.
 // ---------------------------------------------------------------------------
-template <int D, int PHI>
+template <int D, int PHI, bool CAUSAL>
 __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bwd_kv_mfma(Args a) {
     constexpr int F = D, NW = D / 32, NT = 2 * D;
@@ -375,7 +389,8 @@ void k_bwd_kv_mfma(Args a) {
     const u16 *qbase = static_cast<const u16 *>(a.q);
     const u16 *gbase = static_cast<const u16 *>(a.g);
 
-    const float *Rp = a.ws_Rs + ((size_t)bg * (a.nseg + 1) + seg) * SD;
+    // the segment's exclusive suffix of (R, r) (causal) or the sequence total
+    const float *Rp = a.ws_Rs + ((size_t)bg * (a.nseg + 1) + (CAUSAL ? seg : a.nseg)) * SD;
     f32x16 Rt[NW];
 #pragma unroll
     for (int db = 0; db < NW; ++db)
@@ -398,9 +413,11 @@ void k_bwd_kv_mfma(Args a) {
         const int c0 = row0 + (nch - 1) * kCb;
         rK.load(kh, c0, a.N);
         rV.load(vh, c0, a.N);
-        rQ.load(qbase + bh0 * a.N * D, c0, a.N);
-        rG.load(gbase + bh0 * a.N * D, c0, a.N);
-        load_dc(bh0, c0);
+        if constexpr (CAUSAL) {   // the in-chunk terms need the queries' rows
+            rQ.load(qbase + bh0 * a.N * D, c0, a.N);
+            rG.load(gbase + bh0 * a.N * D, c0, a.N);
+            load_dc(bh0, c0);
+        }
     }
     int pend_c0 = -1;   // dk, dv rows of the previous chunk staged in sQ, sG
     for (int ci = nch - 1; ci >= 0; --ci) {
@@ -415,16 +432,19 @@ void k_bwd_kv_mfma(Args a) {
         const int cn = ci > 0 ? c0 - kCb : c0;   // next chunk (none: reload this one)
         rK.load(kh, cn, a.N);
         rV.load(vh, cn, a.N);
-        // R (bf16, [feature][value]) for the value-gradient's state term
+        // R (bf16, [feature][value]) for the state terms (bidirectional: the
+        // total, staged once)
+        if (CAUSAL || ci == nch - 1) {
 #pragma unroll
-        for (int db = 0; db < NW; ++db)
+            for (int db = 0; db < NW; ++db)
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                float x[4];
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    float x[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = Rt[db][4 * q4 + e];
-                st4bf(sR + TD::at(32 * w + l32, 32 * db + 8 * q4 + 4 * h), x);
-            }
+                    for (int e = 0; e < 4; ++e) x[e] = Rt[db][4 * q4 + e];
+                    st4bf(sR + TD::at(32 * w + l32, 32 * db + 8 * q4 + 4 * h), x);
+                }
+        }
         __syncthreads();
 
         // state terms: dPhi(k)^T = R V^T - r, dv^T = R^T Phi(K)^T
@@ -444,7 +464,8 @@ void k_bwd_kv_mfma(Args a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) dK[r] -= sr[32 * w + acc_row(r, h)];
 
-        for (int rep = 0; rep < a.nrep; ++rep) {
+        // causal: the chunk's own queries (in-chunk terms) and the R update
+        for (int rep = 0; rep < (CAUSAL ? a.nrep : 0); ++rep) {
             __syncthreads();   // previous head's LDS reads and every read of r are done
             rQ.template store_feat<PHI, false, TF, false>(sQ, c0, a.N, a.cw, a.sw, nullptr, nullptr);
             {   // gn = g / den in LDS (rows past N: zeros), and c
@@ -549,7 +570,7 @@ void k_bwd_kv_mfma(Args a) {
     }
 }
 
-template <int D, int PHI>
+template <int D, int PHI, bool CAUSAL>
 hipError_t run(const Args &a, hipStream_t s) {
     constexpr int F = D;
     const unsigned n_units = (unsigned)(a.B * a.Hkv);
@@ -557,8 +578,8 @@ hipError_t run(const Args &a, hipStream_t s) {
     hipError_t e = mfma_state_run(a, PHI, s);
     if (e != hipSuccess) return e;
     {
-        TimedLaunch tl("k_bwd_q_mfma", s);
-        hipLaunchKernelGGL((k_bwd_q_mfma<D, PHI>), dim3(n_units * a.nseg), dim3(4 * D), 0, s, a);
+        TimedLaunch tl(CAUSAL ? "k_bwd_q_mfma" : "k_bwd_q_bidir_mfma", s);
+        hipLaunchKernelGGL((k_bwd_q_mfma<D, PHI, CAUSAL>), dim3(n_units * a.nseg), dim3(4 * D), 0, s, a);
     }
     {
         TimedLaunch tl("k_scan_R", s);
@@ -567,31 +588,28 @@ hipError_t run(const Args &a, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     {
-        TimedLaunch tl("k_bwd_kv_mfma", s);
-        hipLaunchKernelGGL((k_bwd_kv_mfma<D, PHI>), dim3(n_units * a.nseg), dim3(2 * D), 0, s, a);
+        TimedLaunch tl(CAUSAL ? "k_bwd_kv_mfma" : "k_bwd_kv_bidir_mfma", s);
+        hipLaunchKernelGGL((k_bwd_kv_mfma<D, PHI, CAUSAL>), dim3(n_units * a.nseg), dim3(2 * D), 0, s, a);
     }
     return hipGetLastError();
 }
 
-}  // namespace
-
-bool mfma_bwd_serves(int bf16, int causal, int D, int has_cos) {
-    return bf16 && causal && !has_cos && (D == 64 || D == 128);
+template <int D, bool CAUSAL>
+hipError_t by_phi(const Args &a, int phi, hipStream_t s) {
+    switch (phi) {
+        case kElu1: return run<D, kElu1, CAUSAL>(a, s);
+        case kRelu: return run<D, kRelu, CAUSAL>(a, s);
+        default: return run<D, kIdentity, CAUSAL>(a, s);
+    }
 }
 
-hipError_t mfma_bwd_run(const Args &a, int phi, hipStream_t s) {
-    if (a.D == 64) {
-        switch (phi) {
-            case kElu1: return run<64, kElu1>(a, s);
-            case kRelu: return run<64, kRelu>(a, s);
-            default: return run<64, kIdentity>(a, s);
-        }
-    }
-    switch (phi) {
-        case kElu1: return run<128, kElu1>(a, s);
-        case kRelu: return run<128, kRelu>(a, s);
-        default: return run<128, kIdentity>(a, s);
-    }
+}  // namespace
+
+bool mfma_bwd_serves(int bf16, int D, int has_cos) { return bf16 && !has_cos && (D == 64 || D == 128); }
+
+hipError_t mfma_bwd_run(const Args &a, int phi, int causal, hipStream_t s) {
+    if (a.D == 64) return causal ? by_phi<64, true>(a, phi, s) : by_phi<64, false>(a, phi, s);
+    return causal ? by_phi<128, true>(a, phi, s) : by_phi<128, false>(a, phi, s);
 }
 
 }  // namespace la

@@ -265,6 +265,77 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
     if (pend_oh) store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
 }
 
+// ---------------------------------------------------------------------------
+// k_fwd_bidir_mfma: bidirectional row pass (linear_attn page, module
+// docstring: the bidirectional parallel reduction), per (batch, KV head,
+// segment of query rows), for all n_rep query heads:
+//   out_i = Phi(q_i) S / (Phi(q_i) . z + eps)
+// against the totals (S, z) over the whole sequence (the scan's last slot).
+// The total S is constant, so each wave keeps its slice as bf16 operands.
+// ---------------------------------------------------------------------------
+template <int D, int F, int PHI, bool COS>
+__global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2))) void k_fwd_bidir_mfma(Args a) {
+    using TF = typename FwdTiles<D, F>::TF;
+    using TD = typename FwdTiles<D, F>::TD;
+    constexpr int NT = D * 2, FB = F / 32;
+    __shared__ __attribute__((aligned(16))) u16 sQ[kCf * TF::ld];
+    __shared__ __attribute__((aligned(16))) u16 sO[kCf * TD::ld];   // output rows of one head
+    __shared__ __attribute__((aligned(16))) float sz[F];
+    __shared__ float sQZ[kCf];
+    const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const int t = threadIdx.x, l = t & 63, h = l >> 5, l32 = l & 31;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index, uniform
+    const size_t SD = (size_t)F * D + F;
+    const size_t bh0 = (size_t)b * a.H + (size_t)g * a.nrep;
+    const u16 *qbase = static_cast<const u16 *>(a.q);
+    u16 *obase = static_cast<u16 *>(a.out);
+
+    // total state: this wave's value block as the A operands of S^T Phi(Q)^T
+    // (feature k order of an accumulator: 32 fb + 16 s + 8 (e / 4) + 4 h + e % 4)
+    const float *Sp = a.ws_S + ((size_t)bg * (a.nseg + 1) + a.nseg) * SD;
+    bf16x8 Sop[FB][2];
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int f = 32 * fb + 16 * s + 8 * (e >> 2) + 4 * h + (e & 3);
+                Sop[fb][s][e] = (__bf16)Sp[(size_t)f * D + 32 * w + l32];
+            }
+    for (int e = t; e < F; e += NT) sz[e] = Sp[(size_t)F * D + e];
+
+    const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
+    RawTile<D, NT, kCf> rQ;
+    rQ.load(qbase + bh0 * a.N * D, row0, a.N);
+    u16 *pend_oh = nullptr;   // rows staged in sO, stored after the next barrier
+    int pend_c0 = 0;
+    for (int c0 = row0; c0 < row1; c0 += kCf) {
+        for (int rep = 0; rep < a.nrep; ++rep) {
+            __syncthreads();   // previous head: sQ reads done, sO complete (and sz written)
+            if (pend_oh) store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
+            rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+            __syncthreads();
+            {   // Q rows of the next head, or of the first head at the next chunk
+                const bool last = rep + 1 == a.nrep;
+                rQ.load(qbase + (bh0 + (last ? 0 : rep + 1)) * a.N * D, last ? c0 + kCf : c0, a.N);
+            }
+            f32x16 Nt = zero16();
+#pragma unroll
+            for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    Nt = mfma(Sop[fb][s], ld4x2<TF>(sQ, l32, 32 * fb + 16 * s + 4 * h), Nt);
+            stage_out<TD>(sO, Nt, rcp(sQZ[l32] + a.eps), 32 * w);
+            pend_oh = obase + (bh0 + rep) * a.N * D;
+            pend_c0 = c0;
+        }
+    }
+    __syncthreads();
+    if (pend_oh) store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
+}
+
 template <int D, int F, int PHI, bool COS>
 hipError_t run_state(const Args &a, hipStream_t s) {
     constexpr int NT = D * 2;
@@ -278,44 +349,51 @@ hipError_t run_state(const Args &a, hipStream_t s) {
 }
 
 template <int D, int F, int PHI, bool COS>
-hipError_t run(const Args &a, hipStream_t s) {
+hipError_t run(const Args &a, bool causal, hipStream_t s) {
     constexpr int NT = D * 2;
     hipError_t e = run_state<D, F, PHI, COS>(a, s);
     if (e != hipSuccess) return e;
-    {
+    const dim3 grid((unsigned)(a.B * a.Hkv * a.nseg));
+    if (causal) {
         TimedLaunch tl("k_fwd_mfma", s);
-        hipLaunchKernelGGL((k_fwd_mfma<D, F, PHI, COS>), dim3((unsigned)(a.B * a.Hkv * a.nseg)),
-                           dim3(NT), 0, s, a);
+        hipLaunchKernelGGL((k_fwd_mfma<D, F, PHI, COS>), grid, dim3(NT), 0, s, a);
+    } else {
+        TimedLaunch tl("k_fwd_bidir_mfma", s);
+        hipLaunchKernelGGL((k_fwd_bidir_mfma<D, F, PHI, COS>), grid, dim3(NT), 0, s, a);
     }
     return hipGetLastError();
 }
 
 template <int D, bool COS>
-hipError_t by_phi(const Args &a, int phi, bool state_only, hipStream_t s) {
+hipError_t by_phi(const Args &a, int phi, bool state_only, bool causal, hipStream_t s) {
     constexpr int F = COS ? 2 * D : D;
     switch (phi) {
-        case kElu1: return state_only ? run_state<D, F, kElu1, COS>(a, s) : run<D, F, kElu1, COS>(a, s);
-        case kRelu: return state_only ? run_state<D, F, kRelu, COS>(a, s) : run<D, F, kRelu, COS>(a, s);
+        case kElu1:
+            return state_only ? run_state<D, F, kElu1, COS>(a, s) : run<D, F, kElu1, COS>(a, causal, s);
+        case kRelu:
+            return state_only ? run_state<D, F, kRelu, COS>(a, s) : run<D, F, kRelu, COS>(a, causal, s);
         default:
-            return state_only ? run_state<D, F, kIdentity, COS>(a, s) : run<D, F, kIdentity, COS>(a, s);
+            return state_only ? run_state<D, F, kIdentity, COS>(a, s) : run<D, F, kIdentity, COS>(a, causal, s);
     }
 }
 
-hipError_t dispatch(const Args &a, int phi, bool state_only, hipStream_t s) {
+hipError_t dispatch(const Args &a, int phi, bool state_only, bool causal, hipStream_t s) {
     const bool cos = a.F == 2 * a.D;
     if (a.D == 64)
-        return cos ? by_phi<64, true>(a, phi, state_only, s) : by_phi<64, false>(a, phi, state_only, s);
-    return cos ? by_phi<128, true>(a, phi, state_only, s) : by_phi<128, false>(a, phi, state_only, s);
+        return cos ? by_phi<64, true>(a, phi, state_only, causal, s)
+                   : by_phi<64, false>(a, phi, state_only, causal, s);
+    return cos ? by_phi<128, true>(a, phi, state_only, causal, s)
+               : by_phi<128, false>(a, phi, state_only, causal, s);
 }
 
 }  // namespace
 
-bool mfma_fwd_serves(int bf16, int causal, int D) {
-    return bf16 && causal && (D == 64 || D == 128);
+bool mfma_fwd_serves(int bf16, int D) { return bf16 && (D == 64 || D == 128); }
+
+hipError_t mfma_fwd_run(const Args &a, int phi, int causal, hipStream_t s) {
+    return dispatch(a, phi, false, causal != 0, s);
 }
 
-hipError_t mfma_fwd_run(const Args &a, int phi, hipStream_t s) { return dispatch(a, phi, false, s); }
-
-hipError_t mfma_state_run(const Args &a, int phi, hipStream_t s) { return dispatch(a, phi, true, s); }
+hipError_t mfma_state_run(const Args &a, int phi, hipStream_t s) { return dispatch(a, phi, true, true, s); }
 
 }  // namespace la

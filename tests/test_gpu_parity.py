@@ -207,8 +207,9 @@ def test_binding_errors_on_gpu():
 
 
 def test_kernel_family_per_case():
-    """bf16 causal forward runs on the matrix-core kernels; float32 on the
-    vector-ALU kernels (checked through the library's launch timing)."""
+    """bf16 runs on the matrix-core kernels (causal and bidirectional, forward
+    and backward; the cos/sin backward excepted); float32 on the vector-ALU
+    kernels (checked through the library's launch timing)."""
     torch, la = gpu_or_skip()
     t = make(1, 4, 2, 256, 128, "bf16", scale=0.5, seed=1)
     la.timing_enable(True)
@@ -226,3 +227,11 @@ def test_kernel_family_per_case():
     finally:
         la.timing_enable(False)
     assert "k_fwd_causal" in names, names
+    t = make(1, 4, 2, 256, 64, "bf16", seed=1)
+    la.timing_enable(True)
+    try:
+        run_gpu(la, t, False, "relu", backward=True)
+        names = set(la.timing_collect())
+    finally:
+        la.timing_enable(False)
+    assert {"k_state_mfma", "k_fwd_bidir_mfma", "k_bwd_q_bidir_mfma", "k_bwd_kv_bidir_mfma"} <= names, names
