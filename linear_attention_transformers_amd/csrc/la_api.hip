@@ -96,8 +96,7 @@ la_status check_common(int B, int H, int H_kv, int N, int D, int dtype, int phi,
 // matrix-core forward runs one workgroup per (batch, KV head, segment), the
 // float32 kernels one per (batch, query head, segment).
 bool uses_mfma(int op_bwd, int dtype, int causal, int D, int has_cos) {
-    (void)causal;   // both modes run on the matrix cores
-    if (op_bwd) return la::mfma_bwd_serves(dtype == LA_BF16, D, has_cos != 0);
+    if (op_bwd) return la::mfma_bwd_serves(dtype == LA_BF16, causal != 0, D, has_cos != 0);
     return la::mfma_fwd_serves(dtype == LA_BF16, D);
 }
 

@@ -26,7 +26,10 @@ bool mfma_fwd_serves(int bf16, int D);
 hipError_t mfma_fwd_run(const Args &a, int phi, int causal, hipStream_t s);
 // per-segment state sums + exclusive prefix and total (the first two steps of both passes)
 hipError_t mfma_state_run(const Args &a, int phi, hipStream_t s);
-bool mfma_bwd_serves(int bf16, int D, int has_cos);
+// backward: causal and bidirectional with F = D; causal with the cos/sin
+// features (F = 2D, la_mfma_bwd_cos.hip)
+bool mfma_bwd_serves(int bf16, int causal, int D, int has_cos);
 hipError_t mfma_bwd_run(const Args &a, int phi, int causal, hipStream_t s);
+hipError_t mfma_bwd_cos_run(const Args &a, int phi, hipStream_t s);
 
 }  // namespace la

@@ -125,6 +125,19 @@ __device__ __forceinline__ bf16x8 acc_op(const f32x16 &acc, int s) {
     return o;
 }
 
+// The rounding remainders of acc_op: x - bf16(x) for registers 8s .. 8s+7,
+// rounded to bf16.  acc_op + acc_lo carry an fp32 accumulator to about 2^-16
+// relative, for products whose results are small differences.
+__device__ __forceinline__ bf16x8 acc_lo(const f32x16 &acc, int s) {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x = acc[8 * s + e];
+        o[e] = (__bf16)(x - (float)(__bf16)x);
+    }
+    return o;
+}
+
 // phi for values that are rounded to bf16 right after: the hardware exp
 // (__expf, a few ulp) is far below bf16 resolution.
 template <int PHI>
@@ -297,6 +310,48 @@ __device__ __forceinline__ void store_rows(u16 *dst, const u16 *sO, int c0, int 
                 *reinterpret_cast<const uint4 *>(sO + L::at(r, c8));
     }
 }
+
+// Accumulator helpers shared by the backward kernels.
+
+// 4 consecutive bf16 of an LDS row as floats.
+__device__ __forceinline__ void ld4f(const u16 *p, float *o) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    o[0] = __uint_as_float(u.x << 16);
+    o[1] = __uint_as_float(u.x & 0xffff0000u);
+    o[2] = __uint_as_float(u.y << 16);
+    o[3] = __uint_as_float(u.y & 0xffff0000u);
+}
+
+__device__ __forceinline__ void st4bf(u16 *p, const float *x) {
+    *reinterpret_cast<uint2 *>(p) = make_uint2(pk2(x[0], x[1]), pk2(x[2], x[3]));
+}
+
+// An accumulator tile through LDS in its register layout: register 4q + e of
+// lane l at float (64q + l) * 4 + e, so each 16-byte access of a wave is
+// contiguous.
+__device__ __forceinline__ void put_acc(float *dst, const f32x16 &x) {
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4 *>(dst + (64 * q + l) * 4) = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+}
+
+__device__ __forceinline__ f32x16 get_acc(const float *src) {
+    const int l = threadIdx.x & 63;
+    f32x16 x;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4 *>(src + (64 * q + l) * 4);
+        x[4 * q] = v.x;
+        x[4 * q + 1] = v.y;
+        x[4 * q + 2] = v.z;
+        x[4 * q + 3] = v.w;
+    }
+    return x;
+}
+
+// Accumulator row index of register r for lane half h.
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
 }  // namespace mf
 }  // namespace la

@@ -44,46 +44,6 @@ using namespace mf;
 
 constexpr int kCb = 32;   // backward chunk length: one 32x32 tile per head
 
-// 4 consecutive bf16 of an LDS row as floats.
-__device__ __forceinline__ void ld4f(const u16 *p, float *o) {
-    const uint2 u = *reinterpret_cast<const uint2 *>(p);
-    o[0] = __uint_as_float(u.x << 16);
-    o[1] = __uint_as_float(u.x & 0xffff0000u);
-    o[2] = __uint_as_float(u.y << 16);
-    o[3] = __uint_as_float(u.y & 0xffff0000u);
-}
-
-__device__ __forceinline__ void st4bf(u16 *p, const float *x) {
-    *reinterpret_cast<uint2 *>(p) = make_uint2(pk2(x[0], x[1]), pk2(x[2], x[3]));
-}
-
-// An accumulator tile through LDS in its register layout: register 4q + e of
-// lane l at float (64q + l) * 4 + e, so each 16-byte access of a wave is
-// contiguous.
-__device__ __forceinline__ void put_acc(float *dst, const f32x16 &x) {
-    const int l = threadIdx.x & 63;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4 *>(dst + (64 * q + l) * 4) = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
-}
-
-__device__ __forceinline__ f32x16 get_acc(const float *src) {
-    const int l = threadIdx.x & 63;
-    f32x16 x;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4 *>(src + (64 * q + l) * 4);
-        x[4 * q] = v.x;
-        x[4 * q + 1] = v.y;
-        x[4 * q + 2] = v.z;
-        x[4 * q + 3] = v.w;
-    }
-    return x;
-}
-
-// Accumulator row index of register r for lane half h.
-__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
-
 // ---------------------------------------------------------------------------
 // k_bwd_q_mfma: forward over the 32-row chunks of one (batch, KV head,
 // segment).  Waves 0 .. D/32-1 ("state waves") hold S^T and z and produce
@@ -186,8 +146,13 @@ void k_bwd_q_mfma(Args a) {
 #pragma unroll
                 for (int db = 0; db < NW; ++db)
 #pragma unroll
-                    for (int s = 0; s < 2; ++s)
-                        U = mfma(acc_op(X[db], s), ld4x2<TD>(sG, l32, 32 * db + 16 * s + 4 * h), U);
+                    for (int s = 0; s < 2; ++s) {
+                        const bf16x8 gq = ld4x2<TD>(sG, l32, 32 * db + 16 * s + 4 * h);
+                        U = mfma(acc_op(X[db], s), gq, U);
+                        // bidirectional: every term goes through the state, and with
+                        // few keys dq is a small difference: S in two bf16 parts
+                        if constexpr (!CAUSAL) U = mfma(acc_lo(X[db], s), gq, U);
+                    }
                 float qu = 0.f, x4[4];
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
@@ -289,12 +254,19 @@ void k_bwd_q_mfma(Args a) {
                     const float4 i0 = *reinterpret_cast<const float4 *>(sInv + k0);
                     const float4 i1 = *reinterpret_cast<const float4 *>(sInv + k0 + 4);
                     const float sc[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+                    bf16x8 qlo;   // bidirectional: Phi(q) / den in two bf16 parts (R v - r is
+                                  // a small difference when few queries see a key)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) qa[e] = (__bf16)((float)qa[e] * sc[e]);
+                    for (int e = 0; e < 8; ++e) {
+                        const float x = (float)qa[e] * sc[e];
+                        qa[e] = (__bf16)x;
+                        qlo[e] = (__bf16)(x - (float)qa[e]);
+                    }
 #pragma unroll
                     for (int db = 0; db < NW; ++db) {
                         const bf16x8 gb = tr8(tr_addr<TD>(sG, k0, 32 * db), tr_addr<TD>(sG, k0 + 4, 32 * db));
                         X[db] = mfma(qa, gb, X[db]);
+                        if constexpr (!CAUSAL) X[db] = mfma(qlo, gb, X[db]);
                     }
                 }
                 if (w >= (NT - F) / 64) {
@@ -373,7 +345,8 @@ void k_bwd_kv_mfma(Args a) {
     __shared__ __attribute__((aligned(16))) u16 sQ[kCb * TF::ld];
     __shared__ __attribute__((aligned(16))) u16 sG[kCb * TD::ld];
     __shared__ __attribute__((aligned(16))) u16 sR[F * TD::ld];
-    __shared__ __attribute__((aligned(16))) float sCc[kCb];
+    __shared__ __attribute__((aligned(16))) u16 sGr[kCb * TD::ld];   // raw g rows (for P)
+    __shared__ __attribute__((aligned(16))) float sCc[kCb], sIq[kCb];   // c_i, 1 / den_i
     __shared__ float sr[F];
 
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
@@ -402,12 +375,14 @@ void k_bwd_kv_mfma(Args a) {
     const int nch = (row1 - row0 + kCb - 1) / kCb;
     RawTile<D, NT, kCb> rK, rV, rQ, rG;
     constexpr int NV = RawTile<D, NT, kCb>::NV, V8 = D / 8;
-    float pden[NV], pc;   // den of this thread's G rows and c of query t % 32, prefetched
+    // prefetched: den of this thread's G rows, c and den of query t % 32
+    float pden[NV], pc, pdq;
     auto load_dc = [&](size_t hh, int cc) {
 #pragma unroll
         for (int k = 0; k < NV; ++k)
             pden[k] = a.ws_den[hh * a.N + min(cc + (t + k * NT) / V8, a.N - 1)];
         pc = a.ws_c[hh * a.N + min(cc + (t & (kCb - 1)), a.N - 1)];
+        pdq = a.ws_den[hh * a.N + min(cc + (t & (kCb - 1)), a.N - 1)];
     };
     {
         const int c0 = row0 + (nch - 1) * kCb;
@@ -452,9 +427,17 @@ void k_bwd_kv_mfma(Args a) {
 #pragma unroll
         for (int db = 0; db < NW; ++db)
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-                dK = mfma(ld4x2<TD>(sR, 32 * w + l32, 32 * db + 16 * s + 4 * h),   // R, as staged
-                          ld4x2<TD>(sV, l32, 32 * db + 16 * s + 4 * h), dK);
+            for (int s = 0; s < 2; ++s) {
+                const bf16x8 vq = ld4x2<TD>(sV, l32, 32 * db + 16 * s + 4 * h);
+                if constexpr (CAUSAL) {
+                    dK = mfma(ld4x2<TD>(sR, 32 * w + l32, 32 * db + 16 * s + 4 * h), vq, dK);   // R, as staged
+                } else {
+                    // R (total) in two bf16 parts: R v - r is a small difference
+                    // when few queries see a key
+                    dK = mfma(acc_op(Rt[db], s), vq, dK);
+                    dK = mfma(acc_lo(Rt[db], s), vq, dK);
+                }
+            }
 #pragma unroll 4
         for (int s = 0; s < F / 16; ++s) {
             const int k0 = 16 * s + 8 * h;
@@ -480,7 +463,11 @@ void k_bwd_kv_mfma(Args a) {
                         wds[e] = pk2(__uint_as_float(wds[e] << 16) * inv, __uint_as_float(wds[e] & 0xffff0000u) * inv);
                     *reinterpret_cast<uint4 *>(sG + TD::at(i, c8)) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
                 }
-                if (t < kCb) sCc[t] = c0 + t < a.N ? pc : 0.f;
+                if (t < kCb) {
+                    sCc[t] = c0 + t < a.N ? pc : 0.f;
+                    sIq[t] = c0 + t < a.N ? rcp(pdq) : 0.f;
+                }
+                rG.template store<TD>(sGr);
             }
             __syncthreads();
             {   // Q, G, den, c of the next head, or of the first head at the next chunk
@@ -492,8 +479,11 @@ void k_bwd_kv_mfma(Args a) {
                 load_dc(hn, cq);
             }
 
-            // A = Phi(Q) Phi(K)^T and P = gn V^T - c (queries x keys), i >= j,
-            // masked and turned into bf16 operands
+            // A = Phi(Q) Phi(K)^T and P = (G V^T) / den - c (queries x keys),
+            // i >= j, masked and turned into bf16 operands.  P comes from the
+            // raw g rows (exact operands) scaled in fp32: it can be a small
+            // difference (one key: P_00 = eps / den_0 * g.v / den_0), which
+            // products with bf16-rounded gn would not resolve.
             bf16x8 Aop[2], Pop[2];
             {
                 f32x16 A = zero16();
@@ -509,15 +499,16 @@ void k_bwd_kv_mfma(Args a) {
                 f32x16 P = zero16();
 #pragma unroll 4
                 for (int s = 0; s < D / 16; ++s)
-                    P = mfma(ld8<TD>(sG, l32, 16 * s + 8 * h), ld8<TD>(sV, l32, 16 * s + 8 * h), P);
+                    P = mfma(ld8<TD>(sGr, l32, 16 * s + 8 * h), ld8<TD>(sV, l32, 16 * s + 8 * h), P);
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const float4 cv = *reinterpret_cast<const float4 *>(sCc + 8 * q4 + 4 * h);
-                    const float cr[4] = {cv.x, cv.y, cv.z, cv.w};
+                    const float4 iv = *reinterpret_cast<const float4 *>(sIq + 8 * q4 + 4 * h);
+                    const float cr[4] = {cv.x, cv.y, cv.z, cv.w}, ir[4] = {iv.x, iv.y, iv.z, iv.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * q4 + e;
-                        P[r] = acc_row(r, h) >= l32 ? P[r] - cr[e] : 0.f;
+                        P[r] = acc_row(r, h) >= l32 ? P[r] * ir[e] - cr[e] : 0.f;
                     }
                 }
                 Pop[0] = acc_op(P, 0);
@@ -605,9 +596,12 @@ hipError_t by_phi(const Args &a, int phi, hipStream_t s) {
 
 }  // namespace
 
-bool mfma_bwd_serves(int bf16, int D, int has_cos) { return bf16 && !has_cos && (D == 64 || D == 128); }
+bool mfma_bwd_serves(int bf16, int causal, int D, int has_cos) {
+    return bf16 && (D == 64 || D == 128) && (!has_cos || causal);
+}
 
 hipError_t mfma_bwd_run(const Args &a, int phi, int causal, hipStream_t s) {
+    if (a.F == 2 * a.D) return mfma_bwd_cos_run(a, phi, s);   // causal (mfma_bwd_serves)
     if (a.D == 64) return causal ? by_phi<64, true>(a, phi, s) : by_phi<64, false>(a, phi, s);
     return causal ? by_phi<128, true>(a, phi, s) : by_phi<128, false>(a, phi, s);
 }

@@ -1,0 +1,575 @@
+// la_mfma_bwd_cos.hip -- bf16 causal backward with the cos/sin features
+// (F = 2D) on the gfx950 matrix cores.
+//
+// The derivative is the one of la_mfma_bwd.hip (SVD_linear_Attention,
+// "Module neuralops.core.triton_kernels.linear_attn", function bwd; module
+// docstring: cos/sin modulation) with Phi(x_t) = [cos_t phi(x_t),
+// sin_t phi(x_t)] of width F = 2D.  The chain rule through the modulation
+// gives, for d < D,
+//   dq_d = phi'(q_d) (cos_i dPhi(q_i)_d + sin_i dPhi(q_i)_{D+d}),   likewise dk.
+// There are twice as many feature blocks (F/32) as value blocks, so one wave
+// per feature block holds its slice of the state (S^T in the dq kernel, R^T
+// in the dk/dv kernel): a workgroup is F/32 waves, and the two halves of
+// dPhi meet through LDS.  With every wave busy with its own state, the
+// per-segment (R, r) sums get a pass of their own (k_bwd_r_cos_mfma) between
+// the dq and the dk/dv kernels; it reads the den_i and c_i the dq kernel
+// writes.  Each wave computes the chunk's A (over the F features) and T
+// tiles itself.
+#include "la_common.h"
+#include "la_kernels.h"
+#include "la_mfma.h"
+#include "la_timing.h"
+
+namespace la {
+namespace {
+
+using namespace mf;
+
+constexpr int kCc = 32;   // chunk length: one 32x32 tile of A per head
+
+// phi' of a raw bf16 input (the modulated features do not give it back);
+// the gradients it scales are rounded to bf16.
+template <int PHI>
+__device__ __forceinline__ float phi_d_raw(float x) {
+    if constexpr (PHI == kElu1) return x > 0.f ? 1.f : __expf(x);
+    else return phi_d<PHI>(x);
+}
+
+// ---------------------------------------------------------------------------
+// k_bwd_q_cos_mfma: forward over the 32-row chunks of one (batch, KV head,
+// segment) for the n_rep query heads.  Wave w (of F/32) holds S^T for
+// feature block w (all value blocks) and z of that block; it forms A^T, T^T
+// (A over all F features), U = S g for its block, dPhi(q) for its block,
+// and the waves of the sin half pass cos/sin-weighted tiles to those of the
+// cos half, which apply phi' and store dq.  Writes den_i and c_i.
+// ---------------------------------------------------------------------------
+template <int D, int PHI>
+__global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2)))
+void k_bwd_q_cos_mfma(Args a) {
+    constexpr int F = 2 * D, NW = D / 32, FW = F / 32, NT = 64 * FW;
+    using TF = Pad<F>;
+    using TD = Pad<D>;
+    __shared__ __attribute__((aligned(16))) u16 sK[kCc * TF::ld];
+    __shared__ __attribute__((aligned(16))) u16 sV[kCc * TD::ld];
+    __shared__ __attribute__((aligned(16))) u16 sQ[kCc * TF::ld];
+    __shared__ __attribute__((aligned(16))) u16 sQr[kCc * TD::ld];   // raw q rows, for phi'
+    __shared__ __attribute__((aligned(16))) u16 sG[kCc * TD::ld];
+    __shared__ __attribute__((aligned(16))) float sz[F];
+    __shared__ __attribute__((aligned(16))) float sX[NW][64 * 16];   // sin halves of dPhi(q)
+    __shared__ float sQZ[kCc], sQU[FW][kCc];
+
+    const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const int t = threadIdx.x, l = t & 63, w = t >> 6, h = l >> 5, l32 = l & 31;
+    const size_t SD = (size_t)F * D + F;
+    const u16 *kh = static_cast<const u16 *>(a.k) + (size_t)bg * a.N * D;
+    const u16 *vh = static_cast<const u16 *>(a.v) + (size_t)bg * a.N * D;
+    const size_t bh0 = (size_t)b * a.H + (size_t)g * a.nrep;
+    const u16 *qbase = static_cast<const u16 *>(a.q);
+    const u16 *gbase = static_cast<const u16 *>(a.g);
+    u16 *dqbase = static_cast<u16 *>(a.dq);
+
+    // exclusive prefix state of the segment: S^T tiles (value block db x
+    // feature block w) and the z tile of block w
+    const float *Sp = a.ws_S + ((size_t)bg * (a.nseg + 1) + seg) * SD;
+    f32x16 X[NW], Z;
+#pragma unroll
+    for (int db = 0; db < NW; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) X[db][r] = Sp[(size_t)(32 * w + l32) * D + 32 * db + acc_row(r, h)];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Z[r] = Sp[(size_t)F * D + 32 * w + acc_row(r, h)];
+    for (int e = t; e < F; e += NT) sz[e] = Sp[(size_t)F * D + e];
+    const bf16x8 one = ones8();
+
+    const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
+    RawTile<D, NT, kCc> rK, rV, rQ, rG;
+    rK.load(kh, row0, a.N);
+    rV.load(vh, row0, a.N);
+    rQ.load(qbase + bh0 * a.N * D, row0, a.N);
+    rG.load(gbase + bh0 * a.N * D, row0, a.N);
+    for (int c0 = row0; c0 < row1; c0 += kCc) {
+        __syncthreads();
+        rK.template store_feat<PHI, true, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rV.template store<TD>(sV);
+        rK.load(kh, c0 + kCc, a.N);   // next chunk (past the segment: unused)
+        rV.load(vh, c0 + kCc, a.N);
+        const int ti = min(c0 + l32, a.N - 1);
+        const float mq = w < NW ? a.cw[ti] : a.sw[ti];   // this lane's query weight for block w
+        for (int rep = 0; rep < a.nrep; ++rep) {
+            const size_t bh = bh0 + rep;
+            if (rep > 0) __syncthreads();
+            rQ.template store_feat<PHI, true, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+            rQ.template store<TD>(sQr);
+            rG.template store<TD>(sG);
+            __syncthreads();
+            {   // Q, G rows of the next head, or of the first head at the next chunk
+                const bool last = rep + 1 == a.nrep;
+                const size_t hn = bh0 + (last ? 0 : rep + 1);
+                const int cn = last ? c0 + kCc : c0;
+                rQ.load(qbase + hn * a.N * D, cn, a.N);
+                rG.load(gbase + hn * a.N * D, cn, a.N);
+            }
+            const bool ok = c0 + l32 < a.N;   // this lane's query row exists
+
+            // A^T over the F features (the cos/sin weighting included), T^T
+            f32x16 At = zero16(), Tt = zero16();
+#pragma unroll 4
+            for (int s = 0; s < F / 16; ++s)
+                At = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), At);
+#pragma unroll 4
+            for (int s = 0; s < D / 16; ++s)
+                Tt = mfma(ld8<TD>(sV, l32, 16 * s + 8 * h), ld8<TD>(sG, l32, 16 * s + 8 * h), Tt);
+            float dA = 0.f, aT = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float x = acc_row(r, h) <= l32 ? (float)(__bf16)At[r] : 0.f;   // the forward's A
+                dA += x;
+                aT += x * Tt[r];
+            }
+            dA += __shfl_xor(dA, 32);
+            aT += __shfl_xor(aT, 32);
+            const float den = ok ? dA + sQZ[l32] + a.eps : 1.f;
+            // U^T = S g (feature block w x the chunk's queries), Phi(q).U over the block
+            f32x16 U = zero16();
+#pragma unroll
+            for (int db = 0; db < NW; ++db)
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    U = mfma(acc_op(X[db], s), ld4x2<TD>(sG, l32, 32 * db + 16 * s + 4 * h), U);
+            float qu = 0.f;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                float x4[4];
+                ld4f(sQ + TF::at(l32, 32 * w + 8 * q4 + 4 * h), x4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qu += x4[e] * U[4 * q4 + e];
+            }
+            qu += __shfl_xor(qu, 32);
+            if (h == 0) sQU[w][l32] = qu;
+            __syncthreads();
+
+            float gsum = aT;
+#pragma unroll
+            for (int ww = 0; ww < FW; ++ww) gsum += sQU[ww][l32];
+            const float inv = rcp(den);
+            const float c = ok ? gsum * inv * inv : 0.f;
+            if (w == 0 && h == 0 && ok) {   // for the R pass and the dk/dv kernel
+                a.ws_den[bh * a.N + c0 + l32] = den;
+                a.ws_c[bh * a.N + c0 + l32] = c;
+            }
+            // P^T = T^T / den - c (masked); dPhi(q)^T = Phi(K)^T P^T + U^T / den - z c
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Tt[r] = acc_row(r, h) <= l32 ? Tt[r] * inv - c : 0.f;
+            f32x16 Qd = zero16();
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int k0 = 16 * s + 4 * h;
+                const bf16x8 ka = tr8(tr_addr<TF>(sK, k0, 32 * w), tr_addr<TF>(sK, k0 + 8, 32 * w));
+                Qd = mfma(ka, acc_op(Tt, s), Qd);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                Qd[r] = mq * (Qd[r] + U[r] * inv - sz[32 * w + acc_row(r, h)] * c);
+            if (w >= NW) put_acc(sX[w - NW], Qd);   // sin half, to the wave of the same dims
+            __syncthreads();
+            if (w < NW) {
+                const f32x16 Qs = get_acc(sX[w]);
+                const int row = c0 + l32;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int d0 = 32 * w + 8 * q4 + 4 * h;
+                    float qr[4], o[4];
+                    ld4f(sQr + TD::at(l32, d0), qr);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = phi_d_raw<PHI>(qr[e]) * (Qd[4 * q4 + e] + Qs[4 * q4 + e]);
+                    if (row < a.N) st4bf(dqbase + bh * a.N * D + (size_t)row * D + d0, o);
+                }
+            }
+        }
+        // carry (S^T, z) past this chunk
+#pragma unroll
+        for (int s = 0; s < kCc / 16; ++s) {
+            const int k0 = 16 * s + 8 * h;
+            const bf16x8 kb = tr8(tr_addr<TF>(sK, k0, 32 * w), tr_addr<TF>(sK, k0 + 4, 32 * w));
+            Z = mfma(kb, one, Z);
+#pragma unroll
+            for (int db = 0; db < NW; ++db) {
+                const bf16x8 va = tr8(tr_addr<TD>(sV, k0, 32 * db), tr_addr<TD>(sV, k0 + 4, 32 * db));
+                X[db] = mfma(va, kb, X[db]);
+            }
+        }
+        // every staging of this chunk has read sz; only this wave reads block w
+        if (l32 == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sz[32 * w + acc_row(r, h)] = Z[r];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_bwd_r_cos_mfma: per (batch, KV head, segment) the segment's sums over
+// the n_rep query heads of R = sum_i Phi(q_i) gn_i^T (F x D) and
+// r = sum_i c_i Phi(q_i), gn_i = g_i / den_i, written as fp32 to the
+// workspace record of the segment.  Wave w owns value block w: the F/32 R
+// tiles of that block, and the r tiles of feature blocks w, w + D/32, ...
+// (r = Phi(Q)^T c on the matrix cores with c rounded to bf16, every column
+// of an r tile holding r).
+// ---------------------------------------------------------------------------
+template <int D, int PHI>
+__global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(1))) void k_bwd_r_cos_mfma(Args a) {
+    constexpr int F = 2 * D, NW = D / 32, FB = F / 32, ZB = FB / NW, NT = 2 * D;
+    using TF = PadI<F>;
+    using TD = PadI<D>;
+    __shared__ __attribute__((aligned(16))) u16 sQ[kCc * TF::ld];
+    __shared__ __attribute__((aligned(16))) u16 sG[kCc * TD::ld];
+    __shared__ __attribute__((aligned(16))) float sC[kCc];
+    const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const int t = threadIdx.x, l = t & 63, h = l >> 5, l32 = l & 31;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // value block, uniform
+    const size_t bh0 = (size_t)b * a.H + (size_t)g * a.nrep;
+    const u16 *qbase = static_cast<const u16 *>(a.q);
+    const u16 *gbase = static_cast<const u16 *>(a.g);
+    f32x16 R[FB], Zr[ZB];
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb) R[fb] = zero16();
+#pragma unroll
+    for (int c = 0; c < ZB; ++c) Zr[c] = zero16();
+
+    const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
+    constexpr int NV = RawTile<D, NT, kCc>::NV, V8 = D / 8;
+    RawTile<D, NT, kCc> rQ, rG;
+    float pden[NV], pc;   // den of this thread's G rows and c of row t % 32, prefetched
+    auto load_dc = [&](size_t hh, int cc) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) pden[k] = a.ws_den[hh * a.N + min(cc + (t + k * NT) / V8, a.N - 1)];
+        pc = a.ws_c[hh * a.N + min(cc + (t & (kCc - 1)), a.N - 1)];
+    };
+    rQ.load(qbase + bh0 * a.N * D, row0, a.N);
+    rG.load(gbase + bh0 * a.N * D, row0, a.N);
+    load_dc(bh0, row0);
+    for (int c0 = row0; c0 < row1; c0 += kCc) {
+        for (int rep = 0; rep < a.nrep; ++rep) {
+            __syncthreads();   // the previous head's LDS reads are done
+            rQ.template store_feat<PHI, true, TF, false>(sQ, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {   // gn = g / den (rows past N: zeros)
+                const int idx = t + k * NT, i = idx / V8, c8 = (idx % V8) * 8;
+                const float inv = c0 + i < a.N ? rcp(pden[k]) : 0.f;
+                const uint4 u = rG.v[k];
+                uint32_t wds[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    wds[e] = pk2(__uint_as_float(wds[e] << 16) * inv, __uint_as_float(wds[e] & 0xffff0000u) * inv);
+                *reinterpret_cast<uint4 *>(sG + TD::at(i, c8)) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+            }
+            if (t < kCc) sC[t] = c0 + t < a.N ? pc : 0.f;
+            __syncthreads();
+            {   // the next head's rows, or the first head's at the next chunk
+                const bool last = rep + 1 == a.nrep;
+                const size_t hn = bh0 + (last ? 0 : rep + 1);
+                const int cn = last ? c0 + kCc : c0;
+                rQ.load(qbase + hn * a.N * D, cn, a.N);
+                rG.load(gbase + hn * a.N * D, cn, a.N);
+                load_dc(hn, cn);
+            }
+            // R[fb] += Phi(Q)^T gn, r += Phi(Q)^T c (natural k order: half h
+            // holds rows 16s + 8h .. +7)
+#pragma unroll
+            for (int s = 0; s < kCc / 16; ++s) {
+                const int k0 = 16 * s + 8 * h;
+                const bf16x8 gb = tr8(tr_addr<TD>(sG, k0, 32 * w), tr_addr<TD>(sG, k0 + 4, 32 * w));
+                const float4 c_lo = *reinterpret_cast<const float4 *>(sC + k0);
+                const float4 c_hi = *reinterpret_cast<const float4 *>(sC + k0 + 4);
+                const float cr[8] = {c_lo.x, c_lo.y, c_lo.z, c_lo.w, c_hi.x, c_hi.y, c_hi.z, c_hi.w};
+                bf16x8 cb;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) cb[e] = (__bf16)cr[e];
+#pragma unroll
+                for (int fb = 0; fb < FB; ++fb) {
+                    const bf16x8 qa = tr8(tr_addr<TF>(sQ, k0, 32 * fb), tr_addr<TF>(sQ, k0 + 4, 32 * fb));
+                    R[fb] = mfma(qa, gb, R[fb]);
+                    if (fb % NW == w) Zr[fb / NW] = mfma(qa, cb, Zr[fb / NW]);
+                }
+            }
+        }
+    }
+    float *Ro = a.ws_Rp + ((size_t)bg * a.nseg + seg) * ((size_t)F * D + F);
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Ro[(size_t)(32 * fb + acc_row(r, h)) * D + 32 * w + l32] = R[fb][r];
+    if (l32 == 0) {
+#pragma unroll
+        for (int c = 0; c < ZB; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Ro[(size_t)F * D + 32 * (w + NW * c) + acc_row(r, h)] = Zr[c][r];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_bwd_kv_cos_mfma: backward over the 32-row chunks of one (batch, KV head,
+// segment) from the exclusive suffix (R, r).  Wave w (of F/32) holds R^T for
+// feature block w and forms dPhi(k) of that block; waves w < D/32 also form
+// dv for value block w.  The sin-half waves pass their weighted dPhi(k)
+// tiles to the cos-half waves, which apply phi' and stage dk.
+// ---------------------------------------------------------------------------
+template <int D, int PHI>
+__global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2)))
+void k_bwd_kv_cos_mfma(Args a) {
+    constexpr int F = 2 * D, NW = D / 32, FW = F / 32, NT = 64 * FW;
+    using TF = Pad<F>;
+    using TD = Pad<D>;
+    __shared__ __attribute__((aligned(16))) u16 sK[kCc * TF::ld];
+    __shared__ __attribute__((aligned(16))) u16 sKr[kCc * TD::ld];   // raw k (phi'), then dk rows
+    __shared__ __attribute__((aligned(16))) u16 sV[kCc * TD::ld];
+    __shared__ __attribute__((aligned(16))) u16 sQ[kCc * TF::ld];    // also the sin halves of dPhi(k)
+    __shared__ __attribute__((aligned(16))) u16 sG[kCc * TD::ld];    // gn, then dv rows
+    __shared__ __attribute__((aligned(16))) u16 sR[F * TD::ld];
+    __shared__ __attribute__((aligned(16))) u16 sGr[kCc * TD::ld];   // raw g rows (for P)
+    __shared__ __attribute__((aligned(16))) float sCc[kCc], sIq[kCc];   // c_i, 1 / den_i
+    __shared__ float sr[F];
+    static_assert(sizeof(sQ) >= NW * 64 * 16 * sizeof(float), "sQ holds the sin-half tiles");
+
+    const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const int t = threadIdx.x, l = t & 63, w = t >> 6, h = l >> 5, l32 = l & 31;
+    const size_t SD = (size_t)F * D + F;
+    const u16 *kh = static_cast<const u16 *>(a.k) + (size_t)bg * a.N * D;
+    const u16 *vh = static_cast<const u16 *>(a.v) + (size_t)bg * a.N * D;
+    u16 *dkh = static_cast<u16 *>(a.dk) + (size_t)bg * a.N * D;
+    u16 *dvh = static_cast<u16 *>(a.dv) + (size_t)bg * a.N * D;
+    const size_t bh0 = (size_t)b * a.H + (size_t)g * a.nrep;
+    const u16 *qbase = static_cast<const u16 *>(a.q);
+    const u16 *gbase = static_cast<const u16 *>(a.g);
+    float *sX = reinterpret_cast<float *>(sQ);
+
+    const float *Rp = a.ws_Rs + ((size_t)bg * (a.nseg + 1) + seg) * SD;
+    f32x16 Rt[NW];
+#pragma unroll
+    for (int db = 0; db < NW; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Rt[db][r] = Rp[(size_t)(32 * w + l32) * D + 32 * db + acc_row(r, h)];
+    for (int e = t; e < F; e += NT) sr[e] = Rp[(size_t)F * D + e];
+
+    const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
+    const int nch = (row1 - row0 + kCc - 1) / kCc;
+    constexpr int NV = RawTile<D, NT, kCc>::NV, V8 = D / 8;
+    RawTile<D, NT, kCc> rK, rV, rQ, rG;
+    // prefetched: den of this thread's G rows, c and den of query t % 32
+    float pden[NV], pc, pdq;
+    auto load_dc = [&](size_t hh, int cc) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) pden[k] = a.ws_den[hh * a.N + min(cc + (t + k * NT) / V8, a.N - 1)];
+        pc = a.ws_c[hh * a.N + min(cc + (t & (kCc - 1)), a.N - 1)];
+        pdq = a.ws_den[hh * a.N + min(cc + (t & (kCc - 1)), a.N - 1)];
+    };
+    {
+        const int c0 = row0 + (nch - 1) * kCc;
+        rK.load(kh, c0, a.N);
+        rV.load(vh, c0, a.N);
+        rQ.load(qbase + bh0 * a.N * D, c0, a.N);
+        rG.load(gbase + bh0 * a.N * D, c0, a.N);
+        load_dc(bh0, c0);
+    }
+    for (int ci = nch - 1; ci >= 0; --ci) {
+        const int c0 = row0 + ci * kCc;
+        const int cn = ci > 0 ? c0 - kCc : c0;   // next chunk (none: reload this one)
+        __syncthreads();   // the previous chunk's rows are stored
+        rK.template store_feat<PHI, true, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rK.template store<TD>(sKr);
+        rV.template store<TD>(sV);
+        rK.load(kh, cn, a.N);
+        rV.load(vh, cn, a.N);
+        // R (bf16, [feature][value]) for the state terms
+#pragma unroll
+        for (int db = 0; db < NW; ++db)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                float x[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = Rt[db][4 * q4 + e];
+                st4bf(sR + TD::at(32 * w + l32, 32 * db + 8 * q4 + 4 * h), x);
+            }
+        __syncthreads();
+
+        // state terms: dPhi(k)^T = R V^T - r (block w); dv^T = R^T Phi(K)^T (value block w)
+        f32x16 dK = zero16(), dV = zero16();
+#pragma unroll
+        for (int db = 0; db < NW; ++db)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                dK = mfma(ld4x2<TD>(sR, 32 * w + l32, 32 * db + 16 * s + 4 * h),
+                          ld4x2<TD>(sV, l32, 32 * db + 16 * s + 4 * h), dK);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dK[r] -= sr[32 * w + acc_row(r, h)];
+        if (w < NW) {
+#pragma unroll 4
+            for (int s = 0; s < F / 16; ++s) {
+                const int k0 = 16 * s + 8 * h;
+                dV = mfma(tr8(tr_addr<TD>(sR, k0, 32 * w), tr_addr<TD>(sR, k0 + 4, 32 * w)),
+                          ld8<TF>(sK, l32, 16 * s + 8 * h), dV);
+            }
+        }
+
+        for (int rep = 0; rep < a.nrep; ++rep) {
+            __syncthreads();   // the previous head's LDS reads (and of r) are done
+            rQ.template store_feat<PHI, true, TF, false>(sQ, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {   // gn = g / den (rows past N: zeros)
+                const int idx = t + k * NT, i = idx / V8, c8 = (idx % V8) * 8;
+                const float inv = c0 + i < a.N ? rcp(pden[k]) : 0.f;
+                const uint4 u = rG.v[k];
+                uint32_t wds[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    wds[e] = pk2(__uint_as_float(wds[e] << 16) * inv, __uint_as_float(wds[e] & 0xffff0000u) * inv);
+                *reinterpret_cast<uint4 *>(sG + TD::at(i, c8)) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+            }
+            if (t < kCc) {
+                sCc[t] = c0 + t < a.N ? pc : 0.f;
+                sIq[t] = c0 + t < a.N ? rcp(pdq) : 0.f;
+            }
+            rG.template store<TD>(sGr);
+            __syncthreads();
+            {   // Q, G, den, c of the next head, or of the first head at the next chunk
+                const bool last = rep + 1 == a.nrep;
+                const size_t hn = bh0 + (last ? 0 : rep + 1);
+                const int cq = last ? cn : c0;
+                rQ.load(qbase + hn * a.N * D, cq, a.N);
+                rG.load(gbase + hn * a.N * D, cq, a.N);
+                load_dc(hn, cq);
+            }
+            // A = Phi(Q) Phi(K)^T (over F) and P = (G V^T) / den - c (queries x keys),
+            // i >= j; P from the raw g rows scaled in fp32 (it can be a small
+            // difference, which bf16-rounded gn would not resolve)
+            bf16x8 Aop[2], Pop[2];
+            {
+                f32x16 A = zero16();
+#pragma unroll 4
+                for (int s = 0; s < F / 16; ++s)
+                    A = mfma(ld8<TF>(sQ, l32, 16 * s + 8 * h), ld8<TF>(sK, l32, 16 * s + 8 * h), A);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) A[r] = acc_row(r, h) >= l32 ? A[r] : 0.f;
+                Aop[0] = acc_op(A, 0);
+                Aop[1] = acc_op(A, 1);
+            }
+            {
+                f32x16 P = zero16();
+#pragma unroll 4
+                for (int s = 0; s < D / 16; ++s)
+                    P = mfma(ld8<TD>(sGr, l32, 16 * s + 8 * h), ld8<TD>(sV, l32, 16 * s + 8 * h), P);
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const float4 cv = *reinterpret_cast<const float4 *>(sCc + 8 * q4 + 4 * h);
+                    const float4 iv = *reinterpret_cast<const float4 *>(sIq + 8 * q4 + 4 * h);
+                    const float cr[4] = {cv.x, cv.y, cv.z, cv.w}, ir[4] = {iv.x, iv.y, iv.z, iv.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * q4 + e;
+                        P[r] = acc_row(r, h) >= l32 ? P[r] * ir[e] - cr[e] : 0.f;
+                    }
+                }
+                Pop[0] = acc_op(P, 0);
+                Pop[1] = acc_op(P, 1);
+            }
+            // in-chunk terms: dPhi(k)^T += Phi(Q)^T P (block w), dv^T += gn^T A (value block w)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int k0 = 16 * s + 4 * h;
+                dK = mfma(tr8(tr_addr<TF>(sQ, k0, 32 * w), tr_addr<TF>(sQ, k0 + 8, 32 * w)), Pop[s], dK);
+                if (w < NW)
+                    dV = mfma(tr8(tr_addr<TD>(sG, k0, 32 * w), tr_addr<TD>(sG, k0 + 8, 32 * w)), Aop[s], dV);
+            }
+            // R^T += gn^T Phi(Q) for this chunk's rows; r += Phi(Q)^T c
+#pragma unroll
+            for (int s = 0; s < kCc / 16; ++s) {
+                const int k0 = 16 * s + 8 * h;
+                const bf16x8 qb = tr8(tr_addr<TF>(sQ, k0, 32 * w), tr_addr<TF>(sQ, k0 + 4, 32 * w));
+#pragma unroll
+                for (int db = 0; db < NW; ++db) {
+                    const bf16x8 ga = tr8(tr_addr<TD>(sG, k0, 32 * db), tr_addr<TD>(sG, k0 + 4, 32 * db));
+                    Rt[db] = mfma(ga, qb, Rt[db]);
+                }
+            }
+            if (t < F) {
+                float acc = 0.f;
+#pragma unroll 8
+                for (int i = 0; i < kCc; ++i) acc += sCc[i] * bf2f(sQ[TF::at(i, t)]);
+                sr[t] += acc;
+            }
+        }
+        // chain rule through cos/sin: the sin-half waves hand sin_j dPhi(k) to
+        // the cos-half wave of the same dims (in sQ, free after the last head)
+        const int tj = min(c0 + l32, a.N - 1);
+        const float mk = w < NW ? a.cw[tj] : a.sw[tj];   // this lane's key weight for block w
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dK[r] *= mk;
+        __syncthreads();   // every read of sQ (and sG) of the last head is done
+        if (w >= NW) put_acc(sX + (w - NW) * 64 * 16, dK);
+        __syncthreads();
+        if (w < NW) {
+            const f32x16 Ks = get_acc(sX + w * 64 * 16);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d0 = 32 * w + 8 * q4 + 4 * h;
+                float kr[4];
+                ld4f(sKr + TD::at(l32, d0), kr);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dK[4 * q4 + e] = phi_d_raw<PHI>(kr[e]) * (dK[4 * q4 + e] + Ks[4 * q4 + e]);
+            }
+            // this lane overwrites exactly the raw-k entries it just read
+            stage_out<TD>(sKr, dK, 1.f, 32 * w);
+            stage_out<TD>(sG, dV, 1.f, 32 * w);
+        }
+        __syncthreads();
+        store_rows<D, NT, TD>(dkh, sKr, c0, a.N);
+        store_rows<D, NT, TD>(dvh, sG, c0, a.N);
+    }
+}
+
+template <int D, int PHI>
+hipError_t run(const Args &a, hipStream_t s) {
+    constexpr int F = 2 * D;
+    const unsigned n_units = (unsigned)(a.B * a.Hkv);
+    const size_t SD = (size_t)F * D + F;
+    hipError_t e = mfma_state_run(a, PHI, s);
+    if (e != hipSuccess) return e;
+    {
+        TimedLaunch tl("k_bwd_q_cos_mfma", s);
+        hipLaunchKernelGGL((k_bwd_q_cos_mfma<D, PHI>), dim3(n_units * a.nseg), dim3(4 * D), 0, s, a);
+    }
+    {
+        TimedLaunch tl("k_bwd_r_cos_mfma", s);
+        hipLaunchKernelGGL((k_bwd_r_cos_mfma<D, PHI>), dim3(n_units * a.nseg), dim3(2 * D), 0, s, a);
+    }
+    {
+        TimedLaunch tl("k_scan_R", s);
+        // per-segment records are already summed over the group's heads
+        e = scan_suffix(a.ws_Rp, a.ws_Rs, a.nseg, SD, a.Hkv, a.Hkv, 1, n_units, s);
+        if (e != hipSuccess) return e;
+    }
+    {
+        TimedLaunch tl("k_bwd_kv_cos_mfma", s);
+        hipLaunchKernelGGL((k_bwd_kv_cos_mfma<D, PHI>), dim3(n_units * a.nseg), dim3(4 * D), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t by_phi(const Args &a, int phi, hipStream_t s) {
+    switch (phi) {
+        case kElu1: return run<D, kElu1>(a, s);
+        case kRelu: return run<D, kRelu>(a, s);
+        default: return run<D, kIdentity>(a, s);
+    }
+}
+
+}  // namespace
+
+hipError_t mfma_bwd_cos_run(const Args &a, int phi, hipStream_t s) {
+    return a.D == 64 ? by_phi<64>(a, phi, s) : by_phi<128>(a, phi, s);
+}
+
+}  // namespace la

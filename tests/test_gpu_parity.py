@@ -64,7 +64,7 @@ def test_small_shapes(case):
 @pytest.mark.parametrize("causal", [True, False])
 def test_edge_lengths(N, causal):
     torch, la = gpu_or_skip()
-    for dtype, D, cos in (("f32", 64, False), ("bf16", 128, True)):
+    for dtype, D, cos in (("f32", 64, False), ("bf16", 128, False), ("bf16", 128, True)):
         t = make(1, 2, 1, N, D, dtype, scale=0.5, cos=cos, seed=N)
         # with one row and a tiny eps, out = v exactly up to eps and dq, dk are
         # O(eps): a normwise comparison would measure rounding noise only
@@ -208,7 +208,7 @@ def test_binding_errors_on_gpu():
 
 def test_kernel_family_per_case():
     """bf16 runs on the matrix-core kernels (causal and bidirectional, forward
-    and backward; the cos/sin backward excepted); float32 on the vector-ALU
+    and backward; the cos/sin backward when causal); float32 on the vector-ALU
     kernels (checked through the library's launch timing)."""
     torch, la = gpu_or_skip()
     t = make(1, 4, 2, 256, 128, "bf16", scale=0.5, seed=1)
@@ -235,3 +235,11 @@ def test_kernel_family_per_case():
     finally:
         la.timing_enable(False)
     assert {"k_state_mfma", "k_fwd_bidir_mfma", "k_bwd_q_bidir_mfma", "k_bwd_kv_bidir_mfma"} <= names, names
+    t = make(1, 4, 2, 256, 64, "bf16", cos=True, scale=0.5, seed=1)
+    la.timing_enable(True)
+    try:
+        run_gpu(la, t, True, "relu", backward=True)
+        names = set(la.timing_collect())
+    finally:
+        la.timing_enable(False)
+    assert {"k_bwd_q_cos_mfma", "k_bwd_r_cos_mfma", "k_bwd_kv_cos_mfma"} <= names, names
