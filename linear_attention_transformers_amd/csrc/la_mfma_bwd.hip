@@ -369,7 +369,9 @@ void k_bwd_kv_mfma(Args a) {
     for (int db = 0; db < NW; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) Rt[db][r] = Rp[(size_t)(32 * w + l32) * D + 32 * db + acc_row(r, h)];
-    for (int e = t; e < F; e += NT) sr[e] = Rp[(size_t)F * D + e];
+    // r lives in the registers of threads t < F (the running suffix); each
+    // chunk publishes a copy to sr for the state term
+    float racc = t < F ? Rp[(size_t)F * D + t] : 0.f;
 
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
     const int nch = (row1 - row0 + kCb - 1) / kCb;
@@ -394,21 +396,44 @@ void k_bwd_kv_mfma(Args a) {
             load_dc(bh0, c0);
         }
     }
-    int pend_c0 = -1;   // dk, dv rows of the previous chunk staged in sQ, sG
+    // this head's query rows into LDS: Phi(Q), gn = g / den, raw g, c, 1 / den
+    // (rows past N: zeros), then the next head's (or the next chunk's first
+    // head's) loads
+    auto stage_head = [&](int c0, int rep, int cn) {
+        rQ.template store_feat<PHI, false, TF, false>(sQ, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int idx = t + k * NT, i = idx / V8, c8 = (idx % V8) * 8, row = c0 + i;
+            const float inv = row < a.N ? rcp(pden[k]) : 0.f;
+            const uint4 u = rG.v[k];
+            uint32_t wds[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                wds[e] = pk2(__uint_as_float(wds[e] << 16) * inv, __uint_as_float(wds[e] & 0xffff0000u) * inv);
+            *reinterpret_cast<uint4 *>(sG + TD::at(i, c8)) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+        }
+        rG.template store<TD>(sGr);
+        if (t < kCb) {
+            sCc[t] = c0 + t < a.N ? pc : 0.f;
+            sIq[t] = c0 + t < a.N ? rcp(pdq) : 0.f;
+        }
+        const bool last = rep + 1 == a.nrep;
+        const size_t hn = bh0 + (last ? 0 : rep + 1);
+        const int cq = last ? cn : c0;
+        rQ.load(qbase + hn * a.N * D, cq, a.N);
+        rG.load(gbase + hn * a.N * D, cq, a.N);
+        load_dc(hn, cq);
+    };
     for (int ci = nch - 1; ci >= 0; --ci) {
         const int c0 = row0 + ci * kCb;
-        __syncthreads();
-        if (pend_c0 >= 0) {
-            store_rows<D, NT, TD>(dkh, sQ, pend_c0, a.N);
-            store_rows<D, NT, TD>(dvh, sG, pend_c0, a.N);
-        }
+        const int cn = ci > 0 ? c0 - kCb : c0;   // next chunk (none: reload this one)
+        __syncthreads();   // every read of the previous chunk's tiles is done
         rK.template store_feat<PHI, false, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
         rV.template store<TD>(sV);
-        const int cn = ci > 0 ? c0 - kCb : c0;   // next chunk (none: reload this one)
         rK.load(kh, cn, a.N);
         rV.load(vh, cn, a.N);
         // R (bf16, [feature][value]) for the state terms (bidirectional: the
-        // total, staged once)
+        // total, staged once), r for the state term
         if (CAUSAL || ci == nch - 1) {
 #pragma unroll
             for (int db = 0; db < NW; ++db)
@@ -419,9 +444,10 @@ void k_bwd_kv_mfma(Args a) {
                     for (int e = 0; e < 4; ++e) x[e] = Rt[db][4 * q4 + e];
                     st4bf(sR + TD::at(32 * w + l32, 32 * db + 8 * q4 + 4 * h), x);
                 }
+            if (t < F) sr[t] = racc;
         }
+        if constexpr (CAUSAL) stage_head(c0, 0, cn);
         __syncthreads();
-
         // state terms: dPhi(k)^T = R V^T - r, dv^T = R^T Phi(K)^T
         f32x16 dK = zero16(), dV = zero16();
 #pragma unroll
@@ -447,38 +473,14 @@ void k_bwd_kv_mfma(Args a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) dK[r] -= sr[32 * w + acc_row(r, h)];
 
-        // causal: the chunk's own queries (in-chunk terms) and the R update
+        // causal: the chunk's own queries (in-chunk terms) and the R update;
+        // the first head's rows were staged with the chunk
         for (int rep = 0; rep < (CAUSAL ? a.nrep : 0); ++rep) {
-            __syncthreads();   // previous head's LDS reads and every read of r are done
-            rQ.template store_feat<PHI, false, TF, false>(sQ, c0, a.N, a.cw, a.sw, nullptr, nullptr);
-            {   // gn = g / den in LDS (rows past N: zeros), and c
-#pragma unroll
-                for (int k = 0; k < NV; ++k) {
-                    const int idx = t + k * NT, i = idx / V8, c8 = (idx % V8) * 8, row = c0 + i;
-                    const float inv = row < a.N ? rcp(pden[k]) : 0.f;
-                    const uint4 u = rG.v[k];
-                    uint32_t wds[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        wds[e] = pk2(__uint_as_float(wds[e] << 16) * inv, __uint_as_float(wds[e] & 0xffff0000u) * inv);
-                    *reinterpret_cast<uint4 *>(sG + TD::at(i, c8)) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
-                }
-                if (t < kCb) {
-                    sCc[t] = c0 + t < a.N ? pc : 0.f;
-                    sIq[t] = c0 + t < a.N ? rcp(pdq) : 0.f;
-                }
-                rG.template store<TD>(sGr);
+            if (rep > 0) {
+                __syncthreads();   // the previous head's LDS reads are done
+                stage_head(c0, rep, cn);
+                __syncthreads();
             }
-            __syncthreads();
-            {   // Q, G, den, c of the next head, or of the first head at the next chunk
-                const bool last = rep + 1 == a.nrep;
-                const size_t hn = bh0 + (last ? 0 : rep + 1);
-                const int cq = last ? cn : c0;
-                rQ.load(qbase + hn * a.N * D, cq, a.N);
-                rG.load(gbase + hn * a.N * D, cq, a.N);
-                load_dc(hn, cq);
-            }
-
             // A = Phi(Q) Phi(K)^T and P = (G V^T) / den - c (queries x keys),
             // i >= j, masked and turned into bf16 operands.  P comes from the
             // raw g rows (exact operands) scaled in fp32: it can be a small
@@ -536,28 +538,27 @@ void k_bwd_kv_mfma(Args a) {
                 float acc = 0.f;
 #pragma unroll 8
                 for (int i = 0; i < kCb; ++i) acc += sCc[i] * bf2f(sQ[TF::at(i, t)]);
-                sr[t] += acc;
+                racc += acc;
             }
         }
-        // dk = phi'(k) dPhi(k), dv; lane holds key l32 and columns 32w + 8q + 4h + 0..3.
-        // The last head's reads of sQ and sG must be over before they take the rows.
-        __syncthreads();
+        // dk = phi'(k) dPhi(k), dv; lane holds key l32 and columns 32w + 8q + 4h + 0..3,
+        // stored straight from the registers (the next chunk's tiles take the LDS)
+        const int row = c0 + l32;
+        if (row < a.N) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int f0 = 32 * w + 8 * q4 + 4 * h;
-            float kf[4];
-            ld4f(sK + TF::at(l32, f0), kf);
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int f0 = 32 * w + 8 * q4 + 4 * h;
+                float kf[4], ok4[4], ov4[4];
+                ld4f(sK + TF::at(l32, f0), kf);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dK[4 * q4 + e] *= phi_d_feat<PHI>(kf[e]);
+                for (int e = 0; e < 4; ++e) {
+                    ok4[e] = dK[4 * q4 + e] * phi_d_feat<PHI>(kf[e]);
+                    ov4[e] = dV[4 * q4 + e];
+                }
+                st4bf(dkh + (size_t)row * D + f0, ok4);
+                st4bf(dvh + (size_t)row * D + f0, ov4);
+            }
         }
-        stage_out<TF>(sQ, dK, 1.f, 32 * w);
-        stage_out<TD>(sG, dV, 1.f, 32 * w);
-        pend_c0 = c0;
-    }
-    __syncthreads();
-    if (pend_c0 >= 0) {
-        store_rows<D, NT, TD>(dkh, sQ, pend_c0, a.N);
-        store_rows<D, NT, TD>(dvh, sG, pend_c0, a.N);
     }
 }
 
