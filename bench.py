@@ -7,7 +7,10 @@ attention over one batch of seeded synthetic input, on one MI355X.
 Default workload: causal, bf16 storage, B=2, H=32, N=16384, D=128, elu+1,
 eps=1e-6 (q, k, v ~ 0.5 N(0,1), grad_out ~ N(0,1), seed 0).  Inputs, outputs
 and workspaces are resident in HBM before timing; W untimed steps, then K
-timed steps between device synchronisations.  One JSON line on stdout:
+timed steps between device synchronisations.  The forward and the backward of
+a step share one workspace, so the backward reuses the forward's state records
+(la_bwd_saved, as the autograd form does); the rate with the backward
+recomputing them (la_bwd) is reported beside.  One JSON line on stdout:
 throughput (tokens/s), the dominant kernel against its roofline (timed with
 HIP events on the library's own stream), and the CPU oracle's throughput on a
 bounded sample of the same workload.
@@ -48,10 +51,14 @@ def kernel_bytes(name, w, s):
         "bwd_q_bidir": 3 * qb,                            # q, g -> dq
         "bwd_kv_causal": 2 * qb + 4 * kvb + 2 * rows,     # q, g, den, c, k, v -> dk, dv
         "bwd_kv_bidir": 4 * kvb,                          # k, v -> dk, dv
+        "bwd_r": 2 * qb + 2 * rows,                       # q, g, den, c (per-segment R, r)
     }
     # matrix-core kernels compute the same parts of the method
     alias = {"k_state_mfma": "state", "k_fwd_mfma": "fwd_causal", "k_bwd_q_mfma": "bwd_q_causal",
-             "k_bwd_kv_mfma": "bwd_kv_causal"}
+             "k_bwd_kv_mfma": "bwd_kv_causal", "k_fwd_bidir_mfma": "fwd_bidir",
+             "k_bwd_q_bidir_mfma": "bwd_q_bidir", "k_bwd_kv_bidir_mfma": "bwd_kv_bidir",
+             "k_bwd_q_cos_mfma": "bwd_q_causal", "k_bwd_r_cos_mfma": "bwd_r",
+             "k_bwd_kv_cos_mfma": "bwd_kv_causal"}
     if name in alias:
         return table[alias[name]]
     for key, val in table.items():
@@ -192,17 +199,18 @@ def main():
     out = torch.empty_like(t["q"])
     grads = (torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"]))
     code = la.LA_BF16 if dtype == "bf16" else la.LA_F32
-    ws_f = torch.empty(la.workspace_bytes("fwd", w.B, w.H, w.Hkv, w.N, w.D, code, causal,
-                                          w.cos), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(la.workspace_bytes("bwd", w.B, w.H, w.Hkv, w.N, w.D, code, causal,
-                                          w.cos), dtype=torch.uint8, device=dev)
+    # one workspace for the forward and the backward: the backward reuses the
+    # forward's state records (la_bwd_saved), as the autograd form does
+    ws = torch.empty(la.workspace_bytes("bwd" if w.backward else "fwd", w.B, w.H, w.Hkv, w.N, w.D,
+                                        code, causal, w.cos), dtype=torch.uint8, device=dev)
 
-    def step():
+    def step(saved=True):
         la.fwd(t["q"], t["k"], t["v"], is_causal=causal, phi=w.phi, eps=w.eps, cos_weight=cw,
-               sin_weight=sw, out=out, workspace=ws_f)
+               sin_weight=sw, out=out, workspace=ws)
         if w.backward:
             la.bwd(t["q"], t["k"], t["v"], t["grad_out"], is_causal=causal, phi=w.phi,
-                   eps=w.eps, cos_weight=cw, sin_weight=sw, workspace=ws_b, grads=grads)
+                   eps=w.eps, cos_weight=cw, sin_weight=sw, workspace=ws, grads=grads,
+                   state_from_fwd=saved)
 
     if args.calibration_copy_mib > 0:
         n = args.calibration_copy_mib * (1 << 20) // 4
@@ -249,6 +257,21 @@ def main():
     t_roof, step_bytes, step_flops = step_roofline(w, s, causal)
     matrix = any("mfma" in k for k in ktimes)
 
+    recompute = None
+    if w.backward:
+        # the same step with the backward computing the state records again
+        # (la_bwd): the rate of a caller that does not keep the workspace
+        log("bench: %d steps with the backward recomputing the forward's state" % args.steps)
+        step(saved=False)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            step(saved=False)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t1
+        recompute = {"ms_per_step": el * 1e3 / args.steps, "value": tokens * args.steps / el,
+                     "unit": "tokens/s"}
+
     result = {
         "metric": "fwd+bwd tokens/sec and % roofline, causal bf16 N=16384 D=128",
         "value": value,
@@ -264,11 +287,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "B": w.B, "H": w.H, "H_kv": w.Hkv, "N": w.N, "D": w.D,
                    "phi": w.phi, "causal": causal, "cos_sin": w.cos, "storage": dtype,
-                   "eps": w.eps, "pass": "fwd+bwd" if w.backward else "fwd"},
+                   "eps": w.eps, "pass": "fwd+bwd" if w.backward else "fwd",
+                   "bwd_state": "saved by the forward (la_bwd_saved)" if w.backward else None},
         "roofline": roof,
         "step_roofline": {"t_roof_ms": t_roof * 1e3, "frac": t_roof * 1e3 / ms_step,
                           "algorithmic_bytes": step_bytes, "algorithmic_flops": step_flops},
         "kernels_ms_per_step": {k: v[1] / args.steps for k, v in ktimes.items()},
+        "bwd_recomputing_state": recompute,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

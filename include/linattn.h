@@ -142,6 +142,33 @@ la_status la_bwd_ex(const void *q, const void *k, const void *v,
                     void *ws, size_t ws_bytes, void *stream, int seg_len);
 
 /*
+ * la_bwd_saved / la_bwd_saved_ex -- la_bwd / la_bwd_ex for a backward that
+ * follows la_fwd / la_fwd_ex with the same arguments (inputs, shape, dtype,
+ * causal, phi, eps, cos_w, sin_w, seg_len) and the same workspace: the
+ * per-segment state records (S, z) that the forward left in ws are used
+ * instead of being computed again (the forward's work saved for the
+ * backward, as autograd saves activations).  ws must hold at least
+ * la_workspace_bytes(LA_OP_BWD, ...) bytes, be given to that la_fwd call,
+ * and be left unchanged in between (any other la_fwd / la_bwd on it
+ * overwrites the records).  These preconditions are the caller's: the
+ * library cannot check them, and when they do not hold the gradients are
+ * wrong.  Results are bitwise equal to la_bwd's.  Errors as la_bwd.
+ */
+la_status la_bwd_saved(const void *q, const void *k, const void *v,
+                       const void *grad_out, void *dq, void *dk, void *dv,
+                       int B, int H, int H_kv, int N, int D, int dtype,
+                       int causal, int phi, float eps, const float *cos_w,
+                       const float *sin_w, void *ws, size_t ws_bytes,
+                       void *stream);
+
+la_status la_bwd_saved_ex(const void *q, const void *k, const void *v,
+                          const void *grad_out, void *dq, void *dk, void *dv,
+                          int B, int H, int H_kv, int N, int D, int dtype,
+                          int causal, int phi, float eps, const float *cos_w,
+                          const float *sin_w, void *ws, size_t ws_bytes,
+                          void *stream, int seg_len);
+
+/*
  * Kernel timing, for measurement tools.  la_timing_enable(1) makes every
  * kernel launch of later la_fwd / la_bwd calls on the calling thread record
  * a pair of HIP events on that call's stream (creating them allocates host

@@ -82,7 +82,10 @@ def load_library(path: str = LIB_PATH):
         lib.la_fwd_ex.argtypes = fwd_args + [i]
         lib.la_bwd.argtypes = bwd_args
         lib.la_bwd_ex.argtypes = bwd_args + [i]
-        for fn in (lib.la_fwd, lib.la_fwd_ex, lib.la_bwd, lib.la_bwd_ex):
+        lib.la_bwd_saved.argtypes = bwd_args
+        lib.la_bwd_saved_ex.argtypes = bwd_args + [i]
+        for fn in (lib.la_fwd, lib.la_fwd_ex, lib.la_bwd, lib.la_bwd_ex, lib.la_bwd_saved,
+                   lib.la_bwd_saved_ex):
             fn.restype = i
         lib.la_status_string.argtypes = [i]
         lib.la_status_string.restype = ctypes.c_char_p
@@ -220,8 +223,13 @@ def fwd(q, k, v, is_causal: bool = False, phi: str = "elu+1", eps: float = 1e-6,
 
 
 def bwd(q, k, v, grad_out, is_causal: bool = False, phi: str = "elu+1", eps: float = 1e-6,
-        cos_weight=None, sin_weight=None, seg_len: int = 0, workspace=None, grads=None):
-    """Backward: (dq [B,H,N,D], dk [B,H_kv,N,D], dv [B,H_kv,N,D]) of fwd for grad_out."""
+        cos_weight=None, sin_weight=None, seg_len: int = 0, workspace=None, grads=None,
+        state_from_fwd: bool = False):
+    """Backward: (dq [B,H,N,D], dk [B,H_kv,N,D], dv [B,H_kv,N,D]) of fwd for grad_out.
+
+    state_from_fwd: `workspace` is the one the forward on these same inputs and
+    arguments was given (sized by workspace_bytes("bwd", ...)) and still holds
+    its state records, which the backward then reuses (la_bwd_saved)."""
     import torch
 
     lib = load_library()
@@ -239,9 +247,14 @@ def bwd(q, k, v, grad_out, is_causal: bool = False, phi: str = "elu+1", eps: flo
                 raise ValueError("%s must be a contiguous tensor like %s" % (name, "q" if name == "dq" else "k"))
     nbytes = workspace_bytes("bwd", B, H, Hkv, N, D, code, is_causal, cos_weight is not None,
                              seg_len)
-    if workspace is None or workspace.numel() < nbytes:
+    if state_from_fwd:
+        if workspace is None or workspace.numel() < nbytes:
+            raise ValueError("state_from_fwd needs the forward's workspace, of at least %d bytes"
+                             % nbytes)
+    elif workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    st = lib.la_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(grad_out), _ptr(dq), _ptr(dk), _ptr(dv),
+    entry = lib.la_bwd_saved_ex if state_from_fwd else lib.la_bwd_ex
+    st = entry(_ptr(q), _ptr(k), _ptr(v), _ptr(grad_out), _ptr(dq), _ptr(dk), _ptr(dv),
                        B, H, Hkv, N, D, code, int(bool(is_causal)), PHI[phi], float(eps),
                        _fptr(cos_weight), _fptr(sin_weight), _ptr(workspace), workspace.numel(),
                        _stream(q.device), int(seg_len))

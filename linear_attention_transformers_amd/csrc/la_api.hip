@@ -34,7 +34,12 @@ bool timing_on() { return g_timing; }
 
 void timing_begin(const char *name, hipStream_t s) {
     TimingRec r{name, nullptr, nullptr};
-    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) return;
+    // timing-only events: no system-scope fence (cache writeback) at each record
+    if (hipEventCreateWithFlags(&r.start, hipEventDisableSystemFence) != hipSuccess) return;
+    if (hipEventCreateWithFlags(&r.stop, hipEventDisableSystemFence) != hipSuccess) {
+        (void)hipEventDestroy(r.start);
+        return;
+    }
     if (hipEventRecord(r.start, s) != hipSuccess) {
         (void)hipEventDestroy(r.start);
         (void)hipEventDestroy(r.stop);
@@ -190,10 +195,13 @@ la_status la_fwd(const void *q, const void *k, const void *v, void *out, int B, 
                      ws_bytes, stream, 0);
 }
 
-la_status la_bwd_ex(const void *q, const void *k, const void *v, const void *grad_out, void *dq,
-                    void *dk, void *dv, int B, int H, int H_kv, int N, int D, int dtype,
-                    int causal, int phi, float eps, const float *cos_w, const float *sin_w,
-                    void *ws, size_t ws_bytes, void *stream, int seg_len) {
+namespace {
+
+// The backward; state_ready: ws holds the forward's state records (la_bwd_saved).
+la_status bwd_impl(const void *q, const void *k, const void *v, const void *grad_out, void *dq,
+                   void *dk, void *dv, int B, int H, int H_kv, int N, int D, int dtype,
+                   int causal, int phi, float eps, const float *cos_w, const float *sin_w,
+                   void *ws, size_t ws_bytes, void *stream, int seg_len, int state_ready) {
     g_err[0] = 0;
     if (!q || !k || !v || !grad_out || !dq || !dk || !dv)
         return fail(LA_ERR_INVALID, "q, k, v, grad_out, dq, dk and dv must be non-NULL");
@@ -214,18 +222,46 @@ la_status la_bwd_ex(const void *q, const void *k, const void *v, const void *gra
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
+    a.state_ready = state_ready;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (uses_mfma(1, dtype, causal, D, cos_w != nullptr))
         return launch_status(la::mfma_bwd_run(a, phi, causal, s));
     return launch_status(la::generic_run(a, dtype == LA_BF16, 1, causal != 0, phi, s));
 }
 
+}  // namespace
+
+la_status la_bwd_ex(const void *q, const void *k, const void *v, const void *grad_out, void *dq,
+                    void *dk, void *dv, int B, int H, int H_kv, int N, int D, int dtype,
+                    int causal, int phi, float eps, const float *cos_w, const float *sin_w,
+                    void *ws, size_t ws_bytes, void *stream, int seg_len) {
+    return bwd_impl(q, k, v, grad_out, dq, dk, dv, B, H, H_kv, N, D, dtype, causal, phi, eps,
+                    cos_w, sin_w, ws, ws_bytes, stream, seg_len, 0);
+}
+
 la_status la_bwd(const void *q, const void *k, const void *v, const void *grad_out, void *dq,
                  void *dk, void *dv, int B, int H, int H_kv, int N, int D, int dtype, int causal,
                  int phi, float eps, const float *cos_w, const float *sin_w, void *ws,
                  size_t ws_bytes, void *stream) {
-    return la_bwd_ex(q, k, v, grad_out, dq, dk, dv, B, H, H_kv, N, D, dtype, causal, phi, eps,
-                     cos_w, sin_w, ws, ws_bytes, stream, 0);
+    return bwd_impl(q, k, v, grad_out, dq, dk, dv, B, H, H_kv, N, D, dtype, causal, phi, eps,
+                    cos_w, sin_w, ws, ws_bytes, stream, 0, 0);
+}
+
+la_status la_bwd_saved_ex(const void *q, const void *k, const void *v, const void *grad_out,
+                          void *dq, void *dk, void *dv, int B, int H, int H_kv, int N, int D,
+                          int dtype, int causal, int phi, float eps, const float *cos_w,
+                          const float *sin_w, void *ws, size_t ws_bytes, void *stream,
+                          int seg_len) {
+    return bwd_impl(q, k, v, grad_out, dq, dk, dv, B, H, H_kv, N, D, dtype, causal, phi, eps,
+                    cos_w, sin_w, ws, ws_bytes, stream, seg_len, 1);
+}
+
+la_status la_bwd_saved(const void *q, const void *k, const void *v, const void *grad_out,
+                       void *dq, void *dk, void *dv, int B, int H, int H_kv, int N, int D,
+                       int dtype, int causal, int phi, float eps, const float *cos_w,
+                       const float *sin_w, void *ws, size_t ws_bytes, void *stream) {
+    return bwd_impl(q, k, v, grad_out, dq, dk, dv, B, H, H_kv, N, D, dtype, causal, phi, eps,
+                    cos_w, sin_w, ws, ws_bytes, stream, 0, 1);
 }
 
 const char *la_status_string(int status) {

@@ -77,6 +77,7 @@ struct Args {
     int L;          // segment length in rows (multiple of every chunk length)
     int nseg;
     float eps;
+    int state_ready;  // backward: ws_S already holds the forward's prefix / total records
 };
 
 // ---------------------------------------------------------------------------

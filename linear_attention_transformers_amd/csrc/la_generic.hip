@@ -731,11 +731,11 @@ hipError_t run_bwd(const Args &a, int causal, hipStream_t s) {
     const unsigned n_kv = n_units * a.nseg;
     const size_t SD = (size_t)F * D + F;
     const dim3 scan_grid((unsigned)((SD + kNT - 1) / kNT), n_units);
-    {
-        TimedLaunch tl("k_state", s);
-        hipLaunchKernelGGL((k_state<T, D, F, PHI>), dim3(n_units * a.nseg), dim3(kNT), 0, s, a);
-    }
-    {
+    if (!a.state_ready) {   // else the forward's records are in ws_S already
+        {
+            TimedLaunch tl("k_state", s);
+            hipLaunchKernelGGL((k_state<T, D, F, PHI>), dim3(n_units * a.nseg), dim3(kNT), 0, s, a);
+        }
         TimedLaunch tl("k_scan_S", s);
         hipLaunchKernelGGL(k_scan_S, scan_grid, dim3(kNT), 0, s, a.ws_S, a.nseg, SD,
                            (size_t)n_units);
