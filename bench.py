@@ -2,7 +2,7 @@
 """Benchmark: one step = forward + backward of fused feature-map linear
 attention over one batch of seeded synthetic input, on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K=50] [--warmup W=200] [--workload NAME]
 
 Default workload: causal, bf16 storage, B=2, H=32, N=16384, D=128, elu+1,
 eps=1e-6 (q, k, v ~ 0.5 N(0,1), grad_out ~ N(0,1), seed 0).  Inputs, outputs
@@ -162,8 +162,10 @@ def cpu_baseline(w, tensors, budget_heads=None, min_seconds=10.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    # about 0.3 s of warm-up: the GPU's clocks ramp up over the first tenths
+    # of a second of load, and a short warm-up times the ramp
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
