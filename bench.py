@@ -2,12 +2,12 @@
 """Benchmark: one step = forward + backward of fused feature-map linear
 attention over one batch of seeded synthetic input, on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K=50] [--warmup W=200] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K=50] [--warmup W] [--workload NAME]
 
 Default workload: causal, bf16 storage, B=2, H=32, N=16384, D=128, elu+1,
 eps=1e-6 (q, k, v ~ 0.5 N(0,1), grad_out ~ N(0,1), seed 0).  Inputs, outputs
-and workspaces are resident in HBM before timing; W untimed steps, then K
-timed steps between device synchronisations.  The forward and the backward of
+and workspaces are resident in HBM before timing; W untimed steps (default:
+as many as fill 0.5 s), then K timed steps between device synchronisations.  The forward and the backward of
 a step share one workspace, so the backward reuses the forward's state records
 (la_bwd_saved, as the autograd form does); the rate with the backward
 recomputing them (la_bwd) is reported beside.  One JSON line on stdout:
@@ -98,7 +98,8 @@ def measured_traffic(workload, kernel):
 
 
 def step_roofline(w, s, causal):
-    """Time of one fwd+bwd step at the roofline: algorithmic bytes at HBM peak
+    """Time of one step (fwd+bwd, or fwd for a forward-only workload) at the
+    roofline: algorithmic bytes at HBM peak
     vs algorithmic flops at the bf16 matrix peak (state updates and reads,
     2*F*D per token each; F = 2D with cos/sin)."""
     br = 2 if w.cos else 1
@@ -107,6 +108,8 @@ def step_roofline(w, s, causal):
     bwd_bytes = s * tokD * (3 * w.H + 4 * w.Hkv)
     fwd_flops = br * 2 * w.D * w.D * w.B * w.N * (w.H + w.Hkv)
     bwd_flops = br * 2 * w.D * w.D * w.B * w.N * (3 * w.H + 3 * w.Hkv)
+    if not w.backward:   # forward-only workload
+        bwd_bytes = bwd_flops = 0
     t_bytes = (fwd_bytes + bwd_bytes) / (HBM_PEAK_GBS * 1e9)
     t_flops = (fwd_flops + bwd_flops) / (BF16_PEAK_TFLOPS * 1e12)
     return max(t_bytes, t_flops), fwd_bytes + bwd_bytes, fwd_flops + bwd_flops
@@ -127,12 +130,12 @@ def cpu_baseline(w, tensors, budget_heads=None, min_seconds=10.0):
     take = min(take, n_groups)
     units = [(b, g) for b in range(w.B) for g in range(w.Hkv)][:take]
     f64 = {n: si.exact_f64(t) for n, t in tensors.items() if t is not None and t.dim() == 4}
-    parts = [oracle.group_slice(f64["q"], f64["k"], f64["v"], f64["grad_out"], b, g)
+    parts = [oracle.group_slice(f64["q"], f64["k"], f64["v"], f64.get("grad_out"), b, g)
              for b, g in units]
     q = np.concatenate([p[0] for p in parts])
     k = np.concatenate([p[1] for p in parts])
     v = np.concatenate([p[2] for p in parts])
-    g = np.concatenate([p[3] for p in parts])
+    g = np.concatenate([p[3] for p in parts]) if w.backward else None
     cw = sw = None
     if tensors.get("cos_weight") is not None:
         cw, sw = si.exact_f64(tensors["cos_weight"]), si.exact_f64(tensors["sin_weight"])
@@ -143,7 +146,8 @@ def cpu_baseline(w, tensors, budget_heads=None, min_seconds=10.0):
     while reps == 0 or (total < min_seconds and reps < 64):
         t0 = time.perf_counter()
         oracle.fwd(q, k, v, **kw)
-        oracle.bwd(q, k, v, g, **kw)
+        if w.backward:
+            oracle.bwd(q, k, v, g, **kw)
         total += time.perf_counter() - t0
         reps += 1
     dt = total / reps
@@ -154,8 +158,8 @@ def cpu_baseline(w, tensors, budget_heads=None, min_seconds=10.0):
         "cores": min(threads, take * nrep),
         "kind": "oracle",
         "sample": "%d of %d (batch, KV head) groups (%d query heads each) at full N=%d, "
-                  "fwd+bwd in fp64, mean of %d runs (%.1f s in all); scaled by group count"
-                  % (take, n_groups, nrep, w.N, reps, total),
+                  "%s in fp64, mean of %d runs (%.1f s in all); scaled by group count"
+                  % (take, n_groups, nrep, w.N, "fwd+bwd" if w.backward else "fwd", reps, total),
     }
 
 
@@ -163,9 +167,10 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # about 0.3 s of warm-up: the GPU's clocks ramp up over the first tenths
-    # of a second of load, and a short warm-up times the ramp
-    ap.add_argument("--warmup", type=int, default=200)
+    # default: as many steps as fill 0.5 s (at least 3): the GPU's clocks ramp
+    # up over the first tenths of a second of load, and a short warm-up would
+    # time the ramp; the count used is reported
+    ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -224,10 +229,19 @@ def main():
         del src, dst
         log("bench: calibration copy of %d MiB done" % args.calibration_copy_mib)
 
-    log("bench: %d warmup steps" % args.warmup)
-    for _ in range(args.warmup):
-        step()
+    if args.warmup is None:
+        n, t_w = 0, time.perf_counter()
+        while n < 3 or time.perf_counter() - t_w < 0.5:
+            step()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
+        args.warmup = n
+    else:
+        for _ in range(args.warmup):
+            step()
     torch.cuda.synchronize()
+    log("bench: %d warmup steps done" % args.warmup)
 
     log("bench: %d timed steps" % args.steps)
     la.timing_enable(True)
@@ -266,16 +280,20 @@ def main():
         log("bench: %d steps with the backward recomputing the forward's state" % args.steps)
         step(saved=False)
         torch.cuda.synchronize()
+        la.timing_enable(True)   # timed like the main region (events on every launch)
         t1 = time.perf_counter()
         for _ in range(args.steps):
             step(saved=False)
         torch.cuda.synchronize()
         el = time.perf_counter() - t1
+        la.timing_enable(False)
+        la.timing_collect()
         recompute = {"ms_per_step": el * 1e3 / args.steps, "value": tokens * args.steps / el,
                      "unit": "tokens/s"}
 
     result = {
-        "metric": "fwd+bwd tokens/sec and % roofline, causal bf16 N=16384 D=128",
+        "metric": ("fwd+bwd tokens/sec and % roofline, causal bf16 N=16384 D=128" if name == si.HEADLINE
+                   else "%s tokens/sec and %% roofline, %s" % ("fwd+bwd" if w.backward else "fwd", name)),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
