@@ -150,6 +150,35 @@ __device__ __forceinline__ float phi_fast(float x) {
 // rounded to bf16 or scale bf16 operands.
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// Cross-lane sums in registers.  A shuffle through the LDS crossbar
+// (ds_bpermute) costs a round trip and a wait per step; these use the
+// permute paths of the vector ALU instead.
+//
+// x + (x of lane ^ 32): the wave's halves swapped by v_permlane32_swap.
+// Both lanes of a pair add the same two values, so they get the same bits.
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    return __int_as_float(p[0]) + __int_as_float(p[1]);
+}
+
+// Sum over each group of G consecutive lanes (G = 8 or 16, groups aligned),
+// with DPP: pairs, quads, then the mirrored halves of each 8- and 16-lane
+// row.  Every lane of a group ends with the same bits (each step adds the
+// same two values in both lanes it pairs).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(G == 8 || G == 16, "DPP rows hold 16 lanes");
+    x = dpp_add<0xB1>(x);    // quad_perm [1,0,3,2]: lane ^ 1
+    x = dpp_add<0x4E>(x);    // quad_perm [2,3,0,1]: lane ^ 2
+    x = dpp_add<0x141>(x);   // row_half_mirror: lane i <-> 7 - i within 8 lanes
+    if constexpr (G == 16) x = dpp_add<0x140>(x);   // row_mirror: i <-> 15 - i
+    return x;
+}
+
 __device__ __forceinline__ float bf2f(u16 x) { return __uint_as_float((uint32_t)x << 16); }
 
 __device__ __forceinline__ u16 f2bf(float x) {
@@ -215,7 +244,7 @@ struct RawTile {
 
     // Features: phi, then with COS [cos_t phi, sin_t phi] (row width 2D),
     // rounded to bf16.  With QZ, also sQZ[r] = Phi(x_r) . z (features before
-    // rounding, fp32; fixed-order shuffle reduction across the V8 threads of
+    // rounding, fp32; fixed-order register reduction across the V8 threads of
     // a row).  Branch-free per element: rows >= N hold zeros (load) and phi
     // of them is finite; only a ragged tile (uniform test) multiplies them
     // by a 0/1 row factor.
@@ -265,8 +294,7 @@ struct RawTile {
                 }
             }
             if constexpr (QZ) {
-#pragma unroll
-                for (int o2 = 1; o2 < V8; o2 <<= 1) qz += __shfl_xor(qz, o2);
+                qz = group_sum<V8>(qz);
                 if (idx % V8 == 0) sQZ[r] = qz;
             }
         }

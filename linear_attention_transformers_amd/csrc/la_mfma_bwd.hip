@@ -54,7 +54,7 @@ constexpr int kCb = 32;   // backward chunk length: one 32x32 tile per head
 // denominators) and T^T and pass them to the state waves through LDS, which
 // meanwhile form U = S g: the state waves' chain is the kernel's critical path.
 // After that exchange (one barrier) the two wave kinds run independently: the
-// R update needs only 1/den, and the waves that own r recompute c.
+// R update needs only 1/den, and the R waves recompute c for r.
 // ---------------------------------------------------------------------------
 template <int D, int PHI, bool CAUSAL>
 __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2)))
@@ -70,6 +70,7 @@ void k_bwd_q_mfma(Args a) {
     __shared__ __attribute__((aligned(16))) float sInv[kCb];
     __shared__ __attribute__((aligned(16))) float sAt[64 * 16], sTt[64 * 16];   // accumulator tiles
     __shared__ float sQZ[kCb], sDen[kCb], sQU[NW][kCb];
+    __shared__ __attribute__((aligned(16))) float sCw[NW][kCb];   // each R wave's c, for its operands
 
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
@@ -104,7 +105,7 @@ void k_bwd_q_mfma(Args a) {
         for (int db = 0; db < NW; ++db) X[db] = zero16();
     }
     for (int e = t; e < F; e += NT) sz[e] = Sp[(size_t)F * D + e];
-    float rr = 0.f;   // thread NT - F + f owns r[f]
+    f32x16 Rr = zero16();   // R waves: r of feature block wr in every column
     const bf16x8 one = ones8();
 
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
@@ -125,11 +126,18 @@ void k_bwd_q_mfma(Args a) {
             rK.load(kh, c0 + kCb, a.N);
             rV.load(vh, c0 + kCb, a.N);
         }
+        // the first head's rows are staged here, in straight-line code (in the
+        // head loop, the wait for them would also wait for the K, V loads
+        // just issued: the loop header merges the later heads' path)
+        rQ.template store_feat<PHI, false, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+        rG.template store<TD>(sG);
         for (int rep = 0; rep < a.nrep; ++rep) {
             const size_t bh = bh0 + rep;
-            if (rep > 0) __syncthreads();
-            rQ.template store_feat<PHI, false, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
-            rG.template store<TD>(sG);
+            if (rep > 0) {
+                __syncthreads();
+                rQ.template store_feat<PHI, false, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+                rG.template store<TD>(sG);
+            }
             __syncthreads();
             {   // Q, G rows of the next head, or of the first head at the next chunk
                 const bool last = rep + 1 == a.nrep;
@@ -160,7 +168,7 @@ void k_bwd_q_mfma(Args a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) qu += x4[e] * U[4 * q4 + e];
                 }
-                qu += __shfl_xor(qu, 32);
+                qu = sum_halves(qu);
                 if (h == 0) sQU[w][l32] = qu;
             } else if (w == NW) {
                 // causal: A^T (keys x queries), causal mask, rounded to bf16
@@ -176,7 +184,7 @@ void k_bwd_q_mfma(Args a) {
                         At[r] = acc_row(r, h) <= l32 ? (float)(__bf16)At[r] : 0.f;
                         dA += At[r];
                     }
-                    dA += __shfl_xor(dA, 32);
+                    dA = sum_halves(dA);
                     put_acc(sAt, At);
                 }
                 if (h == 0) {
@@ -202,7 +210,7 @@ void k_bwd_q_mfma(Args a) {
                     const f32x16 At = get_acc(sAt);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) aT += At[r] * Tt[r];
-                    aT += __shfl_xor(aT, 32);
+                    aT = sum_halves(aT);
                 }
                 float gsum = aT;
 #pragma unroll
@@ -246,11 +254,41 @@ void k_bwd_q_mfma(Args a) {
                 }
             }
             if (!state_wave) {
-                // R (feature block wr x every value block) += (Phi(Q) / den)^T G
+                // c_i for this lane's query, as the state waves form it (same
+                // bits), then through this wave's LDS row into operand order:
+                // lane (n, h) needs c of rows 16s + 8h + 0..7
+                float aT = 0.f;
+                if constexpr (CAUSAL) {
+                    const f32x16 At = get_acc(sAt), Tt = get_acc(sTt);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) aT += At[r] * Tt[r];
+                    aT = sum_halves(aT);
+                }
+                float gsum = aT;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) gsum += sQU[ww][l32];
+                const float iq = sInv[l32];
+                if (h == 0) sCw[wr][l32] = ok ? gsum * iq * iq : 0.f;
+                // R (feature block wr x every value block) += (Phi(Q) / den)^T G,
+                // r (feature block wr) += Phi(Q)^T c: c in two bf16 parts as the
+                // B operand of every column, so each column of Rr holds r
 #pragma unroll
                 for (int s = 0; s < kCb / 16; ++s) {
                     const int k0 = 16 * s + 8 * h;
                     bf16x8 qa = tr8(tr_addr<TF>(sQ, k0, 32 * wr), tr_addr<TF>(sQ, k0 + 4, 32 * wr));
+                    {
+                        const float4 c0v = *reinterpret_cast<const float4 *>(&sCw[wr][k0]);
+                        const float4 c1v = *reinterpret_cast<const float4 *>(&sCw[wr][k0 + 4]);
+                        const float cv[8] = {c0v.x, c0v.y, c0v.z, c0v.w, c1v.x, c1v.y, c1v.z, c1v.w};
+                        bf16x8 chi, clo;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            chi[e] = (__bf16)cv[e];
+                            clo[e] = (__bf16)(cv[e] - (float)chi[e]);
+                        }
+                        Rr = mfma(qa, chi, Rr);
+                        Rr = mfma(qa, clo, Rr);
+                    }
                     const float4 i0 = *reinterpret_cast<const float4 *>(sInv + k0);
                     const float4 i1 = *reinterpret_cast<const float4 *>(sInv + k0 + 4);
                     const float sc[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
@@ -268,29 +306,6 @@ void k_bwd_q_mfma(Args a) {
                         X[db] = mfma(qa, gb, X[db]);
                         if constexpr (!CAUSAL) X[db] = mfma(qlo, gb, X[db]);
                     }
-                }
-                if (w >= (NT - F) / 64) {
-                    // r += Phi(Q)^T c: these waves form c_i themselves, in the
-                    // state waves' order (same bits), rather than wait for them
-                    float aT = 0.f;
-                    if constexpr (CAUSAL) {
-                        const f32x16 At = get_acc(sAt), Tt = get_acc(sTt);
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) aT += At[r] * Tt[r];
-                        aT += __shfl_xor(aT, 32);
-                    }
-                    float gsum = aT;
-#pragma unroll
-                    for (int ww = 0; ww < NW; ++ww) gsum += sQU[ww][l32];
-                    const float inv = sInv[l32];
-                    const float cq = ok ? gsum * inv * inv : 0.f;   // c of query l32
-                    const int tf = t - (NT - F);
-                    float acc = 0.f;
-#pragma unroll
-                    for (int i = 0; i < kCb; ++i)
-                        acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cq), i)) *
-                               bf2f(sQ[TF::at(i, tf)]);
-                    rr += acc;
                 }
             }
         }
@@ -323,8 +338,10 @@ void k_bwd_q_mfma(Args a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 Ro[(size_t)(32 * wr + acc_row(r, h)) * D + 32 * db + l32] = X[db][r];
-        const int tf = t - (NT - F);
-        if (tf >= 0) Ro[(size_t)F * D + tf] = rr;
+        if (l32 == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Ro[(size_t)F * D + 32 * wr + acc_row(r, h)] = Rr[r];
+        }
     }
 }
 

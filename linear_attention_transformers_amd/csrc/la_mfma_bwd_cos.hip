@@ -96,12 +96,20 @@ void k_bwd_q_cos_mfma(Args a) {
         rV.load(vh, c0 + kCc, a.N);
         const int ti = min(c0 + l32, a.N - 1);
         const float mq = w < NW ? a.cw[ti] : a.sw[ti];   // this lane's query weight for block w
+        // the first head's rows are staged here, in straight-line code (in the
+        // head loop, the wait for them would also wait for the K, V loads
+        // just issued: the loop header merges the later heads' path)
+        rQ.template store_feat<PHI, true, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+        rQ.template store<TD>(sQr);
+        rG.template store<TD>(sG);
         for (int rep = 0; rep < a.nrep; ++rep) {
             const size_t bh = bh0 + rep;
-            if (rep > 0) __syncthreads();
-            rQ.template store_feat<PHI, true, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
-            rQ.template store<TD>(sQr);
-            rG.template store<TD>(sG);
+            if (rep > 0) {
+                __syncthreads();
+                rQ.template store_feat<PHI, true, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+                rQ.template store<TD>(sQr);
+                rG.template store<TD>(sG);
+            }
             __syncthreads();
             {   // Q, G rows of the next head, or of the first head at the next chunk
                 const bool last = rep + 1 == a.nrep;
@@ -127,8 +135,8 @@ void k_bwd_q_cos_mfma(Args a) {
                 dA += x;
                 aT += x * Tt[r];
             }
-            dA += __shfl_xor(dA, 32);
-            aT += __shfl_xor(aT, 32);
+            dA = sum_halves(dA);
+            aT = sum_halves(aT);
             const float den = ok ? dA + sQZ[l32] + a.eps : 1.f;
             // U^T = S g (feature block w x the chunk's queries), Phi(q).U over the block
             f32x16 U = zero16();
@@ -145,7 +153,7 @@ void k_bwd_q_cos_mfma(Args a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) qu += x4[e] * U[4 * q4 + e];
             }
-            qu += __shfl_xor(qu, 32);
+            qu = sum_halves(qu);
             if (h == 0) sQU[w][l32] = qu;
             __syncthreads();
 
@@ -413,11 +421,12 @@ void k_bwd_kv_cos_mfma(Args a) {
             }
         }
 
-        for (int rep = 0; rep < a.nrep; ++rep) {
-            __syncthreads();   // the previous head's LDS reads (and of r) are done
+        // one head's query rows into LDS: Phi(Q), gn = g / den (rows past N:
+        // zeros), raw g, c, 1 / den
+        auto stage_head = [&]() {
             rQ.template store_feat<PHI, true, TF, false>(sQ, c0, a.N, a.cw, a.sw, nullptr, nullptr);
 #pragma unroll
-            for (int k = 0; k < NV; ++k) {   // gn = g / den (rows past N: zeros)
+            for (int k = 0; k < NV; ++k) {
                 const int idx = t + k * NT, i = idx / V8, c8 = (idx % V8) * 8;
                 const float inv = c0 + i < a.N ? rcp(pden[k]) : 0.f;
                 const uint4 u = rG.v[k];
@@ -432,6 +441,16 @@ void k_bwd_kv_cos_mfma(Args a) {
                 sIq[t] = c0 + t < a.N ? rcp(pdq) : 0.f;
             }
             rG.template store<TD>(sGr);
+        };
+        // the first head is staged in straight-line code (in the head loop, the
+        // wait for its rows would also wait for the K, V loads just issued)
+        __syncthreads();   // the state terms' LDS reads (and of r) are done
+        stage_head();
+        for (int rep = 0; rep < a.nrep; ++rep) {
+            if (rep > 0) {
+                __syncthreads();   // the previous head's LDS reads are done
+                stage_head();
+            }
             __syncthreads();
             {   // Q, G, den, c of the next head, or of the first head at the next chunk
                 const bool last = rep + 1 == a.nrep;

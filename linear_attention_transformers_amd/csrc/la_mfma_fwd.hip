@@ -192,13 +192,18 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
         // loaded clamped and never used, and no register copies are needed)
         rK.load(kh, c0 + kCf, a.N);
         rV.load(vh, c0 + kCf, a.N);
+        // the first head's rows are staged here, in straight-line code: staged
+        // at the top of the head loop, they would share its header with the
+        // later heads, whose wait for their own rows would also wait for the
+        // K, V loads just issued
+        rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
         for (int rep = 0; rep < a.nrep; ++rep) {
             u16 *oh = obase + (bh0 + rep) * a.N * D;
             if (rep > 0) {
                 __syncthreads();   // every wave is done with the previous head's sQ; sO complete
-                store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
+                rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+                store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);   // after the staging's wait
             }
-            rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
             __syncthreads();
             {   // Q rows of the next head, or of the first head at the next chunk
                 const bool last = rep + 1 == a.nrep;
@@ -314,8 +319,10 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2))) void
     for (int c0 = row0; c0 < row1; c0 += kCf) {
         for (int rep = 0; rep < a.nrep; ++rep) {
             __syncthreads();   // previous head: sQ reads done, sO complete (and sz written)
-            if (pend_oh) store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
+            // staging first: its wait for the Q rows would otherwise also wait
+            // for the output stores issued just before
             rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+            if (pend_oh) store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
             __syncthreads();
             {   // Q rows of the next head, or of the first head at the next chunk
                 const bool last = rep + 1 == a.nrep;
