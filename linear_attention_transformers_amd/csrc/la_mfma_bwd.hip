@@ -386,9 +386,9 @@ void k_bwd_kv_mfma(Args a) {
     for (int db = 0; db < NW; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) Rt[db][r] = Rp[(size_t)(32 * w + l32) * D + 32 * db + acc_row(r, h)];
-    // r lives in the registers of threads t < F (the running suffix); each
-    // chunk publishes a copy to sr for the state term
-    float racc = t < F ? Rp[(size_t)F * D + t] : 0.f;
+    // r (the running suffix): both lanes (n, h) of wave w hold r[32w + n];
+    // each chunk publishes the wave's block to sr for the state term
+    float racc = Rp[(size_t)F * D + 32 * w + l32];
 
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
     const int nch = (row1 - row0 + kCb - 1) / kCb;
@@ -461,7 +461,7 @@ void k_bwd_kv_mfma(Args a) {
                     for (int e = 0; e < 4; ++e) x[e] = Rt[db][4 * q4 + e];
                     st4bf(sR + TD::at(32 * w + l32, 32 * db + 8 * q4 + 4 * h), x);
                 }
-            if (t < F) sr[t] = racc;
+            if (h == 0) sr[32 * w + l32] = racc;
         }
         if constexpr (CAUSAL) stage_head(c0, 0, cn);
         __syncthreads();
@@ -551,11 +551,17 @@ void k_bwd_kv_mfma(Args a) {
                     Rt[db] = mfma(ga, qb, Rt[db]);
                 }
             }
-            if (t < F) {
+            {   // r += Phi(Q)^T c: feature 32w + n, rows 16h .. 16h+15 per lane
                 float acc = 0.f;
-#pragma unroll 8
-                for (int i = 0; i < kCb; ++i) acc += sCc[i] * bf2f(sQ[TF::at(i, t)]);
-                racc += acc;
+#pragma unroll
+                for (int j = 0; j < kCb / 8; ++j) {
+                    const float4 cv = *reinterpret_cast<const float4 *>(sCc + 16 * h + 4 * j);
+                    const float c4[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc += c4[e] * bf2f(sQ[TF::at(16 * h + 4 * j + e, 32 * w + l32)]);
+                }
+                racc += sum_halves(acc);
             }
         }
         // dk = phi'(k) dPhi(k), dv; lane holds key l32 and columns 32w + 8q + 4h + 0..3,

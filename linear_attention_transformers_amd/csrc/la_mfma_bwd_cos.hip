@@ -512,11 +512,18 @@ void k_bwd_kv_cos_mfma(Args a) {
                     Rt[db] = mfma(ga, qb, Rt[db]);
                 }
             }
-            if (t < F) {
+            {   // r += Phi(Q)^T c: feature 32w + n, rows 16h .. 16h+15 per lane
                 float acc = 0.f;
-#pragma unroll 8
-                for (int i = 0; i < kCc; ++i) acc += sCc[i] * bf2f(sQ[TF::at(i, t)]);
-                sr[t] += acc;
+#pragma unroll
+                for (int j = 0; j < kCc / 8; ++j) {
+                    const float4 cv = *reinterpret_cast<const float4 *>(sCc + 16 * h + 4 * j);
+                    const float c4[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc += c4[e] * bf2f(sQ[TF::at(16 * h + 4 * j + e, 32 * w + l32)]);
+                }
+                acc = sum_halves(acc);
+                if (h == 0) sr[32 * w + l32] += acc;
             }
         }
         // chain rule through cos/sin: the sin-half waves hand sin_j dPhi(k) to
