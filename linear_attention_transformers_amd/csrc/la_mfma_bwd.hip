@@ -21,8 +21,8 @@
 // chain rule through phi takes phi' from the staged bf16 features
 // (phi_d_feat), so the raw q and k rows are not kept.
 //
-// LDS tiles use the padded layout: in these kernels the permuted layout's
-// extra address arithmetic costs more than its bank conflicts save.
+// LDS tiles use the permuted padded layout (PadI): transposed 4-row reads
+// are conflict-free in it.
 //
 // Layout of the work: one workgroup per (batch, KV head, segment) serving the
 // n_rep query heads.  Each wave computes the chunk's 32x32 tile of A and T
@@ -60,8 +60,8 @@ template <int D, int PHI, bool CAUSAL>
 __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bwd_q_mfma(Args a) {
     constexpr int F = D, NW = D / 32, NT = 4 * D;
-    using TF = Pad<F>;
-    using TD = Pad<D>;
+    using TF = PadI<F>;
+    using TD = PadI<D>;
     __shared__ __attribute__((aligned(16))) u16 sK[kCb * TF::ld];
     __shared__ __attribute__((aligned(16))) u16 sV[kCb * TD::ld];
     __shared__ __attribute__((aligned(16))) u16 sQ[kCb * TF::ld];
@@ -355,8 +355,8 @@ template <int D, int PHI, bool CAUSAL>
 __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bwd_kv_mfma(Args a) {
     constexpr int F = D, NW = D / 32, NT = 2 * D;
-    using TF = Pad<F>;
-    using TD = Pad<D>;
+    using TF = PadI<F>;
+    using TD = PadI<D>;
     __shared__ __attribute__((aligned(16))) u16 sK[kCb * TF::ld];
     __shared__ __attribute__((aligned(16))) u16 sV[kCb * TD::ld];
     __shared__ __attribute__((aligned(16))) u16 sQ[kCb * TF::ld];

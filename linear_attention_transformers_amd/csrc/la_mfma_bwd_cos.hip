@@ -47,8 +47,8 @@ template <int D, int PHI>
 __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bwd_q_cos_mfma(Args a) {
     constexpr int F = 2 * D, NW = D / 32, FW = F / 32, NT = 64 * FW;
-    using TF = Pad<F>;
-    using TD = Pad<D>;
+    using TF = PadI<F>;
+    using TD = PadI<D>;
     __shared__ __attribute__((aligned(16))) u16 sK[kCc * TF::ld];
     __shared__ __attribute__((aligned(16))) u16 sV[kCc * TD::ld];
     __shared__ __attribute__((aligned(16))) u16 sQ[kCc * TF::ld];
@@ -327,8 +327,8 @@ template <int D, int PHI>
 __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bwd_kv_cos_mfma(Args a) {
     constexpr int F = 2 * D, NW = D / 32, FW = F / 32, NT = 64 * FW;
-    using TF = Pad<F>;
-    using TD = Pad<D>;
+    using TF = PadI<F>;
+    using TD = PadI<D>;
     __shared__ __attribute__((aligned(16))) u16 sK[kCc * TF::ld];
     __shared__ __attribute__((aligned(16))) u16 sKr[kCc * TD::ld];   // raw k (phi'), then dk rows
     __shared__ __attribute__((aligned(16))) u16 sV[kCc * TD::ld];
