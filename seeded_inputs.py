@@ -10,7 +10,8 @@ float32, drawn in the order q [B,H,N,D], k [B,H_kv,N,D], v [B,H_kv,N,D],
 grad_out [B,H,N,D]; q, k and v are multiplied by ``scale`` in float32; bf16
 tensors are the round-to-nearest-even image of those float32 draws.  The
 cos/sin weights are cos(pi*i/(2N)) and sin(pi*i/(2N)), i = 0..N-1, computed
-in float64 and rounded once to float32.
+in float64 and rounded once to float32.  The materialised GQA op draws its own
+k, v, grad_k, grad_v (``gqa_draw``).
 """
 from __future__ import annotations
 
@@ -81,6 +82,24 @@ def draw(B, H, Hkv, N, D, scale=1.0, seed=0, grad=True):
     if grad:
         out["grad_out"] = rng.standard_normal((B, H, N, D), dtype=np.float32)
     return out
+
+
+def gqa_draw(B, H, Hkv, N, D, seed=0):
+    """float32 draws for the materialised GQA expansion and its adjoint: k, v
+    [B,H_kv,N,D] ~ 0.5 N(0,1) and grad_k, grad_v [B,H,N,D] ~ N(0,1), drawn in
+    that order from ``default_rng(seed)``."""
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((B, Hkv, N, D), dtype=np.float32) * np.float32(0.5)
+    v = rng.standard_normal((B, Hkv, N, D), dtype=np.float32) * np.float32(0.5)
+    gk = rng.standard_normal((B, H, N, D), dtype=np.float32)
+    gv = rng.standard_normal((B, H, N, D), dtype=np.float32)
+    return {"k": k, "v": v, "grad_k": gk, "grad_v": gv}
+
+
+# The materialised GQA op, measured on the long GQA workload's head shapes.
+GQA_OPS = {
+    "gqa_expand_reduce_b1h32kv8n65536d128": dict(B=1, H=32, Hkv=8, N=65536, D=128, dtype="bf16"),
+}
 
 
 def cos_sin(N):
