@@ -4,6 +4,9 @@ attention over one batch of seeded synthetic input, on one MI355X.
 
     python bench.py [--gpus 1] [--steps K=50] [--warmup W] [--workload NAME]
 
+NAME is an attention workload of seeded_inputs.WORKLOADS, or the materialised
+GQA op (seeded_inputs.GQA_OPS: expand + reduce per step).
+
 Default workload: causal, bf16 storage, B=2, H=32, N=16384, D=128, elu+1,
 eps=1e-6 (q, k, v ~ 0.5 N(0,1), grad_out ~ N(0,1), seed 0).  Inputs, outputs
 and workspaces are resident in HBM before timing; W untimed steps (default:
@@ -22,6 +25,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -163,6 +168,124 @@ def cpu_baseline(w, tensors, budget_heads=None, min_seconds=10.0):
     }
 
 
+def gqa_cpu_baseline(c, arrays, min_seconds=10.0):
+    """The GQA oracle as it is (float64, NumPy) on one KV slab of k and its
+    n_rep gradient slabs at full N; scaled to the op by slab count (2 B H_kv)."""
+    from oracle import gqa as og
+
+    nrep = c["H"] // c["Hkv"]
+    k = arrays["k"][0:1, 0:1].astype(np.float64)
+    gk = arrays["grad_k"][0:1, 0:nrep].astype(np.float64)
+    reps, total = 0, 0.0
+    while reps == 0 or (total < min_seconds and reps < 64):
+        t0 = time.perf_counter()
+        og.round_to(og.expand(k, nrep), c["dtype"])
+        og.round_to(og.reduce(gk, nrep), c["dtype"])
+        total += time.perf_counter() - t0
+        reps += 1
+    t_full = total / reps * 2 * c["B"] * c["Hkv"]
+    return {"value": c["B"] * c["N"] / t_full, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "one KV slab of k (N=%d, D=%d) expanded to %d heads and its %d gradient "
+                      "slabs summed, fp64 NumPy, mean of %d runs (%.1f s in all); scaled by the "
+                      "op's %d slabs" % (c["N"], c["D"], nrep, nrep, reps, total,
+                                          2 * c["B"] * c["Hkv"])}
+
+
+def bench_gqa(args, name):
+    """One step = la_gqa_expand (k, v) + la_gqa_reduce (grad_k, grad_v) on
+    resident buffers; the same JSON fields as the attention workloads."""
+    import ctypes
+
+    import torch
+
+    import linear_attention_transformers_amd as la
+    import seeded_inputs as si
+
+    c = si.GQA_OPS[name]
+    B, H, Hkv, N, D = c["B"], c["H"], c["Hkv"], c["N"], c["D"]
+    s = 2 if c["dtype"] == "bf16" else 4
+    code = la.LA_BF16 if c["dtype"] == "bf16" else la.LA_F32
+    lib = la.load_library()
+    log("bench: drawing %s inputs" % name)
+    arrays = si.gqa_draw(B, H, Hkv, N, D)
+    t = si.to_torch(arrays, c["dtype"], "cuda")
+    ko = torch.empty((B, H, N, D), dtype=t["k"].dtype, device="cuda")
+    vo = torch.empty_like(ko)
+    gk = torch.empty_like(t["k"])
+    gv = torch.empty_like(t["v"])
+    P = lambda x: ctypes.c_void_p(x.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("bench: calibration copy of %d MiB done" % args.calibration_copy_mib)
+
+    def step():
+        st = lib.la_gqa_expand(P(t["k"]), P(t["v"]), P(ko), P(vo), B, Hkv, H, N, D, code, stream)
+        st = st or lib.la_gqa_reduce(P(t["grad_k"]), P(t["grad_v"]), P(gk), P(gv), B, Hkv, H, N, D,
+                                     code, stream)
+        if st:
+            raise RuntimeError(lib.la_last_error().decode())
+
+    if args.warmup is None:
+        n, t_w = 0, time.perf_counter()
+        while n < 3 or time.perf_counter() - t_w < 0.5:
+            step()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
+        args.warmup = n
+    else:
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+    log("bench: %d warmup steps done; %d timed steps" % (args.warmup, args.steps))
+    la.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    la.timing_enable(False)
+    ktimes = la.timing_collect()
+    kvb, qb = B * Hkv * N * D * s, B * H * N * D * s
+    per_launch = {"k_gqa_expand": 2 * kvb + 2 * qb, "k_gqa_reduce": 2 * qb + 2 * kvb}
+    dom_name, (launches, total_ms) = max(ktimes.items(), key=lambda kv: kv[1][1])
+    avg_s = total_ms / launches / 1e3
+    nbytes = per_launch[dom_name]
+    ms_step = elapsed * 1e3 / args.steps
+    step_bytes = sum(per_launch.values())
+    t_roof = step_bytes / (HBM_PEAK_GBS * 1e9)
+    result = {
+        "metric": "GQA expand+reduce tokens/sec and %% roofline, %s" % name,
+        "value": B * N * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": c["dtype"], "data": "synthetic",
+        "config": {"workload": name, "B": B, "H": H, "H_kv": Hkv, "N": N, "D": D,
+                   "storage": c["dtype"], "pass": "expand (k, v) + reduce (grad_k, grad_v)"},
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": nbytes / avg_s / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": nbytes / avg_s / 1e9 / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(name, dom_name), "avg_launch_ms": avg_s * 1e3,
+                     "algorithmic_bytes_per_launch": nbytes},
+        "step_roofline": {"t_roof_ms": t_roof * 1e3, "frac": t_roof * 1e3 / ms_step,
+                          "algorithmic_bytes": step_bytes, "algorithmic_flops": 0},
+        "kernels_ms_per_step": {k: v[1] / args.steps for k, v in ktimes.items()},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline")
+        result["cpu_baseline"] = gqa_cpu_baseline(c, arrays)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,6 +317,8 @@ def main():
         sys.exit(1)
     la.load_library()
     name = args.workload or si.HEADLINE
+    if name in si.GQA_OPS:
+        return bench_gqa(args, name)
     w = si.WORKLOADS[name]
     dtype = w.dtypes[0]
     causal = "causal" in w.modes

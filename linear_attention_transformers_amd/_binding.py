@@ -19,7 +19,8 @@ import threading
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblinattn.so")
-HEADER = os.path.join(os.path.dirname(_PKG), "include", "linattn.h")
+INCLUDE = os.path.join(os.path.dirname(_PKG), "include")
+HEADER = os.path.join(INCLUDE, "linattn.h")
 
 LA_OK, LA_ERR_INVALID, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
 LA_F32, LA_BF16 = 0, 1
@@ -95,16 +96,25 @@ def load_library(path: str = LIB_PATH):
         lib.la_timing_enable.restype = i
         lib.la_timing_collect.argtypes = [ctypes.POINTER(KernelTime), i]
         lib.la_timing_collect.restype = i
+        gqa_args = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
+        lib.la_gqa_expand.argtypes = gqa_args
+        lib.la_gqa_reduce.argtypes = gqa_args
+        lib.la_gqa_expand.restype = i
+        lib.la_gqa_reduce.restype = i
         if path == LIB_PATH:
             _lib = lib
         return lib
 
 
-def header_functions(header: str = HEADER):
-    """Names of the functions include/linattn.h declares."""
-    text = open(header).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(la_[a-z0-9_]+)\s*\(", text)))
+def header_functions(header: str | None = None):
+    """Names of the functions a header declares (default: every include/*.h)."""
+    paths = [header] if header else sorted(
+        os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
+    names = set()
+    for path in paths:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"\b(la_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def _check(lib, st: int):

@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "linattn.h"
+#include "la_gqa.h"
 #include "la_common.h"
 #include "la_kernels.h"
 #include "la_timing.h"
@@ -306,6 +307,42 @@ int la_timing_collect(la_kernel_time *out, int max_entries) {
     }
     la::g_recs.clear();
     return n;
+}
+
+// Grouped-query head expansion and its adjoint (include/la_gqa.h).
+static la_status gqa_check(const void *a, const void *b, const void *ao, const void *bo, int B,
+                           int H_kv, int H, int N, int D, int dtype) {
+    if (B <= 0 || H_kv <= 0 || H <= 0 || N <= 0 || D <= 0)
+        return fail(LA_ERR_INVALID, "B, H_kv, H, N and D must be positive");
+    if (H % H_kv != 0) return fail(LA_ERR_INVALID, "H must be a multiple of H_kv");
+    if (dtype != LA_F32 && dtype != LA_BF16) return fail(LA_ERR_INVALID, "unknown dtype");
+    if (!a || !ao) return fail(LA_ERR_INVALID, "the k pair of pointers must be non-NULL");
+    if ((b == nullptr) != (bo == nullptr))
+        return fail(LA_ERR_INVALID, "the v pair of pointers must both be given or both be NULL");
+    const uintptr_t es = dtype == LA_BF16 ? 2 : 4;
+    if (!aligned(a, es) || !aligned(ao, es) || (b && (!aligned(b, es) || !aligned(bo, es))))
+        return fail(LA_ERR_INVALID, "pointers must be aligned to the element size");
+    if ((long long)B * H_kv > 65535) return fail(LA_ERR_UNSUPPORTED, "B * H_kv must be at most 65535");
+    return LA_OK;
+}
+
+la_status la_gqa_expand(const void *k, const void *v, void *k_out, void *v_out, int B, int H_kv,
+                        int H, int N, int D, int dtype, void *stream) {
+    const la_status st = gqa_check(k, v, k_out, v_out, B, H_kv, H, N, D, dtype);
+    if (st != LA_OK) return st;
+    const hipError_t e = la::gqa_expand_run(k, v, k_out, v_out, B, H_kv, H, (long long)N * D,
+                                            dtype == LA_BF16, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LA_OK : fail(LA_ERR_HIP, hipGetErrorString(e));
+}
+
+la_status la_gqa_reduce(const void *grad_k, const void *grad_v, void *gk_out, void *gv_out, int B,
+                        int H_kv, int H, int N, int D, int dtype, void *stream) {
+    const la_status st = gqa_check(grad_k, grad_v, gk_out, gv_out, B, H_kv, H, N, D, dtype);
+    if (st != LA_OK) return st;
+    const hipError_t e = la::gqa_reduce_run(grad_k, grad_v, gk_out, gv_out, B, H_kv, H,
+                                            (long long)N * D, dtype == LA_BF16,
+                                            static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LA_OK : fail(LA_ERR_HIP, hipGetErrorString(e));
 }
 
 }  // extern "C"

@@ -32,4 +32,10 @@ bool mfma_bwd_serves(int bf16, int causal, int D, int has_cos);
 hipError_t mfma_bwd_run(const Args &a, int phi, int causal, hipStream_t s);
 hipError_t mfma_bwd_cos_run(const Args &a, int phi, hipStream_t s);
 
+// Materialised GQA head expansion / n_rep sum (la_gqa.hip); v / vo NULL = k only.
+hipError_t gqa_expand_run(const void *k, const void *v, void *ko, void *vo, int B, int Hkv, int H,
+                          long long slab_elems, int bf16, hipStream_t s);
+hipError_t gqa_reduce_run(const void *gk, const void *gv, void *ko, void *vo, int B, int Hkv, int H,
+                          long long slab_elems, int bf16, hipStream_t s);
+
 }  // namespace la

@@ -136,3 +136,45 @@ def test_product_never_imports_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read().lower()
                 assert "oracle" not in text, f
+
+
+# ---------------------------------------------------------------------------
+# la_gqa_expand / la_gqa_reduce (include/la_gqa.h): every rejection happens in
+# validation, before any device work
+# ---------------------------------------------------------------------------
+def _gqa(lib, fn, **over):
+    p = ctypes.c_void_p(1 << 20)
+    kw = dict(a=p, b=p, ao=ctypes.c_void_p(1 << 21), bo=ctypes.c_void_p(1 << 22), B=1, H_kv=2, H=8,
+              N=16, D=64, dtype=la.LA_BF16, stream=None)
+    kw.update(over)
+    f = lib.la_gqa_expand if fn == "expand" else lib.la_gqa_reduce
+    return f(kw["a"], kw["b"], kw["ao"], kw["bo"], kw["B"], kw["H_kv"], kw["H"], kw["N"], kw["D"],
+             kw["dtype"], kw["stream"])
+
+
+@pytest.mark.parametrize("fn", ["expand", "reduce"])
+@pytest.mark.parametrize("over,status", [
+    (dict(B=0), 1), (dict(H_kv=0), 1), (dict(H=0), 1), (dict(N=0), 1), (dict(D=-1), 1),
+    (dict(H=7), 1),                      # not a multiple of H_kv
+    (dict(dtype=5), 1),
+    (dict(a=None), 1), (dict(ao=None), 1),
+    (dict(b=None), 1), (dict(bo=None), 1),   # exactly one of the v pair
+    (dict(a=ctypes.c_void_p((1 << 20) + 1)), 1),                     # bf16 needs 2-byte alignment
+    (dict(dtype=la.LA_F32, bo=ctypes.c_void_p((1 << 22) + 2)), 1),   # f32 needs 4-byte alignment
+    (dict(B=65536, H_kv=1, H=1), 2),     # one grid row per KV slab
+])
+def test_gqa_rejects(lib, fn, over, status):
+    assert _gqa(lib, fn, **over) == status
+    assert lib.la_last_error()
+
+
+def test_gqa_python_rejects_bad_heads():
+    torch = pytest.importorskip("torch")
+    from linear_attention_transformers_amd import gqa
+    k = torch.zeros(1, 2, 4, 8)
+    with pytest.raises(ValueError):
+        gqa.fwd(k, k, 2, 5)
+    # equal head counts: the inputs come back untouched, as on the gqa page
+    a, b = gqa.fwd(k, k, 2, 2)
+    assert a is k and b is k
+    assert not gqa.is_supported(k, k, 2, 4)   # CPU tensors
