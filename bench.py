@@ -4,8 +4,9 @@ attention over one batch of seeded synthetic input, on one MI355X.
 
     python bench.py [--gpus 1] [--steps K=50] [--warmup W] [--workload NAME]
 
-NAME is an attention workload of seeded_inputs.WORKLOADS, or the materialised
-GQA op (seeded_inputs.GQA_OPS: expand + reduce per step).
+NAME is an attention workload of seeded_inputs.WORKLOADS, the materialised
+GQA op (seeded_inputs.GQA_OPS: expand + reduce per step) or the low-rank
+projection (seeded_inputs.LOWRANK_OPS: fwd + bwd per step).
 
 Default workload: causal, bf16 storage, B=2, H=32, N=16384, D=128, elu+1,
 eps=1e-6 (q, k, v ~ 0.5 N(0,1), grad_out ~ N(0,1), seed 0).  Inputs, outputs
@@ -286,6 +287,123 @@ def bench_gqa(args, name):
     print(json.dumps(result), flush=True)
 
 
+def lowrank_cpu_baseline(c, arrays, min_seconds=10.0):
+    """The low-rank oracle as it is (float64 NumPy) on a bounded row sample,
+    fwd + bwd; throughput scaled to all M rows (every product is linear in M)."""
+    from oracle import lowrank as olr
+
+    rows = 1024
+    x, U, V = (arrays[k].astype(np.float64) for k in ("x", "U", "V"))
+    b, g = arrays["bias"].astype(np.float64), arrays["grad_out"].astype(np.float64)
+    xs, gs = x[:rows], g[:rows]
+    reps, total = 0, 0.0
+    while reps == 0 or (total < min_seconds and reps < 64):
+        t0 = time.perf_counter()
+        olr.fwd(xs, U, V, b)
+        olr.bwd(xs, U, V, gs, b)
+        total += time.perf_counter() - t0
+        reps += 1
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": rows / (total / reps), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d rows, fwd+bwd in fp64 NumPy (BLAS threads), mean of %d runs "
+                      "(%.1f s in all); rows scale linearly" % (rows, c["M"], reps, total)}
+
+
+def bench_lowrank(args, name):
+    """One step = la_lowrank_fwd + la_lowrank_bwd on resident buffers."""
+    import ctypes
+
+    import torch
+
+    import linear_attention_transformers_amd as la
+    import seeded_inputs as si
+
+    c = si.LOWRANK_OPS[name]
+    M, n_in, rank, n_out = c["M"], c["n_in"], c["rank"], c["n_out"]
+    lib = la.load_library()
+    log("bench: drawing %s inputs" % name)
+    arrays = si.lowrank_draw(M, n_in, rank, n_out)
+    t = {k: torch.from_numpy(v).to("cuda").to(torch.bfloat16).contiguous() for k, v in arrays.items()}
+    y = torch.empty((M, n_out), dtype=torch.bfloat16, device="cuda")
+    gx, gU, gV, gb = (torch.empty_like(t[k]) for k in ("x", "U", "V", "bias"))
+    wsb = int(lib.la_lowrank_workspace_bytes(la.LA_OP_BWD, M, n_in, rank, n_out, la.LA_BF16))
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    P = lambda x: ctypes.c_void_p(x.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def step():
+        st = lib.la_lowrank_fwd(P(t["x"]), P(t["U"]), P(t["V"]), P(t["bias"]), P(y), M, n_in, rank, n_out,
+                                la.LA_BF16, P(ws), wsb, stream)
+        st = st or lib.la_lowrank_bwd(P(t["x"]), P(t["U"]), P(t["V"]), P(t["grad_out"]), P(gx), P(gU), P(gV),
+                                      P(gb), M, n_in, rank, n_out, la.LA_BF16, P(ws), wsb, stream)
+        if st:
+            raise RuntimeError(lib.la_last_error().decode())
+
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.warmup is None:
+        n, t_w = 0, time.perf_counter()
+        while n < 3 or time.perf_counter() - t_w < 0.5:
+            step()
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()
+        args.warmup = n
+    else:
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+    log("bench: %d warmup steps done; %d timed steps" % (args.warmup, args.steps))
+    la.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    la.timing_enable(False)
+    ktimes = la.timing_collect()
+    mnk = 2.0 * M * rank   # flops of one product per unit of its third size
+    flops = {"k_lowrank_gemm_xVt": mnk * n_in, "k_lowrank_gemm_tUt": mnk * n_out,
+             "k_lowrank_gemm_gU": mnk * n_out, "k_lowrank_gemm_gtV": mnk * n_in,
+             "k_lowrank_gemm_gTt": mnk * n_out, "k_lowrank_gemm_gtTx": mnk * n_in}
+    gemms = {k: v for k, v in ktimes.items() if k in flops}
+    dom_name, (launches, total_ms) = max(gemms.items(), key=lambda kv: kv[1][1])
+    avg_s = total_ms / launches / 1e3
+    ms_step = elapsed * 1e3 / args.steps
+    step_flops = mnk * (n_in + n_out) + mnk * (n_in + 2 * n_out + 2 * n_in)   # fwd 2, bwd 5 products
+    step_bytes = 2 * (2 * M * n_in + 2 * M * n_out + 2 * rank * (n_in + n_out) + 2 * n_out)   # x, y, g, gx, U, V, grads
+    t_roof = max(step_flops / (BF16_PEAK_TFLOPS * 1e12), step_bytes / (HBM_PEAK_GBS * 1e9))
+    ach = flops[dom_name] / avg_s / 1e12
+    result = {
+        "metric": "low-rank projection fwd+bwd tokens/sec and %% roofline, %s" % name,
+        "value": M * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "M": M, "n_in": n_in, "rank": rank, "n_out": n_out, "bias": True,
+                   "storage": "bf16", "pass": "fwd + bwd (bwd recomputes t)"},
+        "roofline": {"bound": "mfma", "kernel": dom_name, "achieved": ach, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
+                     "traffic": measured_traffic(name, dom_name), "avg_launch_ms": avg_s * 1e3,
+                     "algorithmic_flops_per_launch": flops[dom_name]},
+        "step_roofline": {"t_roof_ms": t_roof * 1e3, "frac": t_roof * 1e3 / ms_step,
+                          "algorithmic_bytes": step_bytes, "algorithmic_flops": step_flops},
+        "kernels_ms_per_step": {k: v[1] / args.steps for k, v in ktimes.items()},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline")
+        result["cpu_baseline"] = lowrank_cpu_baseline(c, arrays)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -319,6 +437,8 @@ def main():
     name = args.workload or si.HEADLINE
     if name in si.GQA_OPS:
         return bench_gqa(args, name)
+    if name in si.LOWRANK_OPS:
+        return bench_lowrank(args, name)
     w = si.WORKLOADS[name]
     dtype = w.dtypes[0]
     causal = "causal" in w.modes

@@ -101,6 +101,12 @@ def load_library(path: str = LIB_PATH):
         lib.la_gqa_reduce.argtypes = gqa_args
         lib.la_gqa_expand.restype = i
         lib.la_gqa_reduce.restype = i
+        lib.la_lowrank_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        lib.la_lowrank_workspace_bytes.restype = sz
+        lib.la_lowrank_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, sz, vp]
+        lib.la_lowrank_fwd.restype = i
+        lib.la_lowrank_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, sz, vp]
+        lib.la_lowrank_bwd.restype = i
         if path == LIB_PATH:
             _lib = lib
         return lib

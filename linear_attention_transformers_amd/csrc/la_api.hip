@@ -17,6 +17,7 @@
 
 #include "linattn.h"
 #include "la_gqa.h"
+#include "la_lowrank.h"
 #include "la_common.h"
 #include "la_kernels.h"
 #include "la_timing.h"
@@ -342,6 +343,103 @@ la_status la_gqa_reduce(const void *grad_k, const void *grad_v, void *gk_out, vo
     const hipError_t e = la::gqa_reduce_run(grad_k, grad_v, gk_out, gv_out, B, H_kv, H,
                                             (long long)N * D, dtype == LA_BF16,
                                             static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LA_OK : fail(LA_ERR_HIP, hipGetErrorString(e));
+}
+
+typedef unsigned short u16;   // bf16 storage
+
+// Low-rank projection (include/la_lowrank.h).
+struct LowRankPlan {
+    size_t off_t, off_gt, off_part, off_bpart, bytes;
+};
+
+static LowRankPlan lowrank_plan(int op, int M, int n_in, int rank, int n_out) {
+    const size_t a = 256;
+    LowRankPlan p{};
+    size_t off = 0;
+    p.off_t = off;
+    off = la::align_up(off + (size_t)M * rank * 2, a);
+    if (op == LA_OP_BWD) {
+        p.off_gt = off;
+        off = la::align_up(off + (size_t)M * rank * 2, a);
+        const size_t sU = (size_t)la::lowrank_splits(M, n_out, rank) * n_out * rank;
+        const size_t sV = (size_t)la::lowrank_splits(M, rank, n_in) * rank * n_in;
+        p.off_part = off;
+        off = la::align_up(off + 4 * (sU > sV ? sU : sV), a);
+        p.off_bpart = off;
+        off = la::align_up(off + 4 * (size_t)la::lowrank_bias_blocks(M) * n_out, a);
+    }
+    p.bytes = off;
+    return p;
+}
+
+static la_status lowrank_check(int M, int n_in, int rank, int n_out, int dtype) {
+    if (M < 1) return fail(LA_ERR_INVALID, "M must be positive");
+    for (int d : {n_in, rank, n_out})
+        if (d < 8 || d % 8) return fail(LA_ERR_INVALID, "n_in, rank and n_out must be positive multiples of 8");
+    if (dtype == LA_F32) return fail(LA_ERR_UNSUPPORTED, "the low-rank projection serves bf16 storage only");
+    if (dtype != LA_BF16) return fail(LA_ERR_INVALID, "unknown dtype");
+    return LA_OK;
+}
+
+static la_status lowrank_ws(const void *ws, size_t ws_bytes, size_t need) {
+    if (ws == nullptr) return fail(LA_ERR_INVALID, "workspace pointer is NULL");
+    if (!aligned(ws, 256)) return fail(LA_ERR_INVALID, "workspace must be 256-byte aligned");
+    if (ws_bytes < need) return fail(LA_ERR_INVALID, "workspace too small");
+    return LA_OK;
+}
+
+size_t la_lowrank_workspace_bytes(int op, int M, int n_in, int rank, int n_out, int dtype) {
+    if ((op != LA_OP_FWD && op != LA_OP_BWD) || M < 1 || n_in < 8 || rank < 8 || n_out < 8 ||
+        (n_in | rank | n_out) % 8 || dtype != LA_BF16)
+        return 0;
+    return lowrank_plan(op, M, n_in, rank, n_out).bytes;
+}
+
+la_status la_lowrank_fwd(const void *x, const void *U, const void *V, const void *bias, void *y, int M,
+                         int n_in, int rank, int n_out, int dtype, void *ws, size_t ws_bytes,
+                         void *stream) {
+    la_status st = lowrank_check(M, n_in, rank, n_out, dtype);
+    if (st != LA_OK) return st;
+    if (!x || !U || !V || !y) return fail(LA_ERR_INVALID, "x, U, V and y must be non-NULL");
+    for (const void *p : {x, U, V, bias, (const void *)y})
+        if (p && !aligned(p, 16)) return fail(LA_ERR_INVALID, "tensors must be 16-byte aligned");
+    const LowRankPlan p = lowrank_plan(LA_OP_FWD, M, n_in, rank, n_out);
+    if ((st = lowrank_ws(ws, ws_bytes, p.bytes)) != LA_OK) return st;
+    la::LowRankArgs a{};
+    char *w = static_cast<char *>(ws);
+    a.x = static_cast<const u16 *>(x); a.U = static_cast<const u16 *>(U); a.V = static_cast<const u16 *>(V);
+    a.bias = static_cast<const u16 *>(bias); a.y = static_cast<u16 *>(y);
+    a.t = reinterpret_cast<u16 *>(w + p.off_t);
+    a.M = M; a.n_in = n_in; a.rank = rank; a.n_out = n_out;
+    const hipError_t e = la::lowrank_fwd_run(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LA_OK : fail(LA_ERR_HIP, hipGetErrorString(e));
+}
+
+la_status la_lowrank_bwd(const void *x, const void *U, const void *V, const void *grad_out,
+                         void *grad_x, void *grad_U, void *grad_V, void *grad_bias, int M, int n_in,
+                         int rank, int n_out, int dtype, void *ws, size_t ws_bytes, void *stream) {
+    la_status st = lowrank_check(M, n_in, rank, n_out, dtype);
+    if (st != LA_OK) return st;
+    if (!x || !U || !V || !grad_out || !grad_x || !grad_U || !grad_V)
+        return fail(LA_ERR_INVALID, "x, U, V, grad_out, grad_x, grad_U and grad_V must be non-NULL");
+    for (const void *p : {x, U, V, grad_out, (const void *)grad_x, (const void *)grad_U,
+                          (const void *)grad_V, (const void *)grad_bias})
+        if (p && !aligned(p, 16)) return fail(LA_ERR_INVALID, "tensors must be 16-byte aligned");
+    const LowRankPlan p = lowrank_plan(LA_OP_BWD, M, n_in, rank, n_out);
+    if ((st = lowrank_ws(ws, ws_bytes, p.bytes)) != LA_OK) return st;
+    la::LowRankArgs a{};
+    char *w = static_cast<char *>(ws);
+    a.x = static_cast<const u16 *>(x); a.U = static_cast<const u16 *>(U); a.V = static_cast<const u16 *>(V);
+    a.g = static_cast<const u16 *>(grad_out);
+    a.gx = static_cast<u16 *>(grad_x); a.gU = static_cast<u16 *>(grad_U); a.gV = static_cast<u16 *>(grad_V);
+    a.gbias = static_cast<u16 *>(grad_bias);
+    a.t = reinterpret_cast<u16 *>(w + p.off_t);
+    a.gt = reinterpret_cast<u16 *>(w + p.off_gt);
+    a.part = reinterpret_cast<float *>(w + p.off_part);
+    a.bpart = reinterpret_cast<float *>(w + p.off_bpart);
+    a.M = M; a.n_in = n_in; a.rank = rank; a.n_out = n_out;
+    const hipError_t e = la::lowrank_bwd_run(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LA_OK : fail(LA_ERR_HIP, hipGetErrorString(e));
 }
 

@@ -32,6 +32,19 @@ bool mfma_bwd_serves(int bf16, int causal, int D, int has_cos);
 hipError_t mfma_bwd_run(const Args &a, int phi, int causal, hipStream_t s);
 hipError_t mfma_bwd_cos_run(const Args &a, int phi, hipStream_t s);
 
+// Low-rank projection (la_lowrank.hip): bf16 tensors, fp32 scratch in the workspace.
+struct LowRankArgs {
+    const unsigned short *x, *U, *V, *bias, *g;   // bf16 inputs (bias, g optional per pass)
+    unsigned short *y, *gx, *gU, *gV, *gbias;     // bf16 outputs (gbias optional)
+    unsigned short *t, *gt;                        // bf16 [M][rank] intermediates
+    float *part, *bpart;                // split partials, bias partials
+    int M, n_in, rank, n_out;
+};
+int lowrank_splits(int M, int rows, int cols);   // K splits of a token-axis product
+int lowrank_bias_blocks(int M);                  // row blocks of the bias sum
+hipError_t lowrank_fwd_run(const LowRankArgs &a, hipStream_t s);
+hipError_t lowrank_bwd_run(const LowRankArgs &a, hipStream_t s);
+
 // Materialised GQA head expansion / n_rep sum (la_gqa.hip); v / vo NULL = k only.
 hipError_t gqa_expand_run(const void *k, const void *v, void *ko, void *vo, int B, int Hkv, int H,
                           long long slab_elems, int bf16, hipStream_t s);

@@ -11,7 +11,8 @@ grad_out [B,H,N,D]; q, k and v are multiplied by ``scale`` in float32; bf16
 tensors are the round-to-nearest-even image of those float32 draws.  The
 cos/sin weights are cos(pi*i/(2N)) and sin(pi*i/(2N)), i = 0..N-1, computed
 in float64 and rounded once to float32.  The materialised GQA op draws its own
-k, v, grad_k, grad_v (``gqa_draw``).
+k, v, grad_k, grad_v (``gqa_draw``), the low-rank projection its x, U, V,
+bias, grad_out (``lowrank_draw``).
 """
 from __future__ import annotations
 
@@ -99,6 +100,28 @@ def gqa_draw(B, H, Hkv, N, D, seed=0):
 # The materialised GQA op, measured on the long GQA workload's head shapes.
 GQA_OPS = {
     "gqa_expand_reduce_b1h32kv8n65536d128": dict(B=1, H=32, Hkv=8, N=65536, D=128, dtype="bf16"),
+}
+
+
+def lowrank_draw(M, n_in, rank, n_out, seed=0, lead=None):
+    """float32 draws for the low-rank projection, in this order from
+    ``default_rng(seed)``: x [*lead or M, n_in] ~ N(0,1), V [rank, n_in] ~
+    N(0, 1/n_in), U [n_out, rank] ~ N(0, 1/rank), bias [n_out] ~ N(0,1)/10,
+    grad_out [*lead or M, n_out] ~ N(0,1) (factor scales keep y of order 1)."""
+    rng = np.random.default_rng(seed)
+    shape = tuple(lead) if lead else (M,)
+    x = rng.standard_normal((*shape, n_in), dtype=np.float32)
+    V = rng.standard_normal((rank, n_in), dtype=np.float32) * np.float32(1.0 / math.sqrt(n_in))
+    U = rng.standard_normal((n_out, rank), dtype=np.float32) * np.float32(1.0 / math.sqrt(rank))
+    bias = rng.standard_normal(n_out, dtype=np.float32) * np.float32(0.1)
+    g = rng.standard_normal((*shape, n_out), dtype=np.float32)
+    return {"x": x, "V": V, "U": U, "bias": bias, "grad_out": g}
+
+
+# The low-rank projection, measured at the headline workload's token count
+# (B*N = 2*16384) and width (H*D = 32*128) with a quarter rank.
+LOWRANK_OPS = {
+    "lowrank_m32768_in4096_r1024_out4096": dict(M=32768, n_in=4096, rank=1024, n_out=4096),
 }
 
 

@@ -178,3 +178,50 @@ def test_gqa_python_rejects_bad_heads():
     a, b = gqa.fwd(k, k, 2, 2)
     assert a is k and b is k
     assert not gqa.is_supported(k, k, 2, 4)   # CPU tensors
+
+
+# ---------------------------------------------------------------------------
+# la_lowrank_* (include/la_lowrank.h): validation before any device work
+# ---------------------------------------------------------------------------
+def test_lowrank_workspace_bytes(lib):
+    f = lib.la_lowrank_workspace_bytes
+    assert f(la.LA_OP_FWD, 37, 64, 16, 32, la.LA_BF16) >= 37 * 16 * 2
+    assert f(la.LA_OP_BWD, 37, 64, 16, 32, la.LA_BF16) > f(la.LA_OP_FWD, 37, 64, 16, 32, la.LA_BF16)
+    for bad in [(la.LA_OP_FWD, 0, 64, 16, 32, la.LA_BF16), (la.LA_OP_FWD, 8, 60, 16, 32, la.LA_BF16),
+                (la.LA_OP_FWD, 8, 64, 4, 32, la.LA_BF16), (la.LA_OP_FWD, 8, 64, 16, 32, la.LA_F32),
+                (7, 8, 64, 16, 32, la.LA_BF16)]:
+        assert f(*bad) == 0
+
+
+def _lr(lib, fn, **over):
+    p = ctypes.c_void_p(1 << 20)
+    kw = dict(x=p, U=p, V=p, b=None, y=ctypes.c_void_p(1 << 21), g=p, gx=ctypes.c_void_p(1 << 22),
+              gU=ctypes.c_void_p(1 << 23), gV=ctypes.c_void_p(1 << 24), gb=None, M=37, n_in=64, rank=16,
+              n_out=32, dtype=la.LA_BF16, ws=ctypes.c_void_p(1 << 25), ws_bytes=1 << 40, stream=None)
+    kw.update(over)
+    if fn == "fwd":
+        return lib.la_lowrank_fwd(kw["x"], kw["U"], kw["V"], kw["b"], kw["y"], kw["M"], kw["n_in"], kw["rank"],
+                                  kw["n_out"], kw["dtype"], kw["ws"], kw["ws_bytes"], kw["stream"])
+    return lib.la_lowrank_bwd(kw["x"], kw["U"], kw["V"], kw["g"], kw["gx"], kw["gU"], kw["gV"], kw["gb"],
+                              kw["M"], kw["n_in"], kw["rank"], kw["n_out"], kw["dtype"], kw["ws"],
+                              kw["ws_bytes"], kw["stream"])
+
+
+@pytest.mark.parametrize("fn", ["fwd", "bwd"])
+@pytest.mark.parametrize("over,status", [
+    (dict(M=0), 1), (dict(n_in=60), 1), (dict(rank=0), 1), (dict(n_out=12), 1),
+    (dict(dtype=la.LA_F32), 2), (dict(dtype=9), 1),
+    (dict(x=None), 1), (dict(U=None), 1), (dict(V=None), 1),
+    (dict(x=ctypes.c_void_p((1 << 20) + 8)), 1),        # not 16-byte aligned
+    (dict(ws=None), 1), (dict(ws=ctypes.c_void_p((1 << 25) + 16)), 1), (dict(ws_bytes=16), 1),
+])
+def test_lowrank_rejects(lib, fn, over, status):
+    assert _lr(lib, fn, **over) == status
+    assert lib.la_last_error()
+
+
+def test_lowrank_rejects_missing_outputs(lib):
+    assert _lr(lib, "fwd", y=None) == 1
+    for k in ("g", "gx", "gU", "gV"):
+        assert _lr(lib, "bwd", **{k: None}) == 1
+    assert _lr(lib, "bwd", gb=ctypes.c_void_p((1 << 26) + 2)) == 1   # misaligned optional output
