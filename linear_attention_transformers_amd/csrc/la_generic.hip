@@ -134,20 +134,21 @@ __global__ __launch_bounds__(kNT) void k_state(Args a) {
 // ---------------------------------------------------------------------------
 // k_scan_S: per (batch, KV head) and state element, replace the per-segment
 // sums by their exclusive prefix over segments (slot s = rows before segment
-// s) and store the total in slot nseg.  Fixed order: deterministic.
+// s) and, with `total`, store the total in slot nseg (without it the last
+// segment's record is neither read nor needed).  Fixed order: deterministic.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kNT) void k_scan_S(float *ws, int nseg, size_t SD, size_t n_units) {
+__global__ __launch_bounds__(kNT) void k_scan_S(float *ws, int nseg, size_t SD, size_t n_units, int total) {
     const size_t e = (size_t)blockIdx.x * kNT + threadIdx.x;
     const size_t unit = blockIdx.y;
     if (e >= SD || unit >= n_units) return;
     float *base = ws + unit * (nseg + 1) * SD + e;
     float run = 0.f;
     for (int s = 0; s < nseg; ++s) {
-        const float x = base[(size_t)s * SD];
+        const float x = (total || s + 1 < nseg) ? base[(size_t)s * SD] : 0.f;
         base[(size_t)s * SD] = run;
         run += x;
     }
-    base[(size_t)nseg * SD] = run;
+    if (total) base[(size_t)nseg * SD] = run;
 }
 
 // ---------------------------------------------------------------------------
@@ -711,7 +712,7 @@ hipError_t run_fwd(const Args &a, int causal, hipStream_t s) {
     {
         TimedLaunch tl("k_scan_S", s);
         hipLaunchKernelGGL(k_scan_S, scan_grid, dim3(kNT), 0, s, a.ws_S, a.nseg, SD,
-                           (size_t)n_units);
+                           (size_t)n_units, 1);
     }
     if (causal) {
         TimedLaunch tl("k_fwd_causal", s);
@@ -738,7 +739,7 @@ hipError_t run_bwd(const Args &a, int causal, hipStream_t s) {
         }
         TimedLaunch tl("k_scan_S", s);
         hipLaunchKernelGGL(k_scan_S, scan_grid, dim3(kNT), 0, s, a.ws_S, a.nseg, SD,
-                           (size_t)n_units);
+                           (size_t)n_units, 1);
     }
     if (causal) {
         TimedLaunch tl("k_bwd_q_causal", s);
@@ -790,9 +791,9 @@ hipError_t by_shape(const Args &a, int bwd, int causal, int phi, hipStream_t s) 
 
 }  // namespace
 
-hipError_t scan_state(float *ws, int nseg, size_t SD, unsigned n_units, hipStream_t s) {
+hipError_t scan_state(float *ws, int nseg, size_t SD, unsigned n_units, bool total, hipStream_t s) {
     hipLaunchKernelGGL(k_scan_S, dim3((unsigned)((SD + kNT - 1) / kNT), n_units), dim3(kNT), 0, s,
-                       ws, nseg, SD, (size_t)n_units);
+                       ws, nseg, SD, (size_t)n_units, total ? 1 : 0);
     return hipGetLastError();
 }
 

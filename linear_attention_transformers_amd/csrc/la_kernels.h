@@ -12,7 +12,9 @@ hipError_t generic_run(const Args &a, int bf16, int bwd, int causal, int phi, hi
 
 // In-place exclusive prefix over segments of per-segment state records
 // ([n_units][nseg + 1][SD] floats; slot nseg receives the total).
-hipError_t scan_state(float *ws, int nseg, size_t SD, unsigned n_units, hipStream_t s);
+// total: also use the last segment's record and write the total slot (else
+// the last record is not read: the exclusive prefixes do not include it).
+hipError_t scan_state(float *ws, int nseg, size_t SD, unsigned n_units, bool total, hipStream_t s);
 
 // Exclusive suffix over segments of per-segment (R, r) records
 // ([H units][nseg][SD], n_rep consecutive units summed per output unit) into
@@ -25,7 +27,7 @@ hipError_t scan_suffix(const float *Rp, float *Rs, int nseg, size_t SD, int H, i
 bool mfma_fwd_serves(int bf16, int D);
 hipError_t mfma_fwd_run(const Args &a, int phi, int causal, hipStream_t s);
 // per-segment state sums + exclusive prefix and total (the first two steps of both passes)
-hipError_t mfma_state_run(const Args &a, int phi, hipStream_t s);
+hipError_t mfma_state_run(const Args &a, int phi, int causal, hipStream_t s);
 // backward: causal and bidirectional with F = D; causal with the cos/sin
 // features (F = 2D, la_mfma_bwd_cos.hip)
 bool mfma_bwd_serves(int bf16, int causal, int D, int has_cos);

@@ -560,7 +560,7 @@ hipError_t run(const Args &a, hipStream_t s) {
     constexpr int F = 2 * D;
     const unsigned n_units = (unsigned)(a.B * a.Hkv);
     const size_t SD = (size_t)F * D + F;
-    hipError_t e = a.state_ready ? hipSuccess : mfma_state_run(a, PHI, s);
+    hipError_t e = a.state_ready ? hipSuccess : mfma_state_run(a, PHI, 1, s);
     if (e != hipSuccess) return e;
     {
         TimedLaunch tl("k_bwd_q_cos_mfma", s);

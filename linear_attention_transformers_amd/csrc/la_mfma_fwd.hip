@@ -76,13 +76,13 @@ template <int D, int F>
 constexpr int state_waves() { return F == 64 ? 4 : F == 128 ? (D == 128 ? 3 : 2) : 1; }
 
 template <int D, int F, int PHI, bool COS>
-__global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(state_waves<D, F>()))) void k_state_mfma(Args a) {
+__global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(state_waves<D, F>()))) void k_state_mfma(Args a, int nseg_run) {
     using TF = typename FwdTiles<D, F>::TF;
     using TD = typename FwdTiles<D, F>::TD;
     constexpr int NT = D * 2, NW = D / 32, FB = F / 32, ZB = FB / NW;
     __shared__ __attribute__((aligned(16))) u16 sK[kC * TF::ld];
     __shared__ __attribute__((aligned(16))) u16 sV[kC * TD::ld];
-    const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
+    const int seg = blockIdx.x % nseg_run, bg = blockIdx.x / nseg_run;   // segments 0 .. nseg_run-1
     const int t = threadIdx.x, l = t & 63, h = l >> 5, l32 = l & 31;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index, uniform
     const u16 *kh = static_cast<const u16 *>(a.k) + (size_t)bg * a.N * D;
@@ -343,22 +343,27 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2))) void
     if (pend_oh) store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
 }
 
+// Per-segment state sums and their exclusive prefix.  Causal passes read only
+// exclusive prefixes, which never include the last segment: its sum is not
+// computed (and the scan writes no total).
 template <int D, int F, int PHI, bool COS>
-hipError_t run_state(const Args &a, hipStream_t s) {
+hipError_t run_state(const Args &a, bool causal, hipStream_t s) {
     constexpr int NT = D * 2;
     const unsigned n_units = (unsigned)(a.B * a.Hkv);
-    {
+    const int nseg_run = causal ? a.nseg - 1 : a.nseg;
+    if (nseg_run > 0) {
         TimedLaunch tl("k_state_mfma", s);
-        hipLaunchKernelGGL((k_state_mfma<D, F, PHI, COS>), dim3(n_units * a.nseg), dim3(NT), 0, s, a);
+        hipLaunchKernelGGL((k_state_mfma<D, F, PHI, COS>), dim3(n_units * nseg_run), dim3(NT), 0, s, a,
+                           nseg_run);
     }
     TimedLaunch tl("k_scan_S", s);
-    return scan_state(a.ws_S, a.nseg, (size_t)F * D + F, n_units, s);
+    return scan_state(a.ws_S, a.nseg, (size_t)F * D + F, n_units, !causal, s);
 }
 
 template <int D, int F, int PHI, bool COS>
 hipError_t run(const Args &a, bool causal, hipStream_t s) {
     constexpr int NT = D * 2;
-    hipError_t e = run_state<D, F, PHI, COS>(a, s);
+    hipError_t e = run_state<D, F, PHI, COS>(a, causal, s);
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)(a.B * a.Hkv * a.nseg));
     if (causal) {
@@ -376,11 +381,12 @@ hipError_t by_phi(const Args &a, int phi, bool state_only, bool causal, hipStrea
     constexpr int F = COS ? 2 * D : D;
     switch (phi) {
         case kElu1:
-            return state_only ? run_state<D, F, kElu1, COS>(a, s) : run<D, F, kElu1, COS>(a, causal, s);
+            return state_only ? run_state<D, F, kElu1, COS>(a, causal, s) : run<D, F, kElu1, COS>(a, causal, s);
         case kRelu:
-            return state_only ? run_state<D, F, kRelu, COS>(a, s) : run<D, F, kRelu, COS>(a, causal, s);
+            return state_only ? run_state<D, F, kRelu, COS>(a, causal, s) : run<D, F, kRelu, COS>(a, causal, s);
         default:
-            return state_only ? run_state<D, F, kIdentity, COS>(a, s) : run<D, F, kIdentity, COS>(a, causal, s);
+            return state_only ? run_state<D, F, kIdentity, COS>(a, causal, s)
+                              : run<D, F, kIdentity, COS>(a, causal, s);
     }
 }
 
@@ -401,6 +407,8 @@ hipError_t mfma_fwd_run(const Args &a, int phi, int causal, hipStream_t s) {
     return dispatch(a, phi, false, causal != 0, s);
 }
 
-hipError_t mfma_state_run(const Args &a, int phi, hipStream_t s) { return dispatch(a, phi, true, true, s); }
+hipError_t mfma_state_run(const Args &a, int phi, int causal, hipStream_t s) {
+    return dispatch(a, phi, true, causal != 0, s);
+}
 
 }  // namespace la

@@ -211,7 +211,7 @@ def test_kernel_family_per_case():
     and backward; the cos/sin backward when causal); float32 on the vector-ALU
     kernels (checked through the library's launch timing)."""
     torch, la = gpu_or_skip()
-    t = make(1, 4, 2, 256, 128, "bf16", scale=0.5, seed=1)
+    t = make(1, 4, 2, 600, 128, "bf16", scale=0.5, seed=1)   # three 256-row segments
     la.timing_enable(True)
     try:
         run_gpu(la, t, True, "elu+1", backward=False)
@@ -219,6 +219,15 @@ def test_kernel_family_per_case():
     finally:
         la.timing_enable(False)
     assert "k_fwd_mfma" in names and "k_state_mfma" in names, names
+    # one segment: a causal pass needs no segment sums (its prefix is zero)
+    t = make(1, 4, 2, 256, 128, "bf16", scale=0.5, seed=1)
+    la.timing_enable(True)
+    try:
+        run_gpu(la, t, True, "elu+1", backward=False)
+        names = set(la.timing_collect())
+    finally:
+        la.timing_enable(False)
+    assert "k_fwd_mfma" in names and "k_state_mfma" not in names, names
     t = make(1, 4, 2, 256, 128, "f32", seed=1)
     la.timing_enable(True)
     try:
