@@ -58,7 +58,7 @@ constexpr int kCb = 32;   // backward chunk length: one 32x32 tile per head
 // ---------------------------------------------------------------------------
 template <int D, int PHI, bool CAUSAL>
 __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2)))
-void k_bwd_q_mfma(Args a) {
+void k_bwd_q_mfma(Args a, int qm) {
     constexpr int F = D, NW = D / 32, NT = 4 * D;
     using TF = PadI<F>;
     using TD = PadI<D>;
@@ -72,7 +72,11 @@ void k_bwd_q_mfma(Args a) {
     __shared__ float sQZ[kCb], sDen[kCb], sQU[NW][kCb];
     __shared__ __attribute__((aligned(16))) float sCw[NW][kCb];   // each R wave's c, for its operands
 
-    const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
+    // this workgroup walks the qm consecutive segments seg0 .. seg0 + qm - 1
+    // (its state carry runs through their boundaries) and writes each one's
+    // (R, r) record
+    const int nq = (a.nseg + qm - 1) / qm;
+    const int seg0 = (blockIdx.x % nq) * qm, bg = blockIdx.x / nq;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     // w is left per-lane: declared uniform, the wave-role branches keep both
     // roles' registers live and the kernel spills
@@ -90,7 +94,7 @@ void k_bwd_q_mfma(Args a) {
     // state waves: S^T tiles (value block db x feature block w), z tile (block w),
     // the segment's exclusive prefix (causal) or the sequence total
     // R waves: R tiles (feature block wr x value block db)
-    const float *Sp = a.ws_S + ((size_t)bg * (a.nseg + 1) + (CAUSAL ? seg : a.nseg)) * SD;
+    const float *Sp = a.ws_S + ((size_t)bg * (a.nseg + 1) + (CAUSAL ? seg0 : a.nseg)) * SD;
     f32x16 X[NW], Z = zero16();
     if (state_wave) {
 #pragma unroll
@@ -108,7 +112,7 @@ void k_bwd_q_mfma(Args a) {
     f32x16 Rr = zero16();   // R waves: r of feature block wr in every column
     const bf16x8 one = ones8();
 
-    const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
+    const int row0 = seg0 * a.L, row1 = min(row0 + qm * a.L, a.N);
     RawTile<D, NT, kCb> rK, rV, rQ, rG;
     if constexpr (CAUSAL) {
         rK.load(kh, row0, a.N);
@@ -329,20 +333,54 @@ void k_bwd_q_mfma(Args a) {
                 for (int r = 0; r < 16; ++r) sz[32 * w + acc_row(r, h)] = Z[r];
             }
         }
-    }
-    if (!state_wave) {
-        // this segment's (R, r), summed over the group's query heads
-        float *Ro = a.ws_Rp + ((size_t)bg * a.nseg + seg) * SD;
+        if (!state_wave && (c0 + kCb >= row1 || (c0 + kCb - row0) % a.L == 0)) {
+            // the segment ends with this chunk: its (R, r), summed over the
+            // group's query heads, and a fresh sum for the next segment
+            // (segment lengths are multiples of the chunk length)
+            const int seg = seg0 + (c0 - row0) / a.L;
+            float *Ro = a.ws_Rp + ((size_t)bg * a.nseg + seg) * SD;
 #pragma unroll
-        for (int db = 0; db < NW; ++db)
+            for (int db = 0; db < NW; ++db) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                Ro[(size_t)(32 * wr + acc_row(r, h)) * D + 32 * db + l32] = X[db][r];
-        if (l32 == 0) {
+                for (int r = 0; r < 16; ++r)
+                    Ro[(size_t)(32 * wr + acc_row(r, h)) * D + 32 * db + l32] = X[db][r];
+                X[db] = zero16();
+            }
+            if (l32 == 0) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) Ro[(size_t)F * D + 32 * wr + acc_row(r, h)] = Rr[r];
+                for (int r = 0; r < 16; ++r) Ro[(size_t)F * D + 32 * wr + acc_row(r, h)] = Rr[r];
+            }
+            Rr = zero16();
         }
     }
+}
+
+// Segments per dq workgroup.  The dq kernel keeps one workgroup per compute
+// unit (D = 128) and each workgroup starts by loading a state record and ends
+// by writing one, so a second round of short workgroups costs more than
+// fewer, longer ones: take the qm that minimises rounds x segments per
+// workgroup, the larger one on ties.
+template <int D, int PHI, bool CAUSAL>
+int q_segments_per_wg(const Args &a, unsigned n_units) {
+    static int slots = 0;   // resident workgroups on the device
+    if (slots == 0) {
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_bwd_q_mfma<D, PHI, CAUSAL>,
+                                                         4 * D, 0) != hipSuccess ||
+            cus <= 0 || per_cu <= 0)
+            return 1;
+        slots = cus * per_cu;
+    }
+    int best = 1;
+    long long best_t = -1;
+    for (int m = 1; m <= a.nseg; ++m) {
+        const long long wgs = (long long)n_units * ((a.nseg + m - 1) / m);
+        const long long t = (wgs + slots - 1) / slots * m;
+        if (best_t < 0 || t <= best_t) best = m, best_t = t;
+    }
+    return best;
 }
 
 // ---------------------------------------------------------------------------
@@ -593,8 +631,10 @@ hipError_t run(const Args &a, hipStream_t s) {
     hipError_t e = a.state_ready ? hipSuccess : mfma_state_run(a, PHI, CAUSAL, s);
     if (e != hipSuccess) return e;
     {
+        const int qm = q_segments_per_wg<D, PHI, CAUSAL>(a, n_units);
+        const unsigned nq = (unsigned)((a.nseg + qm - 1) / qm);
         TimedLaunch tl(CAUSAL ? "k_bwd_q_mfma" : "k_bwd_q_bidir_mfma", s);
-        hipLaunchKernelGGL((k_bwd_q_mfma<D, PHI, CAUSAL>), dim3(n_units * a.nseg), dim3(4 * D), 0, s, a);
+        hipLaunchKernelGGL((k_bwd_q_mfma<D, PHI, CAUSAL>), dim3(n_units * nq), dim3(4 * D), 0, s, a, qm);
     }
     {
         TimedLaunch tl("k_scan_R", s);

@@ -75,6 +75,25 @@ def test_edge_lengths(N, causal):
         compare(t, out, grads, ref[0], ref[1], dtype, 2, 1, label="N=%d" % N)
 
 
+SPAN = [(128, True, 4, 4), (128, False, 8, 4), (64, True, 8, 4)]
+
+
+@pytest.mark.parametrize("D,causal,H,Hkv", SPAN,
+                         ids=["D%d-%s-h%dkv%d" % (D, "causal" if c else "bidir", H, Hkv)
+                              for D, c, H, Hkv in SPAN])
+def test_dq_workgroup_spans_segments(D, causal, H, Hkv):
+    """Many short segments (seg_len 64) over a long ragged sequence: the dq
+    kernel then walks several consecutive segments per workgroup (its state
+    carry crosses their boundaries) and writes one (R, r) record per segment."""
+    torch, la = gpu_or_skip()
+    B, N = 1, 16300
+    t = make(B, H, Hkv, N, D, "bf16", scale=0.5, cos=False, seed=D + H + N)
+    say("span D=%d causal=%s H=%d Hkv=%d N=%d seg_len=64" % (D, causal, H, Hkv, N))
+    ref = oracle_on(t, causal, "elu+1", 1e-6)
+    out, grads = run_gpu(la, t, causal, "elu+1", 1e-6, seg_len=64)
+    compare(t, out, grads, ref[0], ref[1], "bf16", H, Hkv, label="span")
+
+
 def test_tiny_fp32_workload():
     """B=1, H=2, N=256, D=32, float32, elu+1, eps=1e-6, both modes, fwd+bwd."""
     torch, la = gpu_or_skip()
