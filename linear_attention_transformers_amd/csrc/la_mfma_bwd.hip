@@ -355,14 +355,15 @@ void k_bwd_q_mfma(Args a, int qm) {
     }
 }
 
-// Segments per dq workgroup.  The dq kernel keeps one workgroup per compute
-// unit (D = 128) and each workgroup starts by loading a state record and ends
-// by writing one, so a second round of short workgroups costs more than
-// fewer, longer ones: take the qm that minimises rounds x segments per
-// workgroup, the larger one on ties.
+// Segments per dq workgroup.  Where the dq kernel fits one workgroup per
+// compute unit (D = 128), a second round of short workgroups costs more than
+// fewer, longer ones (each starts by loading a state record and ends by
+// writing one): take the qm that minimises rounds x segments per workgroup,
+// the larger one on ties.  Where two fit, workgroups sharing a compute unit
+// slow each other and more of them keeps it busier: one segment each.
 template <int D, int PHI, bool CAUSAL>
 int q_segments_per_wg(const Args &a, unsigned n_units) {
-    static int slots = 0;   // resident workgroups on the device
+    static int slots = 0;   // resident workgroups on the device (0: not yet asked)
     if (slots == 0) {
         int dev = 0, cus = 0, per_cu = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
@@ -371,8 +372,9 @@ int q_segments_per_wg(const Args &a, unsigned n_units) {
                                                          4 * D, 0) != hipSuccess ||
             cus <= 0 || per_cu <= 0)
             return 1;
-        slots = cus * per_cu;
+        slots = per_cu == 1 ? cus : -1;
     }
+    if (slots < 0) return 1;
     int best = 1;
     long long best_t = -1;
     for (int m = 1; m <= a.nseg; ++m) {

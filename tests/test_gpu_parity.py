@@ -75,16 +75,17 @@ def test_edge_lengths(N, causal):
         compare(t, out, grads, ref[0], ref[1], dtype, 2, 1, label="N=%d" % N)
 
 
-SPAN = [(128, True, 4, 4), (128, False, 8, 4), (64, True, 8, 4)]
+SPAN = [(128, True, 4, 4), (128, False, 8, 4), (128, True, 8, 2)]
 
 
 @pytest.mark.parametrize("D,causal,H,Hkv", SPAN,
                          ids=["D%d-%s-h%dkv%d" % (D, "causal" if c else "bidir", H, Hkv)
                               for D, c, H, Hkv in SPAN])
 def test_dq_workgroup_spans_segments(D, causal, H, Hkv):
-    """Many short segments (seg_len 64) over a long ragged sequence: the dq
-    kernel then walks several consecutive segments per workgroup (its state
-    carry crosses their boundaries) and writes one (R, r) record per segment."""
+    """Many short segments (seg_len 64) over a long ragged sequence at D = 128,
+    where the dq kernel runs one workgroup per compute unit: it then walks
+    several consecutive segments per workgroup (its state carry crosses their
+    boundaries) and writes one (R, r) record per segment."""
     torch, la = gpu_or_skip()
     B, N = 1, 16300
     t = make(B, H, Hkv, N, D, "bf16", scale=0.5, cos=False, seed=D + H + N)
