@@ -110,12 +110,16 @@ bool uses_mfma(int op_bwd, int dtype, int causal, int D, int has_cos) {
 la::Plan plan_for(int op_bwd, int B, int H, int H_kv, int N, int D, int dtype, int causal,
                   int has_cos, int seg_len) {
     // matrix-core kernels: about two workgroups per compute unit (256 on the
-    // device), except the causal cos/sin ones at D = 128 (F = 256), which fit
-    // one per compute unit; they are as fast with one round of longer
-    // segments and the state records then cost half as much
-    if (uses_mfma(op_bwd, dtype, causal, D, has_cos))
+    // device) at D = 128.  The causal cos/sin ones there (F = 256) fit one
+    // per compute unit; they are as fast with one round of longer segments,
+    // and the state records then cost half as much.  At D = 64 the forward
+    // and dk/dv workgroups have two waves: aim for six per compute unit (the
+    // 256-row minimum segment usually binds first)
+    if (uses_mfma(op_bwd, dtype, causal, D, has_cos)) {
+        const long long target = D == 64 ? 1536 : has_cos && causal ? 256 : 512;
         return la::make_plan(op_bwd, B, H, H_kv, N, D, causal, has_cos, seg_len,
-                             (long long)B * H_kv, has_cos && causal && D == 128 ? 256 : 512);
+                             (long long)B * H_kv, target);
+    }
     return la::make_plan(op_bwd, B, H, H_kv, N, D, causal, has_cos, seg_len, (long long)B * H,
                          1024);
 }

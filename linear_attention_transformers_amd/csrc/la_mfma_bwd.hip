@@ -56,9 +56,9 @@ constexpr int kCb = 32;   // backward chunk length: one 32x32 tile per head
 // After that exchange (one barrier) the two wave kinds run independently: the
 // R update needs only 1/den, and the R waves recompute c for r.
 // ---------------------------------------------------------------------------
-template <int D, int PHI, bool CAUSAL>
+template <int D, int PHI, bool CAUSAL, bool MULTI>
 __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2)))
-void k_bwd_q_mfma(Args a, int qm) {
+void k_bwd_q_mfma(Args a, int qm_arg) {
     constexpr int F = D, NW = D / 32, NT = 4 * D;
     using TF = PadI<F>;
     using TD = PadI<D>;
@@ -74,7 +74,9 @@ void k_bwd_q_mfma(Args a, int qm) {
 
     // this workgroup walks the qm consecutive segments seg0 .. seg0 + qm - 1
     // (its state carry runs through their boundaries) and writes each one's
-    // (R, r) record
+    // (R, r) record; without MULTI, qm = 1 at compile time and the segment
+    // loop below is a single pass
+    const int qm = MULTI ? qm_arg : 1;
     const int nq = (a.nseg + qm - 1) / qm;
     const int seg0 = (blockIdx.x % nq) * qm, bg = blockIdx.x / nq;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
@@ -120,224 +122,226 @@ void k_bwd_q_mfma(Args a, int qm) {
     }
     rQ.load(qbase + bh0 * a.N * D, row0, a.N);
     rG.load(gbase + bh0 * a.N * D, row0, a.N);
-    for (int c0 = row0; c0 < row1; c0 += kCb) {
-        __syncthreads();
-        if constexpr (CAUSAL) {
-            rK.template store_feat<PHI, false, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
-            rV.template store<TD>(sV);
-            // the next chunk's K, V (unconditional: rows past the segment are
-            // loaded clamped and never used, and no register copies are needed)
-            rK.load(kh, c0 + kCb, a.N);
-            rV.load(vh, c0 + kCb, a.N);
-        }
-        // the first head's rows are staged here, in straight-line code (in the
-        // head loop, the wait for them would also wait for the K, V loads
-        // just issued: the loop header merges the later heads' path)
-        rQ.template store_feat<PHI, false, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
-        rG.template store<TD>(sG);
-        for (int rep = 0; rep < a.nrep; ++rep) {
-            const size_t bh = bh0 + rep;
-            if (rep > 0) {
+    for (int seg = seg0; seg < seg0 + qm && seg * a.L < row1; ++seg) {
+        const int s1 = min(seg * a.L + a.L, row1);
+        for (int c0 = seg * a.L; c0 < s1; c0 += kCb) {
+            __syncthreads();
+            if constexpr (CAUSAL) {
+                rK.template store_feat<PHI, false, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+                rV.template store<TD>(sV);
+                // the next chunk's K, V (unconditional: rows past the workgroup's
+                // segments are loaded clamped and never used, and no register
+                // copies are needed)
+                rK.load(kh, c0 + kCb, a.N);
+                rV.load(vh, c0 + kCb, a.N);
+            }
+            // the first head's rows are staged here, in straight-line code (in the
+            // head loop, the wait for them would also wait for the K, V loads
+            // just issued: the loop header merges the later heads' path)
+            rQ.template store_feat<PHI, false, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+            rG.template store<TD>(sG);
+            for (int rep = 0; rep < a.nrep; ++rep) {
+                const size_t bh = bh0 + rep;
+                if (rep > 0) {
+                    __syncthreads();
+                    rQ.template store_feat<PHI, false, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+                    rG.template store<TD>(sG);
+                }
                 __syncthreads();
-                rQ.template store_feat<PHI, false, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
-                rG.template store<TD>(sG);
-            }
-            __syncthreads();
-            {   // Q, G rows of the next head, or of the first head at the next chunk
-                const bool last = rep + 1 == a.nrep;
-                const size_t hn = bh0 + (last ? 0 : rep + 1);
-                const int cn = last ? c0 + kCb : c0;
-                rQ.load(qbase + hn * a.N * D, cn, a.N);
-                rG.load(gbase + hn * a.N * D, cn, a.N);
-            }
-            const bool ok = c0 + l32 < a.N;   // this lane's query row exists
-            f32x16 U;
-            if (state_wave) {
-                // U^T = S g (this feature block x the chunk's queries)
-                U = zero16();
-#pragma unroll
-                for (int db = 0; db < NW; ++db)
-#pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        const bf16x8 gq = ld4x2<TD>(sG, l32, 32 * db + 16 * s + 4 * h);
-                        U = mfma(acc_op(X[db], s), gq, U);
-                        // bidirectional: every term goes through the state, and with
-                        // few keys dq is a small difference: S in two bf16 parts
-                        if constexpr (!CAUSAL) U = mfma(acc_lo(X[db], s), gq, U);
-                    }
-                float qu = 0.f, x4[4];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    ld4f(sQ + TF::at(l32, 32 * w + 8 * q4 + 4 * h), x4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) qu += x4[e] * U[4 * q4 + e];
+                {   // Q, G rows of the next head, or of the first head at the next chunk
+                    const bool last = rep + 1 == a.nrep;
+                    const size_t hn = bh0 + (last ? 0 : rep + 1);
+                    const int cn = last ? c0 + kCb : c0;
+                    rQ.load(qbase + hn * a.N * D, cn, a.N);
+                    rG.load(gbase + hn * a.N * D, cn, a.N);
                 }
-                qu = sum_halves(qu);
-                if (h == 0) sQU[w][l32] = qu;
-            } else if (w == NW) {
-                // causal: A^T (keys x queries), causal mask, rounded to bf16
-                // (the forward's A), the tile for the state waves; the denominators
-                float dA = 0.f;
-                if constexpr (CAUSAL) {
-                    f32x16 At = zero16();
-#pragma unroll 4
-                    for (int s = 0; s < F / 16; ++s)
-                        At = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), At);
+                const bool ok = c0 + l32 < a.N;   // this lane's query row exists
+                f32x16 U;
+                if (state_wave) {
+                    // U^T = S g (this feature block x the chunk's queries)
+                    U = zero16();
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        At[r] = acc_row(r, h) <= l32 ? (float)(__bf16)At[r] : 0.f;
-                        dA += At[r];
-                    }
-                    dA = sum_halves(dA);
-                    put_acc(sAt, At);
-                }
-                if (h == 0) {
-                    const float den = ok ? dA + sQZ[l32] + a.eps : 1.f;
-                    sDen[l32] = den;
-                    sInv[l32] = rcp(den);
-                }
-            } else if (CAUSAL && w == NW + 1) {
-                // T^T = V G^T (keys x queries), unmasked: the state waves mask
-                f32x16 Tt = zero16();
-#pragma unroll 4
-                for (int s = 0; s < D / 16; ++s)
-                    Tt = mfma(ld8<TD>(sV, l32, 16 * s + 8 * h), ld8<TD>(sG, l32, 16 * s + 8 * h), Tt);
-                put_acc(sTt, Tt);
-            }
-            __syncthreads();
-            if (state_wave) {
-                // c = (sum_j A_ij T_ij + Phi(q_i).U_i) / den_i^2 (no A term: bidirectional)
-                f32x16 Tt;
-                float aT = 0.f;
-                if constexpr (CAUSAL) {
-                    Tt = get_acc(sTt);
-                    const f32x16 At = get_acc(sAt);
+                    for (int db = 0; db < NW; ++db)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) aT += At[r] * Tt[r];
-                    aT = sum_halves(aT);
-                }
-                float gsum = aT;
-#pragma unroll
-                for (int ww = 0; ww < NW; ++ww) gsum += sQU[ww][l32];
-                const float inv = sInv[l32];
-                const float c = ok ? gsum * inv * inv : 0.f;
-                f32x16 Qd = zero16();
-                if constexpr (CAUSAL) {
-                    if (w == 0 && h == 0 && ok) {   // for the dk/dv pass
-                        a.ws_den[bh * a.N + c0 + l32] = sDen[l32];
-                        a.ws_c[bh * a.N + c0 + l32] = c;
-                    }
-                    // P^T = T^T / den - c (masked), then dPhi(q)^T = Phi(K)^T P^T + U^T / den - z c
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        Tt[r] = acc_row(r, h) <= l32 ? Tt[r] * inv - c : 0.f;
-#pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        const int k0 = 16 * s + 4 * h;
-                        const bf16x8 ka = tr8(tr_addr<TF>(sK, k0, 32 * w), tr_addr<TF>(sK, k0 + 8, 32 * w));
-                        Qd = mfma(ka, acc_op(Tt, s), Qd);
-                    }
-                }
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int f0 = 32 * w + 8 * q4 + 4 * h;
-                    float qf[4];
-                    ld4f(sQ + TF::at(l32, f0), qf);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        Qd[4 * q4 + e] = phi_d_feat<PHI>(qf[e]) *
-                                         (Qd[4 * q4 + e] + U[4 * q4 + e] * inv - sz[f0 + e] * c);
-                }
-                const int row = c0 + l32;
-                if (row < a.N) {
+                        for (int s = 0; s < 2; ++s) {
+                            const bf16x8 gq = ld4x2<TD>(sG, l32, 32 * db + 16 * s + 4 * h);
+                            U = mfma(acc_op(X[db], s), gq, U);
+                            // bidirectional: every term goes through the state, and with
+                            // few keys dq is a small difference: S in two bf16 parts
+                            if constexpr (!CAUSAL) U = mfma(acc_lo(X[db], s), gq, U);
+                        }
+                    float qu = 0.f, x4[4];
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
-                        const float o[4] = {Qd[4 * q4], Qd[4 * q4 + 1], Qd[4 * q4 + 2], Qd[4 * q4 + 3]};
-                        st4bf(dqbase + bh * a.N * D + (size_t)row * D + 32 * w + 8 * q4 + 4 * h, o);
+                        ld4f(sQ + TF::at(l32, 32 * w + 8 * q4 + 4 * h), x4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) qu += x4[e] * U[4 * q4 + e];
+                    }
+                    qu = sum_halves(qu);
+                    if (h == 0) sQU[w][l32] = qu;
+                } else if (w == NW) {
+                    // causal: A^T (keys x queries), causal mask, rounded to bf16
+                    // (the forward's A), the tile for the state waves; the denominators
+                    float dA = 0.f;
+                    if constexpr (CAUSAL) {
+                        f32x16 At = zero16();
+#pragma unroll 4
+                        for (int s = 0; s < F / 16; ++s)
+                            At = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), At);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            At[r] = acc_row(r, h) <= l32 ? (float)(__bf16)At[r] : 0.f;
+                            dA += At[r];
+                        }
+                        dA = sum_halves(dA);
+                        put_acc(sAt, At);
+                    }
+                    if (h == 0) {
+                        const float den = ok ? dA + sQZ[l32] + a.eps : 1.f;
+                        sDen[l32] = den;
+                        sInv[l32] = rcp(den);
+                    }
+                } else if (CAUSAL && w == NW + 1) {
+                    // T^T = V G^T (keys x queries), unmasked: the state waves mask
+                    f32x16 Tt = zero16();
+#pragma unroll 4
+                    for (int s = 0; s < D / 16; ++s)
+                        Tt = mfma(ld8<TD>(sV, l32, 16 * s + 8 * h), ld8<TD>(sG, l32, 16 * s + 8 * h), Tt);
+                    put_acc(sTt, Tt);
+                }
+                __syncthreads();
+                if (state_wave) {
+                    // c = (sum_j A_ij T_ij + Phi(q_i).U_i) / den_i^2 (no A term: bidirectional)
+                    f32x16 Tt;
+                    float aT = 0.f;
+                    if constexpr (CAUSAL) {
+                        Tt = get_acc(sTt);
+                        const f32x16 At = get_acc(sAt);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) aT += At[r] * Tt[r];
+                        aT = sum_halves(aT);
+                    }
+                    float gsum = aT;
+#pragma unroll
+                    for (int ww = 0; ww < NW; ++ww) gsum += sQU[ww][l32];
+                    const float inv = sInv[l32];
+                    const float c = ok ? gsum * inv * inv : 0.f;
+                    f32x16 Qd = zero16();
+                    if constexpr (CAUSAL) {
+                        if (w == 0 && h == 0 && ok) {   // for the dk/dv pass
+                            a.ws_den[bh * a.N + c0 + l32] = sDen[l32];
+                            a.ws_c[bh * a.N + c0 + l32] = c;
+                        }
+                        // P^T = T^T / den - c (masked), then dPhi(q)^T = Phi(K)^T P^T + U^T / den - z c
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            Tt[r] = acc_row(r, h) <= l32 ? Tt[r] * inv - c : 0.f;
+#pragma unroll
+                        for (int s = 0; s < 2; ++s) {
+                            const int k0 = 16 * s + 4 * h;
+                            const bf16x8 ka = tr8(tr_addr<TF>(sK, k0, 32 * w), tr_addr<TF>(sK, k0 + 8, 32 * w));
+                            Qd = mfma(ka, acc_op(Tt, s), Qd);
+                        }
+                    }
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int f0 = 32 * w + 8 * q4 + 4 * h;
+                        float qf[4];
+                        ld4f(sQ + TF::at(l32, f0), qf);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            Qd[4 * q4 + e] = phi_d_feat<PHI>(qf[e]) *
+                                             (Qd[4 * q4 + e] + U[4 * q4 + e] * inv - sz[f0 + e] * c);
+                    }
+                    const int row = c0 + l32;
+                    if (row < a.N) {
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            const float o[4] = {Qd[4 * q4], Qd[4 * q4 + 1], Qd[4 * q4 + 2], Qd[4 * q4 + 3]};
+                            st4bf(dqbase + bh * a.N * D + (size_t)row * D + 32 * w + 8 * q4 + 4 * h, o);
+                        }
+                    }
+                }
+                if (!state_wave) {
+                    // c_i for this lane's query, as the state waves form it (same
+                    // bits), then through this wave's LDS row into operand order:
+                    // lane (n, h) needs c of rows 16s + 8h + 0..7
+                    float aT = 0.f;
+                    if constexpr (CAUSAL) {
+                        const f32x16 At = get_acc(sAt), Tt = get_acc(sTt);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) aT += At[r] * Tt[r];
+                        aT = sum_halves(aT);
+                    }
+                    float gsum = aT;
+#pragma unroll
+                    for (int ww = 0; ww < NW; ++ww) gsum += sQU[ww][l32];
+                    const float iq = sInv[l32];
+                    if (h == 0) sCw[wr][l32] = ok ? gsum * iq * iq : 0.f;
+                    // R (feature block wr x every value block) += (Phi(Q) / den)^T G,
+                    // r (feature block wr) += Phi(Q)^T c: c in two bf16 parts as the
+                    // B operand of every column, so each column of Rr holds r
+#pragma unroll
+                    for (int s = 0; s < kCb / 16; ++s) {
+                        const int k0 = 16 * s + 8 * h;
+                        bf16x8 qa = tr8(tr_addr<TF>(sQ, k0, 32 * wr), tr_addr<TF>(sQ, k0 + 4, 32 * wr));
+                        {
+                            const float4 c0v = *reinterpret_cast<const float4 *>(&sCw[wr][k0]);
+                            const float4 c1v = *reinterpret_cast<const float4 *>(&sCw[wr][k0 + 4]);
+                            const float cv[8] = {c0v.x, c0v.y, c0v.z, c0v.w, c1v.x, c1v.y, c1v.z, c1v.w};
+                            bf16x8 chi, clo;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                chi[e] = (__bf16)cv[e];
+                                clo[e] = (__bf16)(cv[e] - (float)chi[e]);
+                            }
+                            Rr = mfma(qa, chi, Rr);
+                            Rr = mfma(qa, clo, Rr);
+                        }
+                        const float4 i0 = *reinterpret_cast<const float4 *>(sInv + k0);
+                        const float4 i1 = *reinterpret_cast<const float4 *>(sInv + k0 + 4);
+                        const float sc[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+                        bf16x8 qlo;   // bidirectional: Phi(q) / den in two bf16 parts (R v - r is
+                                      // a small difference when few queries see a key)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float x = (float)qa[e] * sc[e];
+                            qa[e] = (__bf16)x;
+                            qlo[e] = (__bf16)(x - (float)qa[e]);
+                        }
+#pragma unroll
+                        for (int db = 0; db < NW; ++db) {
+                            const bf16x8 gb = tr8(tr_addr<TD>(sG, k0, 32 * db), tr_addr<TD>(sG, k0 + 4, 32 * db));
+                            X[db] = mfma(qa, gb, X[db]);
+                            if constexpr (!CAUSAL) X[db] = mfma(qlo, gb, X[db]);
+                        }
                     }
                 }
             }
-            if (!state_wave) {
-                // c_i for this lane's query, as the state waves form it (same
-                // bits), then through this wave's LDS row into operand order:
-                // lane (n, h) needs c of rows 16s + 8h + 0..7
-                float aT = 0.f;
-                if constexpr (CAUSAL) {
-                    const f32x16 At = get_acc(sAt), Tt = get_acc(sTt);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) aT += At[r] * Tt[r];
-                    aT = sum_halves(aT);
-                }
-                float gsum = aT;
-#pragma unroll
-                for (int ww = 0; ww < NW; ++ww) gsum += sQU[ww][l32];
-                const float iq = sInv[l32];
-                if (h == 0) sCw[wr][l32] = ok ? gsum * iq * iq : 0.f;
-                // R (feature block wr x every value block) += (Phi(Q) / den)^T G,
-                // r (feature block wr) += Phi(Q)^T c: c in two bf16 parts as the
-                // B operand of every column, so each column of Rr holds r
+            if (CAUSAL && state_wave) {
+                // carry (S^T, z) past this chunk
 #pragma unroll
                 for (int s = 0; s < kCb / 16; ++s) {
                     const int k0 = 16 * s + 8 * h;
-                    bf16x8 qa = tr8(tr_addr<TF>(sQ, k0, 32 * wr), tr_addr<TF>(sQ, k0 + 4, 32 * wr));
-                    {
-                        const float4 c0v = *reinterpret_cast<const float4 *>(&sCw[wr][k0]);
-                        const float4 c1v = *reinterpret_cast<const float4 *>(&sCw[wr][k0 + 4]);
-                        const float cv[8] = {c0v.x, c0v.y, c0v.z, c0v.w, c1v.x, c1v.y, c1v.z, c1v.w};
-                        bf16x8 chi, clo;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            chi[e] = (__bf16)cv[e];
-                            clo[e] = (__bf16)(cv[e] - (float)chi[e]);
-                        }
-                        Rr = mfma(qa, chi, Rr);
-                        Rr = mfma(qa, clo, Rr);
-                    }
-                    const float4 i0 = *reinterpret_cast<const float4 *>(sInv + k0);
-                    const float4 i1 = *reinterpret_cast<const float4 *>(sInv + k0 + 4);
-                    const float sc[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-                    bf16x8 qlo;   // bidirectional: Phi(q) / den in two bf16 parts (R v - r is
-                                  // a small difference when few queries see a key)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float x = (float)qa[e] * sc[e];
-                        qa[e] = (__bf16)x;
-                        qlo[e] = (__bf16)(x - (float)qa[e]);
-                    }
+                    const bf16x8 kb = tr8(tr_addr<TF>(sK, k0, 32 * w), tr_addr<TF>(sK, k0 + 4, 32 * w));
+                    Z = mfma(kb, one, Z);
 #pragma unroll
                     for (int db = 0; db < NW; ++db) {
-                        const bf16x8 gb = tr8(tr_addr<TD>(sG, k0, 32 * db), tr_addr<TD>(sG, k0 + 4, 32 * db));
-                        X[db] = mfma(qa, gb, X[db]);
-                        if constexpr (!CAUSAL) X[db] = mfma(qlo, gb, X[db]);
+                        const bf16x8 va = tr8(tr_addr<TD>(sV, k0, 32 * db), tr_addr<TD>(sV, k0 + 4, 32 * db));
+                        X[db] = mfma(va, kb, X[db]);
                     }
                 }
-            }
-        }
-        if (CAUSAL && state_wave) {
-            // carry (S^T, z) past this chunk
+                // every staging of this chunk has read sz (each preceded a barrier
+                // this wave has passed), so it can take the new z now
+                if (l32 == 0) {
 #pragma unroll
-            for (int s = 0; s < kCb / 16; ++s) {
-                const int k0 = 16 * s + 8 * h;
-                const bf16x8 kb = tr8(tr_addr<TF>(sK, k0, 32 * w), tr_addr<TF>(sK, k0 + 4, 32 * w));
-                Z = mfma(kb, one, Z);
-#pragma unroll
-                for (int db = 0; db < NW; ++db) {
-                    const bf16x8 va = tr8(tr_addr<TD>(sV, k0, 32 * db), tr_addr<TD>(sV, k0 + 4, 32 * db));
-                    X[db] = mfma(va, kb, X[db]);
+                    for (int r = 0; r < 16; ++r) sz[32 * w + acc_row(r, h)] = Z[r];
                 }
             }
-            // every staging of this chunk has read sz (each preceded a barrier
-            // this wave has passed), so it can take the new z now
-            if (l32 == 0) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sz[32 * w + acc_row(r, h)] = Z[r];
-            }
         }
-        if (!state_wave && (c0 + kCb >= row1 || (c0 + kCb - row0) % a.L == 0)) {
-            // the segment ends with this chunk: its (R, r), summed over the
-            // group's query heads, and a fresh sum for the next segment
-            // (segment lengths are multiples of the chunk length)
-            const int seg = seg0 + (c0 - row0) / a.L;
+        if (!state_wave) {
+            // this segment's (R, r), summed over the group's query heads, and a
+            // fresh sum for the next one
             float *Ro = a.ws_Rp + ((size_t)bg * a.nseg + seg) * SD;
 #pragma unroll
             for (int db = 0; db < NW; ++db) {
@@ -368,7 +372,7 @@ int q_segments_per_wg(const Args &a, unsigned n_units) {
         int dev = 0, cus = 0, per_cu = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_bwd_q_mfma<D, PHI, CAUSAL>,
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_bwd_q_mfma<D, PHI, CAUSAL, false>,
                                                          4 * D, 0) != hipSuccess ||
             cus <= 0 || per_cu <= 0)
             return 1;
@@ -633,10 +637,20 @@ hipError_t run(const Args &a, hipStream_t s) {
     hipError_t e = a.state_ready ? hipSuccess : mfma_state_run(a, PHI, CAUSAL, s);
     if (e != hipSuccess) return e;
     {
-        const int qm = q_segments_per_wg<D, PHI, CAUSAL>(a, n_units);
+        bool launched = false;
+        // several segments per workgroup only where one workgroup fits per
+        // compute unit (D = 128); the one-segment kernel is a separate build
+        const int qm = D == 128 ? q_segments_per_wg<D, PHI, CAUSAL>(a, n_units) : 1;
         const unsigned nq = (unsigned)((a.nseg + qm - 1) / qm);
         TimedLaunch tl(CAUSAL ? "k_bwd_q_mfma" : "k_bwd_q_bidir_mfma", s);
-        hipLaunchKernelGGL((k_bwd_q_mfma<D, PHI, CAUSAL>), dim3(n_units * nq), dim3(4 * D), 0, s, a, qm);
+        if constexpr (D == 128) {
+            if (qm > 1) {
+                hipLaunchKernelGGL((k_bwd_q_mfma<D, PHI, CAUSAL, true>), dim3(n_units * nq), dim3(4 * D), 0, s, a, qm);
+                launched = true;
+            }
+        }
+        if (!launched)
+            hipLaunchKernelGGL((k_bwd_q_mfma<D, PHI, CAUSAL, false>), dim3(n_units * nq), dim3(4 * D), 0, s, a, 1);
     }
     {
         TimedLaunch tl("k_scan_R", s);
