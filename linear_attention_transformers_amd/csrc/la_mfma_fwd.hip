@@ -271,6 +271,149 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
 }
 
 // ---------------------------------------------------------------------------
+// k_fwd_split_mfma: the causal chunk loop of k_fwd_mfma for the wide cos/sin
+// features (F = 2D = 256), with the state's feature blocks split over two
+// sets of D/32 waves.  A 32-column slice of S over all F features takes 128
+// accumulator registers per lane, which leaves one wave per SIMD; split, each
+// wave holds F/64 tiles and two waves share a SIMD.  Wave w owns value block
+// w % (D/32) and the feature blocks of half w / (D/32) (its z block is
+// feature block w).  Every wave forms the chunk's masked A tile over all F
+// features itself; the second half's partial numerators reach the first half
+// through LDS, which then normalises and stages the output rows.
+// ---------------------------------------------------------------------------
+template <int D, int F, int PHI, bool COS>
+__global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void k_fwd_split_mfma(Args a) {
+    using TF = typename FwdTiles<D, F>::TF;
+    using TD = typename FwdTiles<D, F>::TD;
+    constexpr int NT = D * 4, NW = D / 32, FH = F / 64;   // FH feature blocks per half
+    static_assert(F == 2 * D, "two feature halves of D/32 blocks each");
+    __shared__ __attribute__((aligned(16))) u16 sK[kCf * TF::ld];
+    __shared__ __attribute__((aligned(16))) u16 sQ[kCf * TF::ld];
+    __shared__ __attribute__((aligned(16))) u16 sV[kCf * TD::ld];
+    __shared__ __attribute__((aligned(16))) u16 sO[kCf * TD::ld];   // output rows of one head
+    __shared__ __attribute__((aligned(16))) float sNp[NW][64 * 16];   // second half's numerators
+    __shared__ __attribute__((aligned(16))) float sz[F];
+    __shared__ float sQZ[kCf];
+    const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const int t = threadIdx.x, l = t & 63, h = l >> 5, l32 = l & 31;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index, uniform
+    const int vb = w % NW, fh = w / NW;                       // value block, feature half
+    const size_t SD = (size_t)F * D + F;
+    const u16 *kh = static_cast<const u16 *>(a.k) + (size_t)bg * a.N * D;
+    const u16 *vh = static_cast<const u16 *>(a.v) + (size_t)bg * a.N * D;
+    const size_t bh0 = (size_t)b * a.H + (size_t)g * a.nrep;
+    const u16 *qbase = static_cast<const u16 *>(a.q);
+    u16 *obase = static_cast<u16 *>(a.out);
+
+    // exclusive prefix state of this segment: this wave's FH tiles of S
+    // (feature blocks FH*fh .. FH*fh + FH-1, value block vb) and z block w
+    // (every column of the z tile holds z)
+    const float *Sp = a.ws_S + ((size_t)bg * (a.nseg + 1) + seg) * SD;
+    f32x16 S[FH], Z;
+#pragma unroll
+    for (int i = 0; i < FH; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            S[i][r] = Sp[(size_t)(32 * (FH * fh + i) + acc_row(r, h)) * D + 32 * vb + l32];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Z[r] = Sp[(size_t)F * D + 32 * w + acc_row(r, h)];
+    for (int e = t; e < F; e += NT) sz[e] = Sp[(size_t)F * D + e];
+    const bf16x8 one = ones8();
+
+    const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
+    RawTile<D, NT, kCf> rK, rV, rQ;
+    rK.load(kh, row0, a.N);
+    rV.load(vh, row0, a.N);
+    rQ.load(qbase + bh0 * a.N * D, row0, a.N);
+    // rows staged in sO wait for the next barrier to be stored (pend_* = where)
+    u16 *pend_oh = nullptr;
+    int pend_c0 = 0;
+    for (int c0 = row0; c0 < row1; c0 += kCf) {
+        __syncthreads();   // previous chunk: every LDS read done, sz updated, sO complete
+        if (pend_oh) store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
+        rK.template store_feat<PHI, COS, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rV.template store<TD>(sV);
+        rK.load(kh, c0 + kCf, a.N);   // next chunk (past the segment: clamped, unused)
+        rV.load(vh, c0 + kCf, a.N);
+        rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+        for (int rep = 0; rep < a.nrep; ++rep) {
+            u16 *oh = obase + (bh0 + rep) * a.N * D;
+            if (rep > 0) {
+                __syncthreads();   // every wave is done with the previous head's sQ; sO complete
+                rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+                store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
+            }
+            __syncthreads();
+            {   // Q rows of the next head, or of the first head at the next chunk
+                const bool last = rep + 1 == a.nrep;
+                rQ.load(qbase + (bh0 + (last ? 0 : rep + 1)) * a.N * D, last ? c0 + kCf : c0, a.N);
+            }
+            // A^T (keys x queries) over all F features, causal mask, bf16
+            // rounding and the in-chunk denominators, as in k_fwd_mfma
+            f32x16 T = zero16();
+#pragma unroll 4
+            for (int s = 0; s < F / 16; ++s)
+                T = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), T);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) T[r] = acc_row(r, h) <= l32 ? T[r] : 0.f;
+            const bf16x8 B0 = acc_op(T, 0), B1 = acc_op(T, 1);
+
+            // num^T of value block vb: the first half adds V^T A^T, each half
+            // its feature blocks' S^T Phi(Q)^T
+            f32x16 Nt = zero16();
+            if (fh == 0) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const int k0 = 16 * s + 4 * h;
+                    const bf16x8 va = tr8(tr_addr<TD>(sV, k0, 32 * vb), tr_addr<TD>(sV, k0 + 8, 32 * vb));
+                    Nt = mfma(va, s ? B1 : B0, Nt);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < FH; ++i)
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    Nt = mfma(acc_op(S[i], s), ld4x2<TF>(sQ, l32, 32 * (FH * fh + i) + 16 * s + 4 * h), Nt);
+            if (fh == 1) put_acc(sNp[vb], Nt);
+            __syncthreads();
+            if (fh == 0) {
+                const f32x16 P = get_acc(sNp[vb]);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Nt[r] += P[r];
+                // sum_j A_ij on the matrix cores: 1^T A^T, every row holds it
+                const float dsum = mfma(one, B1, mfma(one, B0, zero16()))[0];
+                const float den = dsum + sQZ[l32] + a.eps;
+                stage_out<TD>(sO, Nt, rcp(den), 32 * vb);
+            }
+            pend_oh = oh;
+            pend_c0 = c0;
+        }
+        // carry this wave's part of (S, z) past the chunk
+#pragma unroll
+        for (int s = 0; s < kCf / 16; ++s) {
+            const int k0 = 16 * s + 8 * h;
+            const bf16x8 vo = tr8(tr_addr<TD>(sV, k0, 32 * vb), tr_addr<TD>(sV, k0 + 4, 32 * vb));
+#pragma unroll
+            for (int i = 0; i < FH; ++i) {
+                const int fb = FH * fh + i;
+                const bf16x8 ka = tr8(tr_addr<TF>(sK, k0, 32 * fb), tr_addr<TF>(sK, k0 + 4, 32 * fb));
+                S[i] = mfma(ka, vo, S[i]);
+                if (i == vb) Z = mfma(ka, one, Z);   // feature block w = FH * fh + vb
+            }
+        }
+        // every head's staging has read sz (they all passed the barrier before
+        // their products), so it can take the new z now
+        if (l32 == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sz[32 * w + acc_row(r, h)] = Z[r];
+        }
+    }
+    __syncthreads();
+    if (pend_oh) store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
+}
+
+// ---------------------------------------------------------------------------
 // k_fwd_bidir_mfma: bidirectional row pass (linear_attn page, module
 // docstring: the bidirectional parallel reduction), per (batch, KV head,
 // segment of query rows), for all n_rep query heads:
@@ -366,6 +509,13 @@ hipError_t run(const Args &a, bool causal, hipStream_t s) {
     hipError_t e = run_state<D, F, PHI, COS>(a, causal, s);
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)(a.B * a.Hkv * a.nseg));
+    if constexpr (F == 256) {
+        if (causal) {   // F = 2D = 256: the feature blocks split over two wave sets
+            TimedLaunch tl("k_fwd_split_mfma", s);
+            hipLaunchKernelGGL((k_fwd_split_mfma<D, F, PHI, COS>), grid, dim3(2 * NT), 0, s, a);
+            return hipGetLastError();
+        }
+    }
     if (causal) {
         TimedLaunch tl("k_fwd_mfma", s);
         hipLaunchKernelGGL((k_fwd_mfma<D, F, PHI, COS>), grid, dim3(NT), 0, s, a);
