@@ -349,20 +349,21 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void
                 const bool last = rep + 1 == a.nrep;
                 rQ.load(qbase + (bh0 + (last ? 0 : rep + 1)) * a.N * D, last ? c0 + kCf : c0, a.N);
             }
-            // A^T (keys x queries) over all F features, causal mask, bf16
-            // rounding and the in-chunk denominators, as in k_fwd_mfma
-            f32x16 T = zero16();
-#pragma unroll 4
-            for (int s = 0; s < F / 16; ++s)
-                T = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), T);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) T[r] = acc_row(r, h) <= l32 ? T[r] : 0.f;
-            const bf16x8 B0 = acc_op(T, 0), B1 = acc_op(T, 1);
-
             // num^T of value block vb: the first half adds V^T A^T, each half
-            // its feature blocks' S^T Phi(Q)^T
+            // its feature blocks' S^T Phi(Q)^T.  The first half forms A^T
+            // (keys x queries) over all F features, causal mask, bf16 rounding
+            // (and the in-chunk denominators), as in k_fwd_mfma
             f32x16 Nt = zero16();
+            bf16x8 B0, B1;
             if (fh == 0) {
+                f32x16 T = zero16();
+#pragma unroll 4
+                for (int s = 0; s < F / 16; ++s)
+                    T = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), T);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) T[r] = acc_row(r, h) <= l32 ? T[r] : 0.f;
+                B0 = acc_op(T, 0);
+                B1 = acc_op(T, 1);
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     const int k0 = 16 * s + 4 * h;
