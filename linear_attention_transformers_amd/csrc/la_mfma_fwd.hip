@@ -41,25 +41,27 @@ struct FwdTiles {
     using TD = PadI<D>;
 };
 
-// S[fb] += Phi(K)^T V over the 64 rows of the staged chunk, for this wave's
-// value columns (natural k order: lane half h holds rows 16s + 8h .. +7), and
-// z += Phi(K)^T 1 for the feature blocks fb = w (mod D/32) into Z[fb / (D/32)].
-template <int D, int F>
-__device__ __forceinline__ void state_update(f32x16 *S, f32x16 *Z, const u16 *sK, const u16 *sV, int w) {
+// S += Phi(K)^T V over the 64 rows of the staged chunk for one wave's tiles:
+// value block vb and feature blocks FBW*fh .. FBW*fh + FBW-1 (natural k order:
+// lane half h holds rows 16s + 8h .. +7), and z += Phi(K)^T 1 for the feature
+// blocks fb = w (mod ZW) into Z[fb / ZW].
+template <int D, int F, int FBW, int ZW>
+__device__ __forceinline__ void state_update(f32x16 *S, f32x16 *Z, const u16 *sK, const u16 *sV,
+                                             int w, int vb, int fh) {
     using TF = typename FwdTiles<D, F>::TF;
     using TD = typename FwdTiles<D, F>::TD;
-    constexpr int NW = D / 32;
     const int h = (threadIdx.x & 63) >> 5;
     const bf16x8 one = ones8();
 #pragma unroll
     for (int s = 0; s < kC / 16; ++s) {
         const int k0 = 16 * s + 8 * h;
-        const bf16x8 vb = tr8(tr_addr<TD>(sV, k0, 32 * w), tr_addr<TD>(sV, k0 + 4, 32 * w));
+        const bf16x8 vo = tr8(tr_addr<TD>(sV, k0, 32 * vb), tr_addr<TD>(sV, k0 + 4, 32 * vb));
 #pragma unroll
-        for (int fb = 0; fb < F / 32; ++fb) {
+        for (int i = 0; i < FBW; ++i) {
+            const int fb = FBW * fh + i;
             const bf16x8 ka = tr8(tr_addr<TF>(sK, k0, 32 * fb), tr_addr<TF>(sK, k0 + 4, 32 * fb));
-            S[fb] = mfma(ka, vb, S[fb]);
-            if (fb % NW == w) Z[fb / NW] = mfma(ka, one, Z[fb / NW]);
+            S[i] = mfma(ka, vo, S[i]);
+            if (fb % ZW == w) Z[fb / ZW] = mfma(ka, one, Z[fb / ZW]);
         }
     }
 }
@@ -68,28 +70,37 @@ __device__ __forceinline__ void state_update(f32x16 *S, f32x16 *Z, const u16 *sK
 // k_state_mfma: per (batch, KV head, segment) the segment sums
 // dS = sum_j Phi(k_j) v_j^T (F x D) and dz = sum_j Phi(k_j), written as fp32
 // to the workspace record of the segment.  The next chunk's loads are issued
-// before the current chunk's products.
+// before the current chunk's products.  NH wave sets of D/32 waves split the
+// feature blocks: wave w owns value block w % (D/32) and feature half
+// w / (D/32) (the tiles are disjoint, so nothing crosses waves).  At F = 256
+// two sets keep 64 accumulator registers per lane instead of 128, and two
+// waves share a SIMD instead of one.
 // ---------------------------------------------------------------------------
 // Occupancy the state pass is built for: it streams K and V, so more waves
 // per SIMD hide more load latency (each shape's registers allow this).
 template <int D, int F>
-constexpr int state_waves() { return F == 64 ? 4 : F == 128 ? (D == 128 ? 3 : 2) : 1; }
+constexpr int state_sets() { return F == 256 ? 2 : 1; }
+template <int D, int F>
+constexpr int state_waves() { return F == 64 ? 4 : F == 128 ? (D == 128 ? 3 : 2) : 2; }
 
 template <int D, int F, int PHI, bool COS>
-__global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(state_waves<D, F>()))) void k_state_mfma(Args a, int nseg_run) {
+__global__ __launch_bounds__((D * 2 * state_sets<D, F>())) __attribute__((amdgpu_waves_per_eu(state_waves<D, F>()))) void k_state_mfma(Args a, int nseg_run) {
     using TF = typename FwdTiles<D, F>::TF;
     using TD = typename FwdTiles<D, F>::TD;
-    constexpr int NT = D * 2, NW = D / 32, FB = F / 32, ZB = FB / NW;
+    constexpr int NH = state_sets<D, F>(), NW = D / 32, NT = D * 2 * NH;
+    constexpr int FBW = F / 32 / NH, ZW = NW * NH, ZB = F / 32 / ZW;
+    static_assert(FBW * NH * 32 == F && ZB * ZW * 32 == F, "feature blocks split evenly");
     __shared__ __attribute__((aligned(16))) u16 sK[kC * TF::ld];
     __shared__ __attribute__((aligned(16))) u16 sV[kC * TD::ld];
     const int seg = blockIdx.x % nseg_run, bg = blockIdx.x / nseg_run;   // segments 0 .. nseg_run-1
     const int t = threadIdx.x, l = t & 63, h = l >> 5, l32 = l & 31;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index, uniform
+    const int vb = w % NW, fh = w / NW;                       // value block, feature set
     const u16 *kh = static_cast<const u16 *>(a.k) + (size_t)bg * a.N * D;
     const u16 *vh = static_cast<const u16 *>(a.v) + (size_t)bg * a.N * D;
-    f32x16 S[FB], Z[ZB];
+    f32x16 S[FBW], Z[ZB];
 #pragma unroll
-    for (int fb = 0; fb < FB; ++fb) S[fb] = zero16();
+    for (int i = 0; i < FBW; ++i) S[i] = zero16();
 #pragma unroll
     for (int c = 0; c < ZB; ++c) Z[c] = zero16();
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
@@ -103,15 +114,15 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(state_wav
         __syncthreads();
         rK.load(kh, c0 + kC, a.N);   // next chunk (past the segment: unused)
         rV.load(vh, c0 + kC, a.N);
-        state_update<D, F>(S, Z, sK, sV, w);
+        state_update<D, F, FBW, ZW>(S, Z, sK, sV, w, vb, fh);
     }
     float *out = a.ws_S + ((size_t)bg * (a.nseg + 1) + seg) * ((size_t)F * D + F);
 #pragma unroll
-    for (int fb = 0; fb < FB; ++fb)
+    for (int i = 0; i < FBW; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int f = 32 * fb + 8 * (r >> 2) + 4 * h + (r & 3);
-            out[(size_t)f * D + 32 * w + l32] = S[fb][r];
+            const int f = 32 * (FBW * fh + i) + acc_row(r, h);
+            out[(size_t)f * D + 32 * vb + l32] = S[i][r];
         }
     // every column of a z tile holds z: lane 0 of each half writes its rows
     if (l32 == 0) {
@@ -119,7 +130,7 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(state_wav
         for (int c = 0; c < ZB; ++c)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                out[(size_t)F * D + 32 * (w + NW * c) + 8 * (r >> 2) + 4 * h + (r & 3)] = Z[c][r];
+                out[(size_t)F * D + 32 * (w + ZW * c) + acc_row(r, h)] = Z[c][r];
     }
 }
 
@@ -497,7 +508,8 @@ hipError_t run_state(const Args &a, bool causal, hipStream_t s) {
     const int nseg_run = causal ? a.nseg - 1 : a.nseg;
     if (nseg_run > 0) {
         TimedLaunch tl("k_state_mfma", s);
-        hipLaunchKernelGGL((k_state_mfma<D, F, PHI, COS>), dim3(n_units * nseg_run), dim3(NT), 0, s, a,
+        hipLaunchKernelGGL((k_state_mfma<D, F, PHI, COS>), dim3(n_units * nseg_run),
+                           dim3(NT * state_sets<D, F>()), 0, s, a,
                            nseg_run);
     }
     TimedLaunch tl("k_scan_S", s);
