@@ -219,14 +219,17 @@ void k_bwd_q_cos_mfma(Args a) {
 // k_bwd_r_cos_mfma: per (batch, KV head, segment) the segment's sums over
 // the n_rep query heads of R = sum_i Phi(q_i) gn_i^T (F x D) and
 // r = sum_i c_i Phi(q_i), gn_i = g_i / den_i, written as fp32 to the
-// workspace record of the segment.  Wave w owns value block w: the F/32 R
-// tiles of that block, and the r tiles of feature blocks w, w + D/32, ...
+// workspace record of the segment.  Two sets of D/32 waves split the
+// feature blocks: wave w owns value block w % (D/32) and the F/64 R tiles of
+// feature half w / (D/32) in that block, and the r tile of feature block w
 // (r = Phi(Q)^T c on the matrix cores with c rounded to bf16, every column
-// of an r tile holding r).
+// of an r tile holding r).  The tiles are disjoint, so nothing crosses
+// waves; split, a wave holds 64 accumulator registers per lane instead of
+// 128 and two waves share a SIMD.
 // ---------------------------------------------------------------------------
 template <int D, int PHI>
-__global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(1))) void k_bwd_r_cos_mfma(Args a) {
-    constexpr int F = 2 * D, NW = D / 32, FB = F / 32, ZB = FB / NW, NT = 2 * D;
+__global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void k_bwd_r_cos_mfma(Args a) {
+    constexpr int F = 2 * D, NW = D / 32, FBW = F / 64, NT = 4 * D;
     using TF = PadI<F>;
     using TD = PadI<D>;
     __shared__ __attribute__((aligned(16))) u16 sQ[kCc * TF::ld];
@@ -235,15 +238,14 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(1))) void
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int t = threadIdx.x, l = t & 63, h = l >> 5, l32 = l & 31;
-    const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // value block, uniform
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index, uniform
+    const int vb = w % NW, fh = w / NW;                       // value block, feature half
     const size_t bh0 = (size_t)b * a.H + (size_t)g * a.nrep;
     const u16 *qbase = static_cast<const u16 *>(a.q);
     const u16 *gbase = static_cast<const u16 *>(a.g);
-    f32x16 R[FB], Zr[ZB];
+    f32x16 R[FBW], Zr = zero16();
 #pragma unroll
-    for (int fb = 0; fb < FB; ++fb) R[fb] = zero16();
-#pragma unroll
-    for (int c = 0; c < ZB; ++c) Zr[c] = zero16();
+    for (int i = 0; i < FBW; ++i) R[i] = zero16();
 
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
     constexpr int NV = RawTile<D, NT, kCc>::NV, V8 = D / 8;
@@ -287,7 +289,7 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(1))) void
 #pragma unroll
             for (int s = 0; s < kCc / 16; ++s) {
                 const int k0 = 16 * s + 8 * h;
-                const bf16x8 gb = tr8(tr_addr<TD>(sG, k0, 32 * w), tr_addr<TD>(sG, k0 + 4, 32 * w));
+                const bf16x8 gb = tr8(tr_addr<TD>(sG, k0, 32 * vb), tr_addr<TD>(sG, k0 + 4, 32 * vb));
                 const float4 c_lo = *reinterpret_cast<const float4 *>(sC + k0);
                 const float4 c_hi = *reinterpret_cast<const float4 *>(sC + k0 + 4);
                 const float cr[8] = {c_lo.x, c_lo.y, c_lo.z, c_lo.w, c_hi.x, c_hi.y, c_hi.z, c_hi.w};
@@ -295,24 +297,24 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(1))) void
 #pragma unroll
                 for (int e = 0; e < 8; ++e) cb[e] = (__bf16)cr[e];
 #pragma unroll
-                for (int fb = 0; fb < FB; ++fb) {
+                for (int i = 0; i < FBW; ++i) {
+                    const int fb = FBW * fh + i;
                     const bf16x8 qa = tr8(tr_addr<TF>(sQ, k0, 32 * fb), tr_addr<TF>(sQ, k0 + 4, 32 * fb));
-                    R[fb] = mfma(qa, gb, R[fb]);
-                    if (fb % NW == w) Zr[fb / NW] = mfma(qa, cb, Zr[fb / NW]);
+                    R[i] = mfma(qa, gb, R[i]);
+                    if (i == vb) Zr = mfma(qa, cb, Zr);   // feature block w = FBW * fh + vb
                 }
             }
         }
     }
     float *Ro = a.ws_Rp + ((size_t)bg * a.nseg + seg) * ((size_t)F * D + F);
 #pragma unroll
-    for (int fb = 0; fb < FB; ++fb)
+    for (int i = 0; i < FBW; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) Ro[(size_t)(32 * fb + acc_row(r, h)) * D + 32 * w + l32] = R[fb][r];
+        for (int r = 0; r < 16; ++r)
+            Ro[(size_t)(32 * (FBW * fh + i) + acc_row(r, h)) * D + 32 * vb + l32] = R[i][r];
     if (l32 == 0) {
 #pragma unroll
-        for (int c = 0; c < ZB; ++c)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) Ro[(size_t)F * D + 32 * (w + NW * c) + acc_row(r, h)] = Zr[c][r];
+        for (int r = 0; r < 16; ++r) Ro[(size_t)F * D + 32 * w + acc_row(r, h)] = Zr[r];
     }
 }
 
@@ -568,7 +570,7 @@ hipError_t run(const Args &a, hipStream_t s) {
     }
     {
         TimedLaunch tl("k_bwd_r_cos_mfma", s);
-        hipLaunchKernelGGL((k_bwd_r_cos_mfma<D, PHI>), dim3(n_units * a.nseg), dim3(2 * D), 0, s, a);
+        hipLaunchKernelGGL((k_bwd_r_cos_mfma<D, PHI>), dim3(n_units * a.nseg), dim3(4 * D), 0, s, a);
     }
     {
         TimedLaunch tl("k_scan_R", s);
