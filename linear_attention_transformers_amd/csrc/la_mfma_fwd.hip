@@ -42,12 +42,13 @@ struct FwdTiles {
 };
 
 // S += Phi(K)^T V over the 64 rows of the staged chunk for one wave's tiles:
-// value block vb and feature blocks FBW*fh .. FBW*fh + FBW-1 (natural k order:
-// lane half h holds rows 16s + 8h .. +7), and z += Phi(K)^T 1 for the feature
-// blocks fb = w (mod ZW) into Z[fb / ZW].
-template <int D, int F, int FBW, int ZW>
+// value block vb and feature blocks FBW*fh + i, i < FBW (natural k order:
+// lane half h holds rows 16s + 8h .. +7), and z += Phi(K)^T 1 for the blocks
+// i = vb (mod D/32) of that set into Z[i / (D/32)].
+template <int D, int F, int FBW>
 __device__ __forceinline__ void state_update(f32x16 *S, f32x16 *Z, const u16 *sK, const u16 *sV,
-                                             int w, int vb, int fh) {
+                                             int vb, int fh) {
+    constexpr int NW = D / 32;
     using TF = typename FwdTiles<D, F>::TF;
     using TD = typename FwdTiles<D, F>::TD;
     const int h = (threadIdx.x & 63) >> 5;
@@ -61,7 +62,7 @@ __device__ __forceinline__ void state_update(f32x16 *S, f32x16 *Z, const u16 *sK
             const int fb = FBW * fh + i;
             const bf16x8 ka = tr8(tr_addr<TF>(sK, k0, 32 * fb), tr_addr<TF>(sK, k0 + 4, 32 * fb));
             S[i] = mfma(ka, vo, S[i]);
-            if (fb % ZW == w) Z[fb / ZW] = mfma(ka, one, Z[fb / ZW]);
+            if (i % NW == vb) Z[i / NW] = mfma(ka, one, Z[i / NW]);
         }
     }
 }
@@ -71,10 +72,10 @@ __device__ __forceinline__ void state_update(f32x16 *S, f32x16 *Z, const u16 *sK
 // dS = sum_j Phi(k_j) v_j^T (F x D) and dz = sum_j Phi(k_j), written as fp32
 // to the workspace record of the segment.  The next chunk's loads are issued
 // before the current chunk's products.  NH wave sets of D/32 waves split the
-// feature blocks: wave w owns value block w % (D/32) and feature half
-// w / (D/32) (the tiles are disjoint, so nothing crosses waves).  At F = 256
-// two sets keep 64 accumulator registers per lane instead of 128, and two
-// waves share a SIMD instead of one.
+// feature blocks: wave w owns value block w % (D/32) and the feature blocks
+// of set w / (D/32) (the tiles are disjoint, so nothing crosses waves).  At
+// F = 256 two sets keep 64 accumulator registers per lane instead of 128, and
+// two waves share a SIMD instead of one.
 // ---------------------------------------------------------------------------
 // Occupancy the state pass is built for: it streams K and V, so more waves
 // per SIMD hide more load latency (each shape's registers allow this).
@@ -88,8 +89,8 @@ __global__ __launch_bounds__((D * 2 * state_sets<D, F>())) __attribute__((amdgpu
     using TF = typename FwdTiles<D, F>::TF;
     using TD = typename FwdTiles<D, F>::TD;
     constexpr int NH = state_sets<D, F>(), NW = D / 32, NT = D * 2 * NH;
-    constexpr int FBW = F / 32 / NH, ZW = NW * NH, ZB = F / 32 / ZW;
-    static_assert(FBW * NH * 32 == F && ZB * ZW * 32 == F, "feature blocks split evenly");
+    constexpr int FBW = F / 32 / NH, ZB = (FBW + NW - 1) / NW;   // z tiles per wave (at most)
+    static_assert(FBW * NH * 32 == F, "feature blocks split evenly");
     __shared__ __attribute__((aligned(16))) u16 sK[kC * TF::ld];
     __shared__ __attribute__((aligned(16))) u16 sV[kC * TD::ld];
     const int seg = blockIdx.x % nseg_run, bg = blockIdx.x / nseg_run;   // segments 0 .. nseg_run-1
@@ -114,7 +115,7 @@ __global__ __launch_bounds__((D * 2 * state_sets<D, F>())) __attribute__((amdgpu
         __syncthreads();
         rK.load(kh, c0 + kC, a.N);   // next chunk (past the segment: unused)
         rV.load(vh, c0 + kC, a.N);
-        state_update<D, F, FBW, ZW>(S, Z, sK, sV, w, vb, fh);
+        state_update<D, F, FBW>(S, Z, sK, sV, vb, fh);
     }
     float *out = a.ws_S + ((size_t)bg * (a.nseg + 1) + seg) * ((size_t)F * D + F);
 #pragma unroll
@@ -125,12 +126,15 @@ __global__ __launch_bounds__((D * 2 * state_sets<D, F>())) __attribute__((amdgpu
             out[(size_t)f * D + 32 * vb + l32] = S[i][r];
         }
     // every column of a z tile holds z: lane 0 of each half writes its rows
+    // (z tile c is block i = vb + (D/32) c of this wave's set, if it exists)
     if (l32 == 0) {
 #pragma unroll
         for (int c = 0; c < ZB; ++c)
+            if (vb + NW * c < FBW) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                out[(size_t)F * D + 32 * (w + ZW * c) + acc_row(r, h)] = Z[c][r];
+                for (int r = 0; r < 16; ++r)
+                    out[(size_t)F * D + 32 * (FBW * fh + vb + NW * c) + acc_row(r, h)] = Z[c][r];
+            }
     }
 }
 
