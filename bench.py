@@ -60,7 +60,8 @@ def kernel_bytes(name, w, s):
         "bwd_r": 2 * qb + 2 * rows,                       # q, g, den, c (per-segment R, r)
     }
     # matrix-core kernels compute the same parts of the method
-    alias = {"k_state_mfma": "state", "k_fwd_mfma": "fwd_causal", "k_bwd_q_mfma": "bwd_q_causal",
+    alias = {"k_state_mfma": "state", "k_fwd_mfma": "fwd_causal", "k_fwd_split_mfma": "fwd_causal",
+             "k_bwd_q_mfma": "bwd_q_causal",
              "k_bwd_kv_mfma": "bwd_kv_causal", "k_fwd_bidir_mfma": "fwd_bidir",
              "k_bwd_q_bidir_mfma": "bwd_q_bidir", "k_bwd_kv_bidir_mfma": "bwd_kv_bidir",
              "k_bwd_q_cos_mfma": "bwd_q_causal", "k_bwd_r_cos_mfma": "bwd_r",
