@@ -38,10 +38,12 @@ __device__ __forceinline__ float phi_d_raw(float x) {
 // ---------------------------------------------------------------------------
 // k_bwd_q_cos_mfma: forward over the 32-row chunks of one (batch, KV head,
 // segment) for the n_rep query heads.  Wave w (of F/32) holds S^T for
-// feature block w (all value blocks) and z of that block; it forms A^T, T^T
-// (A over all F features), U = S g for its block, dPhi(q) for its block,
-// and the waves of the sin half pass cos/sin-weighted tiles to those of the
-// cos half, which apply phi' and store dq.  Writes den_i and c_i.
+// feature block w (all value blocks) and z of that block; it forms U = S g
+// for its block and dPhi(q) for its block, and the waves of the sin half
+// pass cos/sin-weighted tiles to those of the cos half, which apply phi' and
+// store dq.  Wave 0 forms A^T (over all F features) and wave 1 T^T for the
+// whole workgroup; they reach every wave through LDS with the Phi(q).U
+// partials.  Writes den_i and c_i.
 // ---------------------------------------------------------------------------
 template <int D, int PHI>
 __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2)))
@@ -56,6 +58,7 @@ void k_bwd_q_cos_mfma(Args a) {
     __shared__ __attribute__((aligned(16))) u16 sG[kCc * TD::ld];
     __shared__ __attribute__((aligned(16))) float sz[F];
     __shared__ __attribute__((aligned(16))) float sX[NW][64 * 16];   // sin halves of dPhi(q)
+    __shared__ __attribute__((aligned(16))) float sAt[64 * 16], sTt[64 * 16];   // A^T, T^T tiles
     __shared__ float sQZ[kCc], sQU[FW][kCc];
 
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
@@ -120,24 +123,21 @@ void k_bwd_q_cos_mfma(Args a) {
             }
             const bool ok = c0 + l32 < a.N;   // this lane's query row exists
 
-            // A^T over the F features (the cos/sin weighting included), T^T
-            f32x16 At = zero16(), Tt = zero16();
+            // A^T over the F features (the cos/sin weighting included) on wave
+            // 0, T^T on wave 1, for every wave after the barrier below
+            if (w == 0) {
+                f32x16 At = zero16();
 #pragma unroll 4
-            for (int s = 0; s < F / 16; ++s)
-                At = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), At);
+                for (int s = 0; s < F / 16; ++s)
+                    At = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), At);
+                put_acc(sAt, At);
+            } else if (w == 1) {
+                f32x16 Tt = zero16();
 #pragma unroll 4
-            for (int s = 0; s < D / 16; ++s)
-                Tt = mfma(ld8<TD>(sV, l32, 16 * s + 8 * h), ld8<TD>(sG, l32, 16 * s + 8 * h), Tt);
-            float dA = 0.f, aT = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float x = acc_row(r, h) <= l32 ? (float)(__bf16)At[r] : 0.f;   // the forward's A
-                dA += x;
-                aT += x * Tt[r];
+                for (int s = 0; s < D / 16; ++s)
+                    Tt = mfma(ld8<TD>(sV, l32, 16 * s + 8 * h), ld8<TD>(sG, l32, 16 * s + 8 * h), Tt);
+                put_acc(sTt, Tt);
             }
-            dA = sum_halves(dA);
-            aT = sum_halves(aT);
-            const float den = ok ? dA + sQZ[l32] + a.eps : 1.f;
             // U^T = S g (feature block w x the chunk's queries), Phi(q).U over the block
             f32x16 U = zero16();
 #pragma unroll
@@ -157,6 +157,20 @@ void k_bwd_q_cos_mfma(Args a) {
             if (h == 0) sQU[w][l32] = qu;
             __syncthreads();
 
+            f32x16 Tt = get_acc(sTt);
+            float dA = 0.f, aT = 0.f;
+            {
+                const f32x16 At = get_acc(sAt);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float x = acc_row(r, h) <= l32 ? (float)(__bf16)At[r] : 0.f;   // the forward's A
+                    dA += x;
+                    aT += x * Tt[r];
+                }
+            }
+            dA = sum_halves(dA);
+            aT = sum_halves(aT);
+            const float den = ok ? dA + sQZ[l32] + a.eps : 1.f;
             float gsum = aT;
 #pragma unroll
             for (int ww = 0; ww < FW; ++ww) gsum += sQU[ww][l32];
