@@ -336,8 +336,11 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void
 // k_bwd_kv_cos_mfma: backward over the 32-row chunks of one (batch, KV head,
 // segment) from the exclusive suffix (R, r).  Wave w (of F/32) holds R^T for
 // feature block w and forms dPhi(k) of that block; waves w < D/32 also form
-// dv for value block w.  The sin-half waves pass their weighted dPhi(k)
-// tiles to the cos-half waves, which apply phi' and stage dk.
+// dv for value block w.  Per head, wave 0 forms the masked A tile and wave 1
+// the P tile for the whole workgroup, as bf16 operands passed through LDS
+// (each lane's registers to its own slot).  The sin-half waves pass their
+// weighted dPhi(k) tiles to the cos-half waves, which apply phi' and stage
+// dk.
 // ---------------------------------------------------------------------------
 template <int D, int PHI>
 __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2)))
@@ -354,6 +357,7 @@ void k_bwd_kv_cos_mfma(Args a) {
     __shared__ __attribute__((aligned(16))) u16 sGr[kCc * TD::ld];   // raw g rows (for P)
     __shared__ __attribute__((aligned(16))) float sCc[kCc], sIq[kCc];   // c_i, 1 / den_i
     __shared__ float sr[F];
+    __shared__ bf16x8 sAop[2][64], sPop[2][64];   // A, P operands of one head, per lane
     static_assert(sizeof(sQ) >= NW * 64 * 16 * sizeof(float), "sQ holds the sin-half tiles");
 
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
@@ -476,21 +480,20 @@ void k_bwd_kv_cos_mfma(Args a) {
                 rG.load(gbase + hn * a.N * D, cq, a.N);
                 load_dc(hn, cq);
             }
-            // A = Phi(Q) Phi(K)^T (over F) and P = (G V^T) / den - c (queries x keys),
-            // i >= j; P from the raw g rows scaled in fp32 (it can be a small
+            // A = Phi(Q) Phi(K)^T (over F) on wave 0 and P = (G V^T) / den - c on
+            // wave 1 (queries x keys, i >= j), as bf16 operands for every wave;
+            // P from the raw g rows scaled in fp32 (it can be a small
             // difference, which bf16-rounded gn would not resolve)
-            bf16x8 Aop[2], Pop[2];
-            {
+            if (w == 0) {
                 f32x16 A = zero16();
 #pragma unroll 4
                 for (int s = 0; s < F / 16; ++s)
                     A = mfma(ld8<TF>(sQ, l32, 16 * s + 8 * h), ld8<TF>(sK, l32, 16 * s + 8 * h), A);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) A[r] = acc_row(r, h) >= l32 ? A[r] : 0.f;
-                Aop[0] = acc_op(A, 0);
-                Aop[1] = acc_op(A, 1);
-            }
-            {
+                sAop[0][l] = acc_op(A, 0);
+                sAop[1][l] = acc_op(A, 1);
+            } else if (w == 1) {
                 f32x16 P = zero16();
 #pragma unroll 4
                 for (int s = 0; s < D / 16; ++s)
@@ -506,18 +509,11 @@ void k_bwd_kv_cos_mfma(Args a) {
                         P[r] = acc_row(r, h) >= l32 ? P[r] * ir[e] - cr[e] : 0.f;
                     }
                 }
-                Pop[0] = acc_op(P, 0);
-                Pop[1] = acc_op(P, 1);
+                sPop[0][l] = acc_op(P, 0);
+                sPop[1][l] = acc_op(P, 1);
             }
-            // in-chunk terms: dPhi(k)^T += Phi(Q)^T P (block w), dv^T += gn^T A (value block w)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int k0 = 16 * s + 4 * h;
-                dK = mfma(tr8(tr_addr<TF>(sQ, k0, 32 * w), tr_addr<TF>(sQ, k0 + 8, 32 * w)), Pop[s], dK);
-                if (w < NW)
-                    dV = mfma(tr8(tr_addr<TD>(sG, k0, 32 * w), tr_addr<TD>(sG, k0 + 8, 32 * w)), Aop[s], dV);
-            }
-            // R^T += gn^T Phi(Q) for this chunk's rows; r += Phi(Q)^T c
+            // R^T += gn^T Phi(Q) for this chunk's rows; r += Phi(Q)^T c (neither
+            // needs A or P)
 #pragma unroll
             for (int s = 0; s < kCc / 16; ++s) {
                 const int k0 = 16 * s + 8 * h;
@@ -540,6 +536,15 @@ void k_bwd_kv_cos_mfma(Args a) {
                 }
                 acc = sum_halves(acc);
                 if (h == 0) sr[32 * w + l32] += acc;
+            }
+            __syncthreads();   // the A and P operands are in LDS
+            // in-chunk terms: dPhi(k)^T += Phi(Q)^T P (block w), dv^T += gn^T A (value block w)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int k0 = 16 * s + 4 * h;
+                dK = mfma(tr8(tr_addr<TF>(sQ, k0, 32 * w), tr_addr<TF>(sQ, k0 + 8, 32 * w)), sPop[s][l], dK);
+                if (w < NW)
+                    dV = mfma(tr8(tr_addr<TD>(sG, k0, 32 * w), tr_addr<TD>(sG, k0 + 8, 32 * w)), sAop[s][l], dV);
             }
         }
         // chain rule through cos/sin: the sin-half waves hand sin_j dPhi(k) to
