@@ -13,10 +13,13 @@ pytestmark = pytest.mark.gpu
 
 # dtype, D, causal, cos, H, H_kv, N, seg_len: the matrix-core causal,
 # bidirectional and cos/sin-GQA paths and the float32 / D = 32 kernels, with
-# and without forced segments
+# and without forced segments.  The last case runs its forward on the matrix
+# cores and its backward on the float32 kernels (bf16 bidirectional cos/sin),
+# whose automatic segmentations differ there (43 and 32 segments).
 CASES = [("bf16", 128, True, False, 4, 2, 200, 0), ("bf16", 128, True, False, 4, 2, 200, 64),
          ("bf16", 64, False, False, 4, 4, 150, 64), ("bf16", 128, True, True, 4, 1, 150, 64),
-         ("f32", 64, True, False, 2, 1, 130, 64), ("bf16", 32, False, True, 2, 2, 100, 0)]
+         ("f32", 64, True, False, 2, 1, 130, 64), ("bf16", 32, False, True, 2, 2, 100, 0),
+         ("bf16", 64, False, True, 32, 32, 16384, 0)]
 
 
 def _id(c):
