@@ -32,6 +32,8 @@
 // reduction, Phi(q_i).U_i over the feature blocks, goes through LDS in a
 // fixed order.  In the q-kernel a second set of waves accumulates the
 // segment's (R, r) so the two register-heavy states live in different waves.
+#include <atomic>
+
 #include "la_common.h"
 #include "la_kernels.h"
 #include "la_mfma.h"
@@ -367,7 +369,11 @@ void k_bwd_q_mfma(Args a, int qm_arg) {
 // slow each other and more of them keeps it busier: one segment each.
 template <int D, int PHI, bool CAUSAL>
 int q_segments_per_wg(const Args &a, unsigned n_units) {
-    static int slots = 0;   // resident workgroups on the device (0: not yet asked)
+    // resident workgroups on the device (0: not yet asked; -1: more than one
+    // per compute unit).  Calls from several host threads may each ask; they
+    // store the same value.
+    static std::atomic<int> cached{0};
+    int slots = cached.load(std::memory_order_relaxed);
     if (slots == 0) {
         int dev = 0, cus = 0, per_cu = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
@@ -377,6 +383,7 @@ int q_segments_per_wg(const Args &a, unsigned n_units) {
             cus <= 0 || per_cu <= 0)
             return 1;
         slots = per_cu == 1 ? cus : -1;
+        cached.store(slots, std::memory_order_relaxed);
     }
     if (slots < 0) return 1;
     int best = 1;
