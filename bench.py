@@ -559,6 +559,16 @@ def main():
         "step_roofline": {"t_roof_ms": t_roof * 1e3, "frac": t_roof * 1e3 / ms_step,
                           "algorithmic_bytes": step_bytes, "algorithmic_flops": step_flops},
         "kernels_ms_per_step": {k: v[1] / args.steps for k, v in ktimes.items()},
+        # algorithmic bytes of each kernel (as for roofline.achieved) over its
+        # average launch time, and the step's algorithmic flops over the step
+        # time against the peak of the units that run them
+        "kernels_gbs": {k: kernel_bytes(k, w, s) / (v[1] / v[0] / 1e3) / 1e9
+                        for k, v in ktimes.items() if v[0] and kernel_bytes(k, w, s) is not None},
+        "matrix": {"achieved": step_flops / (ms_step / 1e3) / 1e12,
+                   "peak": BF16_PEAK_TFLOPS if matrix else FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                   "frac": step_flops / (ms_step / 1e3) / 1e12 /
+                           (BF16_PEAK_TFLOPS if matrix else FP32_PEAK_TFLOPS),
+                   "units": "bf16 matrix cores" if matrix else "fp32 vector ALU"},
         "bwd_recomputing_state": recompute,
         "cpu_baseline": None,
     }
