@@ -39,9 +39,9 @@ __device__ __forceinline__ float phi_d_raw(float x) {
 // k_bwd_q_cos_mfma: forward over the 32-row chunks of one (batch, KV head,
 // segment) for the n_rep query heads.  Wave w (of F/32) holds S^T for
 // feature block w (all value blocks) and z of that block; it forms U = S g
-// for its block and dPhi(q) for its block, and the waves of the sin half
-// pass cos/sin-weighted tiles to those of the cos half, which apply phi' and
-// store dq.  Wave 0 forms A^T (over all F features) and wave 1 T^T for the
+// for its block and dPhi(q) for its block, weighted by cos or sin and by
+// phi'; the waves of the sin half pass their terms to those of the cos half,
+// which add them and store dq after the next head's exchange barrier.  Wave 0 forms A^T (over all F features) and wave 1 T^T for the
 // whole workgroup; they reach every wave through LDS with the Phi(q).U
 // partials.  Writes den_i and c_i.
 // ---------------------------------------------------------------------------
@@ -57,7 +57,7 @@ void k_bwd_q_cos_mfma(Args a) {
     __shared__ __attribute__((aligned(16))) u16 sQr[kCc * TD::ld];   // raw q rows, for phi'
     __shared__ __attribute__((aligned(16))) u16 sG[kCc * TD::ld];
     __shared__ __attribute__((aligned(16))) float sz[F];
-    __shared__ __attribute__((aligned(16))) float sX[NW][64 * 16];   // sin halves of dPhi(q)
+    __shared__ __attribute__((aligned(16))) float sX[2][NW][64 * 16];   // sin halves' dq terms, by head parity
     __shared__ __attribute__((aligned(16))) float sAt[64 * 16], sTt[64 * 16];   // A^T, T^T tiles
     __shared__ float sQZ[kCc], sQU[FW][kCc];
 
@@ -84,6 +84,28 @@ void k_bwd_q_cos_mfma(Args a) {
     for (int r = 0; r < 16; ++r) Z[r] = Sp[(size_t)F * D + 32 * w + acc_row(r, h)];
     for (int e = t; e < F; e += NT) sz[e] = Sp[(size_t)F * D + e];
     const bf16x8 one = ones8();
+
+    // The cos-half wave of dims 32w .. 32w+31 stores dq from its own term and
+    // the sin-half wave's (through sX) after the next head's exchange barrier,
+    // so no barrier of its own is needed: its pending term, rows and buffer
+    f32x16 Qp;
+    bool pend = false;
+    int pbuf = 0, prow = 0;
+    size_t pbh = 0;
+    auto store_pending = [&]() {
+        if (w < NW) {
+            const f32x16 Qs = get_acc(sX[pbuf][w]);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int d0 = 32 * w + 8 * q4 + 4 * h;
+                float o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = Qp[4 * q4 + e] + Qs[4 * q4 + e];
+                if (prow < a.N) st4bf(dqbase + pbh * a.N * D + (size_t)prow * D + d0, o);
+            }
+        }
+    };
+    int step = 0;   // (chunk, head) steps so far: sX buffer parity
 
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
     RawTile<D, NT, kCc> rK, rV, rQ, rG;
@@ -127,7 +149,7 @@ void k_bwd_q_cos_mfma(Args a) {
             // 0, T^T on wave 1, for every wave after the barrier below
             if (w == 0) {
                 f32x16 At = zero16();
-#pragma unroll 4
+#pragma unroll
                 for (int s = 0; s < F / 16; ++s)
                     At = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), At);
                 put_acc(sAt, At);
@@ -156,6 +178,7 @@ void k_bwd_q_cos_mfma(Args a) {
             qu = sum_halves(qu);
             if (h == 0) sQU[w][l32] = qu;
             __syncthreads();
+            if (pend) store_pending();   // the previous head's dq rows
 
             f32x16 Tt = get_acc(sTt);
             float dA = 0.f, aT = 0.f;
@@ -193,21 +216,23 @@ void k_bwd_q_cos_mfma(Args a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 Qd[r] = mq * (Qd[r] + U[r] * inv - sz[32 * w + acc_row(r, h)] * c);
-            if (w >= NW) put_acc(sX[w - NW], Qd);   // sin half, to the wave of the same dims
-            __syncthreads();
-            if (w < NW) {
-                const f32x16 Qs = get_acc(sX[w]);
-                const int row = c0 + l32;
+            // each half's term of dq = phi'(q) (cos dPhi(q)_cos + sin dPhi(q)_sin)
+            // for dims 32 (w mod D/32) ..: the sin half's goes through sX
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const int d0 = 32 * w + 8 * q4 + 4 * h;
-                    float qr[4], o[4];
-                    ld4f(sQr + TD::at(l32, d0), qr);
+            for (int q4 = 0; q4 < 4; ++q4) {
+                float qr[4];
+                ld4f(sQr + TD::at(l32, 32 * (w % NW) + 8 * q4 + 4 * h), qr);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = phi_d_raw<PHI>(qr[e]) * (Qd[4 * q4 + e] + Qs[4 * q4 + e]);
-                    if (row < a.N) st4bf(dqbase + bh * a.N * D + (size_t)row * D + d0, o);
-                }
+                for (int e = 0; e < 4; ++e) Qd[4 * q4 + e] *= phi_d_raw<PHI>(qr[e]);
             }
+            const int buf = step & 1;
+            if (w >= NW) put_acc(sX[buf][w - NW], Qd);
+            Qp = Qd;
+            pend = true;
+            pbuf = buf;
+            prow = c0 + l32;
+            pbh = bh;
+            ++step;
         }
         // carry (S^T, z) past this chunk
 #pragma unroll
@@ -227,6 +252,8 @@ void k_bwd_q_cos_mfma(Args a) {
             for (int r = 0; r < 16; ++r) sz[32 * w + acc_row(r, h)] = Z[r];
         }
     }
+    __syncthreads();   // the last head's sin terms are in sX
+    if (pend) store_pending();
 }
 
 // ---------------------------------------------------------------------------
