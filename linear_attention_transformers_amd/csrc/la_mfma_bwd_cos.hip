@@ -378,14 +378,14 @@ void k_bwd_kv_cos_mfma(Args a) {
     __shared__ __attribute__((aligned(16))) u16 sK[kCc * TF::ld];
     __shared__ __attribute__((aligned(16))) u16 sKr[kCc * TD::ld];   // raw k (phi'), then dk rows
     __shared__ __attribute__((aligned(16))) u16 sV[kCc * TD::ld];
-    __shared__ __attribute__((aligned(16))) u16 sQ[kCc * TF::ld];    // also the sin halves of dPhi(k)
+    __shared__ __attribute__((aligned(16))) u16 sQ[kCc * TF::ld];
+    __shared__ __attribute__((aligned(16))) float sX[NW][64 * 16];   // sin halves of dPhi(k)
     __shared__ __attribute__((aligned(16))) u16 sG[kCc * TD::ld];    // gn, then dv rows
     __shared__ __attribute__((aligned(16))) u16 sR[F * TD::ld];
     __shared__ __attribute__((aligned(16))) u16 sGr[kCc * TD::ld];   // raw g rows (for P)
     __shared__ __attribute__((aligned(16))) float sCc[kCc], sIq[kCc];   // c_i, 1 / den_i
     __shared__ float sr[F];
     __shared__ bf16x8 sAop[2][64], sPop[2][64];   // A, P operands of one head, per lane
-    static_assert(sizeof(sQ) >= NW * 64 * 16 * sizeof(float), "sQ holds the sin-half tiles");
 
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
@@ -398,7 +398,6 @@ void k_bwd_kv_cos_mfma(Args a) {
     const size_t bh0 = (size_t)b * a.H + (size_t)g * a.nrep;
     const u16 *qbase = static_cast<const u16 *>(a.q);
     const u16 *gbase = static_cast<const u16 *>(a.g);
-    float *sX = reinterpret_cast<float *>(sQ);
 
     const float *Rp = a.ws_Rs + ((size_t)bg * (a.nseg + 1) + seg) * SD;
     f32x16 Rt[NW];
@@ -575,16 +574,15 @@ void k_bwd_kv_cos_mfma(Args a) {
             }
         }
         // chain rule through cos/sin: the sin-half waves hand sin_j dPhi(k) to
-        // the cos-half wave of the same dims (in sQ, free after the last head)
+        // the cos-half wave of the same dims
         const int tj = min(c0 + l32, a.N - 1);
         const float mk = w < NW ? a.cw[tj] : a.sw[tj];   // this lane's key weight for block w
 #pragma unroll
         for (int r = 0; r < 16; ++r) dK[r] *= mk;
-        __syncthreads();   // every read of sQ (and sG) of the last head is done
-        if (w >= NW) put_acc(sX + (w - NW) * 64 * 16, dK);
-        __syncthreads();
+        if (w >= NW) put_acc(sX[w - NW], dK);
+        __syncthreads();   // sX complete; every read of sG of the last head is done
         if (w < NW) {
-            const f32x16 Ks = get_acc(sX + w * 64 * 16);
+            const f32x16 Ks = get_acc(sX[w]);
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int d0 = 32 * w + 8 * q4 + 4 * h;
