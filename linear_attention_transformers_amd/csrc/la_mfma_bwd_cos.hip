@@ -446,27 +446,6 @@ void k_bwd_kv_cos_mfma(Args a) {
                 for (int e = 0; e < 4; ++e) x[e] = Rt[db][4 * q4 + e];
                 st4bf(sR + TD::at(32 * w + l32, 32 * db + 8 * q4 + 4 * h), x);
             }
-        __syncthreads();
-
-        // state terms: dPhi(k)^T = R V^T - r (block w); dv^T = R^T Phi(K)^T (value block w)
-        f32x16 dK = zero16(), dV = zero16();
-#pragma unroll
-        for (int db = 0; db < NW; ++db)
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                dK = mfma(ld4x2<TD>(sR, 32 * w + l32, 32 * db + 16 * s + 4 * h),
-                          ld4x2<TD>(sV, l32, 32 * db + 16 * s + 4 * h), dK);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dK[r] -= sr[32 * w + acc_row(r, h)];
-        if (w < NW) {
-#pragma unroll 4
-            for (int s = 0; s < F / 16; ++s) {
-                const int k0 = 16 * s + 8 * h;
-                dV = mfma(tr8(tr_addr<TD>(sR, k0, 32 * w), tr_addr<TD>(sR, k0 + 4, 32 * w)),
-                          ld8<TF>(sK, l32, 16 * s + 8 * h), dV);
-            }
-        }
-
         // one head's query rows into LDS: Phi(Q), gn = g / den (rows past N:
         // zeros), raw g, c, 1 / den
         auto stage_head = [&]() {
@@ -488,16 +467,37 @@ void k_bwd_kv_cos_mfma(Args a) {
             }
             rG.template store<TD>(sGr);
         };
-        // the first head is staged in straight-line code (in the head loop, the
-        // wait for its rows would also wait for the K, V loads just issued)
-        __syncthreads();   // the state terms' LDS reads (and of r) are done
+        // the first head is staged here, in straight-line code, with the chunk
+        // (in the head loop, the wait for its rows would also wait for the K, V
+        // loads just issued); the state terms read none of its tiles
         stage_head();
+        __syncthreads();
+
+        // state terms: dPhi(k)^T = R V^T - r (block w); dv^T = R^T Phi(K)^T (value block w)
+        f32x16 dK = zero16(), dV = zero16();
+#pragma unroll
+        for (int db = 0; db < NW; ++db)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                dK = mfma(ld4x2<TD>(sR, 32 * w + l32, 32 * db + 16 * s + 4 * h),
+                          ld4x2<TD>(sV, l32, 32 * db + 16 * s + 4 * h), dK);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dK[r] -= sr[32 * w + acc_row(r, h)];
+        if (w < NW) {
+#pragma unroll 4
+            for (int s = 0; s < F / 16; ++s) {
+                const int k0 = 16 * s + 8 * h;
+                dV = mfma(tr8(tr_addr<TD>(sR, k0, 32 * w), tr_addr<TD>(sR, k0 + 4, 32 * w)),
+                          ld8<TF>(sK, l32, 16 * s + 8 * h), dV);
+            }
+        }
+
         for (int rep = 0; rep < a.nrep; ++rep) {
             if (rep > 0) {
                 __syncthreads();   // the previous head's LDS reads are done
                 stage_head();
+                __syncthreads();
             }
-            __syncthreads();
             {   // Q, G, den, c of the next head, or of the first head at the next chunk
                 const bool last = rep + 1 == a.nrep;
                 const size_t hn = bh0 + (last ? 0 : rep + 1);
