@@ -292,8 +292,8 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
 // accumulator registers per lane, which leaves one wave per SIMD; split, each
 // wave holds F/64 tiles and two waves share a SIMD.  Wave w owns value block
 // w % (D/32) and the feature blocks of half w / (D/32) (its z block is
-// feature block w).  Every wave forms the chunk's masked A tile over all F
-// features itself; the second half's partial numerators reach the first half
+// feature block w).  The first half forms the chunk's masked A tile over all
+// F features; the second half's partial numerators reach the first half
 // through LDS, which then normalises and stages the output rows.
 // ---------------------------------------------------------------------------
 template <int D, int F, int PHI, bool COS>
