@@ -130,9 +130,12 @@ __device__ uint16_t Lanes<true, uint16_t>::narrow(const double *x) { return (uin
 
 // grid: x = unit block within the slab, y = b * H_kv + g, z = tensor.  The
 // n_rep source units of a thread's outputs are loaded in batches of kRB (all
-// loads of a batch in flight together), then added in head order.
+// loads of a batch in flight together), then added in head order.  Four
+// outputs per thread: 0.240 ms per reduce at B=1, H=32, H_kv=8, N=65536,
+// D=128, against 0.269 with one, 0.251 with two and 0.347 with eight (whose
+// 256 registers per lane leave one wave per SIMD).
 constexpr int kRB = 4;
-constexpr int kPerThreadR = 2;
+constexpr int kPerThreadR = 4;
 constexpr long long kUnitsPerBlockR = (long long)kThreads * kPerThreadR;
 template <bool BF16, class U>
 __global__ __launch_bounds__(kThreads) void k_gqa_reduce(const U *__restrict__ gk, const U *__restrict__ gv,
