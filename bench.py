@@ -2,22 +2,27 @@
 """Benchmark: one step = forward + backward of fused feature-map linear
 attention over one batch of seeded synthetic input, on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K=50] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K=30] [--warmup W] [--workload NAME]
+                    [--dtype bf16|f32] [--mode causal|bidir] [--no-flush]
 
 NAME is an attention workload of seeded_inputs.WORKLOADS, the materialised
 GQA op (seeded_inputs.GQA_OPS: expand + reduce per step) or the low-rank
-projection (seeded_inputs.LOWRANK_OPS: fwd + bwd per step).
+projection (seeded_inputs.LOWRANK_OPS: fwd + bwd per step); --dtype / --mode
+pick among a workload's storage types and modes (default: its first).
 
 Default workload: causal, bf16 storage, B=2, H=32, N=16384, D=128, elu+1,
 eps=1e-6 (q, k, v ~ 0.5 N(0,1), grad_out ~ N(0,1), seed 0).  Inputs, outputs
-and workspaces are resident in HBM before timing; W untimed steps (default:
-as many as fill 0.5 s), then K timed steps between device synchronisations.  The forward and the backward of
-a step share one workspace, so the backward reuses the forward's state records
-(la_bwd_saved, as the autograd form does); the rate with the backward
-recomputing them (la_bwd) is reported beside.  One JSON line on stdout:
-throughput (tokens/s), the dominant kernel against its roofline (timed with
-HIP events on the library's own stream), and the CPU oracle's throughput on a
-bounded sample of the same workload.
+and workspaces are resident in HBM before timing.  W untimed steps (default: as
+many as fill 0.5 s), then K timed steps, each preceded (outside its timing) by
+a read of a 1 GiB buffer that evicts the L2 and last-level caches, and each
+bracketed by a pair of HIP events on the stream the library launches on; the
+K steps are bracketed by device synchronisations.  value = tokens / median
+step time.  Further passes of K flushed steps give the per-kernel breakdown
+(the library's own launch events), the forward alone (la_fwd, the north-star
+quantity) and the step with the backward recomputing the state (la_bwd).  The
+forward and the backward of a step share one workspace, so the backward reuses
+the forward's state records (la_bwd_saved, as the autograd form does).  One
+JSON line on stdout.
 """
 from __future__ import annotations
 
@@ -104,6 +109,15 @@ def measured_traffic(workload, kernel):
     return (fetch * scale[0] + write * scale[1]) * 1024.0
 
 
+def traffic_key(name, dtype, mode):
+    """Name of the counter summary of a workload variant (profiles/counters_<key>.md)."""
+    import seeded_inputs as si
+    w = si.WORKLOADS[name]
+    if dtype == w.dtypes[0] and mode == w.modes[0]:
+        return name
+    return "%s_%s_%s" % (name, dtype, mode)
+
+
 def step_roofline(w, s, causal):
     """Time of one step (fwd+bwd, or fwd for a forward-only workload) at the
     roofline: algorithmic bytes at HBM peak
@@ -122,7 +136,7 @@ def step_roofline(w, s, causal):
     return max(t_bytes, t_flops), fwd_bytes + bwd_bytes, fwd_flops + bwd_flops
 
 
-def cpu_baseline(w, tensors, budget_heads=None, min_seconds=10.0):
+def cpu_baseline(w, tensors, causal, budget_heads=None, min_seconds=10.0):
     """The CPU oracle, as it is, on whole (batch, KV head) groups at full N,
     fwd + bwd; throughput scaled to the whole workload by group count."""
     import numpy as np
@@ -146,7 +160,6 @@ def cpu_baseline(w, tensors, budget_heads=None, min_seconds=10.0):
     cw = sw = None
     if tensors.get("cos_weight") is not None:
         cw, sw = si.exact_f64(tensors["cos_weight"]), si.exact_f64(tensors["sin_weight"])
-    causal = "causal" in w.modes
     kw = dict(is_causal=causal, phi=w.phi, eps=w.eps, cos_weight=cw, sin_weight=sw)
     # repeat the sample until about min_seconds of oracle time have passed
     reps, total = 0, 0.0
@@ -163,6 +176,7 @@ def cpu_baseline(w, tensors, budget_heads=None, min_seconds=10.0):
         "value": w.B * w.N / t_full,
         "unit": "tokens/s",
         "cores": min(threads, take * nrep),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": "%d of %d (batch, KV head) groups (%d query heads each) at full N=%d, "
                   "%s in fp64, mean of %d runs (%.1f s in all); scaled by group count"
@@ -248,31 +262,33 @@ def bench_gqa(args, name):
             step()
     torch.cuda.synchronize()
     log("bench: %d warmup steps done; %d timed steps" % (args.warmup, args.steps))
+    flush = None if args.no_flush else Flusher(torch.device("cuda:0"))
+    step_ms, wall = timed_steps(step, args.steps, flush)
+    st = stats(step_ms)
     la.timing_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    la.timing_enable(False)
+    try:
+        timed_steps(step, args.steps, flush)
+    finally:
+        la.timing_enable(False)
     ktimes = la.timing_collect()
     kvb, qb = B * Hkv * N * D * s, B * H * N * D * s
     per_launch = {"k_gqa_expand": 2 * kvb + 2 * qb, "k_gqa_reduce": 2 * qb + 2 * kvb}
     dom_name, (launches, total_ms) = max(ktimes.items(), key=lambda kv: kv[1][1])
     avg_s = total_ms / launches / 1e3
     nbytes = per_launch[dom_name]
-    ms_step = elapsed * 1e3 / args.steps
+    ms_step = st["median_ms"]
     step_bytes = sum(per_launch.values())
     t_roof = step_bytes / (HBM_PEAK_GBS * 1e9)
     result = {
         "metric": "GQA expand+reduce tokens/sec and %% roofline, %s" % name,
-        "value": B * N * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1,
+        "value": B * N / (ms_step / 1e3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": c["dtype"], "data": "synthetic",
         "config": {"workload": name, "B": B, "H": H, "H_kv": Hkv, "N": N, "D": D,
                    "storage": c["dtype"], "pass": "expand (k, v) + reduce (grad_k, grad_v)"},
+        "timing": dict(st, basis="median of per-step HIP events", flushed=flush is not None,
+                       wall_s_incl_flushes=wall),
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": nbytes / avg_s / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": nbytes / avg_s / 1e9 / HBM_PEAK_GBS,
                      "traffic": measured_traffic(name, dom_name), "avg_launch_ms": avg_s * 1e3,
@@ -361,14 +377,14 @@ def bench_lowrank(args, name):
             step()
     torch.cuda.synchronize()
     log("bench: %d warmup steps done; %d timed steps" % (args.warmup, args.steps))
+    flush = None if args.no_flush else Flusher(torch.device("cuda:0"))
+    step_ms, wall = timed_steps(step, args.steps, flush)
+    st = stats(step_ms)
     la.timing_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    la.timing_enable(False)
+    try:
+        timed_steps(step, args.steps, flush)
+    finally:
+        la.timing_enable(False)
     ktimes = la.timing_collect()
     mnk = 2.0 * M * rank   # flops of one product per unit of its third size
     flops = {"k_lowrank_gemm_xVt": mnk * n_in, "k_lowrank_gemm_tUt": mnk * n_out,
@@ -377,19 +393,21 @@ def bench_lowrank(args, name):
     gemms = {k: v for k, v in ktimes.items() if k in flops}
     dom_name, (launches, total_ms) = max(gemms.items(), key=lambda kv: kv[1][1])
     avg_s = total_ms / launches / 1e3
-    ms_step = elapsed * 1e3 / args.steps
+    ms_step = st["median_ms"]
     step_flops = mnk * (n_in + n_out) + mnk * (n_in + 2 * n_out + 2 * n_in)   # fwd 2, bwd 5 products
     step_bytes = 2 * (2 * M * n_in + 2 * M * n_out + 2 * rank * (n_in + n_out) + 2 * n_out)   # x, y, g, gx, U, V, grads
     t_roof = max(step_flops / (BF16_PEAK_TFLOPS * 1e12), step_bytes / (HBM_PEAK_GBS * 1e9))
     ach = flops[dom_name] / avg_s / 1e12
     result = {
         "metric": "low-rank projection fwd+bwd tokens/sec and %% roofline, %s" % name,
-        "value": M * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1,
+        "value": M / (ms_step / 1e3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": name, "M": M, "n_in": n_in, "rank": rank, "n_out": n_out, "bias": True,
                    "storage": "bf16", "pass": "fwd + bwd (bwd recomputes t)"},
+        "timing": dict(st, basis="median of per-step HIP events", flushed=flush is not None,
+                       wall_s_incl_flushes=wall),
         "roofline": {"bound": "mfma", "kernel": dom_name, "achieved": ach, "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
                      "traffic": measured_traffic(name, dom_name), "avg_launch_ms": avg_s * 1e3,
@@ -405,16 +423,118 @@ def bench_lowrank(args, name):
     print(json.dumps(result), flush=True)
 
 
+class Flusher:
+    """Evicts the L2 and last-level caches between timed steps by reading a
+    1 GiB buffer (larger than both).  A read, not a write: the lines it leaves
+    are clean, whereas the dirty lines of a write would be written back inside
+    the next timed step (a 1 GiB write just before a 512 MiB streaming read
+    slowed that read by about 40% on the box).  Dirty output of the previous
+    step is written back during this read, outside the timed window."""
+
+    def __init__(self, dev, mib=1024):
+        import torch
+        self.buf = torch.zeros((mib << 20) // 4, dtype=torch.float32, device=dev)
+        self.out = torch.empty((), dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        import torch
+        torch.amax(self.buf, dim=0, out=self.out)
+
+
+def timed_steps(step, K, flush):
+    """Per-step times (ms) of K calls of step(), each bracketed by HIP events
+    on the current stream, each preceded by flush() (if given) outside the
+    events; the K steps are bracketed by device synchronisations."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        if flush is not None:
+            flush()
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [e0.elapsed_time(e1) for e0, e1 in evs], wall
+
+
+def stats(ms):
+    v = sorted(ms)
+    return {"median_ms": v[len(v) // 2], "min_ms": v[0], "mean_ms": sum(v) / len(v),
+            "max_ms": v[-1], "n": len(v)}
+
+
+def calibrate(dev, flush):
+    """Achievable peaks measured on this device (flushed, median of 5): a
+    512 MiB device copy (read + write bytes), a 1 GiB reduction (read bytes)
+    and a bf16 GEMM 8192^3 (the vendor library), beside the spec figures."""
+    import torch
+    src = torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    red = torch.zeros((1 << 30) // 4, dtype=torch.float32, device=dev)
+    o = torch.empty((), dtype=torch.float32, device=dev)
+    a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(8192, 8192, device=dev, dtype=torch.bfloat16)
+    for _ in range(2):
+        dst.copy_(src)
+        torch.amax(red, dim=0, out=o)
+        torch.matmul(a, b, out=c)
+    cp, _ = timed_steps(lambda: dst.copy_(src), 5, flush)
+    rd, _ = timed_steps(lambda: torch.amax(red, dim=0, out=o), 5, flush)
+    mm, _ = timed_steps(lambda: torch.matmul(a, b, out=c), 5, flush)
+    med = lambda x: sorted(x)[len(x) // 2] / 1e3
+    res = {"copy_gbs": 2 * src.numel() * 4 / med(cp) / 1e9,
+           "read_gbs": red.numel() * 4 / med(rd) / 1e9,
+           "bf16_gemm_tflops": 2 * 8192 ** 3 / med(mm) / 1e12,
+           "spec_hbm_gbs": HBM_PEAK_GBS, "spec_bf16_tflops": BF16_PEAK_TFLOPS,
+           "how": "flushed, median of 5: torch copy of 512 MiB (read+write bytes), "
+                  "torch amax over 1 GiB (read bytes), torch bf16 matmul 8192^3"}
+    del src, dst, red, a, b, c
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def fwd_roofline(w, s):
+    """Time of one la_fwd at the roofline: q, k, v read and out written once
+    at HBM peak vs the state reads and updates (2 F D per query token and per
+    key token) at the matrix peak."""
+    br = 2 if w.cos else 1
+    tokD = w.B * w.N * w.D
+    nbytes = s * tokD * (2 * w.H + 2 * w.Hkv) + (8 * w.N if w.cos else 0)
+    flops = br * 2 * w.D * w.D * w.B * w.N * (w.H + w.Hkv)
+    peak_f = BF16_PEAK_TFLOPS if s == 2 else FP32_PEAK_TFLOPS
+    return max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (peak_f * 1e12)), nbytes, flops
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=30)
     # default: as many steps as fill 0.5 s (at least 3): the GPU's clocks ramp
     # up over the first tenths of a second of load, and a short warm-up would
     # time the ramp; the count used is reported
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--dtype", default=None, choices=("bf16", "f32"))
+    ap.add_argument("--mode", default=None, choices=("causal", "bidir"))
+    ap.add_argument("--no-flush", action="store_true",
+                    help="time back-to-back steps with warm caches (for comparison)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-calibration", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before warmup, copy a buffer of this many MiB once (a plain "
                          "device copy of known size, to scale HBM byte counters)")
@@ -441,12 +561,16 @@ def main():
     if name in si.LOWRANK_OPS:
         return bench_lowrank(args, name)
     w = si.WORKLOADS[name]
-    dtype = w.dtypes[0]
-    causal = "causal" in w.modes
+    dtype = args.dtype or w.dtypes[0]
+    mode = args.mode or w.modes[0]
+    if dtype not in w.dtypes or mode not in w.modes:
+        print("workload %s has storage %s and modes %s" % (name, w.dtypes, w.modes), file=sys.stderr)
+        sys.exit(2)
+    causal = mode == "causal"
     s = 2 if dtype == "bf16" else 4
     dev = torch.device("cuda:0")
 
-    log("bench: drawing %s inputs" % name)
+    log("bench: drawing %s inputs (%s, %s)" % (name, dtype, mode))
     t = si.workload_inputs(w, dtype, dev)
     cw, sw = t["cos_weight"], t["sin_weight"]
     out = torch.empty_like(t["q"])
@@ -456,10 +580,14 @@ def main():
     # forward's state records (la_bwd_saved), as the autograd form does
     ws = torch.empty(la.workspace_bytes("bwd" if w.backward else "fwd", w.B, w.H, w.Hkv, w.N, w.D,
                                         code, causal, w.cos), dtype=torch.uint8, device=dev)
+    flush = None if args.no_flush else Flusher(dev)
 
-    def step(saved=True):
+    def fwd():
         la.fwd(t["q"], t["k"], t["v"], is_causal=causal, phi=w.phi, eps=w.eps, cos_weight=cw,
                sin_weight=sw, out=out, workspace=ws)
+
+    def step(saved=True):
+        fwd()
         if w.backward:
             la.bwd(t["q"], t["k"], t["v"], t["grad_out"], is_causal=causal, phi=w.phi,
                    eps=w.eps, cos_weight=cw, sin_weight=sw, workspace=ws, grads=grads,
@@ -489,28 +617,43 @@ def main():
     torch.cuda.synchronize()
     log("bench: %d warmup steps done" % args.warmup)
 
-    log("bench: %d timed steps" % args.steps)
+    # A: the headline: per-step events only
+    log("bench: %d timed steps%s" % (args.steps, "" if flush else " (no flush)"))
+    step_ms, wall = timed_steps(step, args.steps, flush)
+    st = stats(step_ms)
+    tokens = w.B * w.N
+    ms_step = st["median_ms"]
+    value = tokens / (ms_step / 1e3)
+
+    # B: per-kernel breakdown from the library's own launch events
+    log("bench: %d steps with per-kernel events" % args.steps)
     la.timing_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    la.timing_enable(False)
+    try:
+        timed_steps(step, args.steps, flush)
+    finally:
+        la.timing_enable(False)
     ktimes = la.timing_collect()
 
-    tokens = w.B * w.N
-    ms_step = elapsed * 1e3 / args.steps
-    value = tokens * args.steps / elapsed
+    # C: the forward alone
+    log("bench: %d forward-only steps" % args.steps)
+    fwd_ms, _ = timed_steps(fwd, args.steps, flush)
+    fst = stats(fwd_ms)
+    t_froof, f_bytes, f_flops = fwd_roofline(w, s)
 
-    # dominant kernel by total event time over the timed region
-    dom = max(ktimes.items(), key=lambda kv: kv[1][1])
-    dom_name, (launches, total_ms) = dom
+    # D: the backward computing the state records again (la_bwd)
+    recompute = None
+    if w.backward:
+        log("bench: %d steps with the backward recomputing the forward's state" % args.steps)
+        rms, _ = timed_steps(lambda: step(saved=False), args.steps, flush)
+        rst = stats(rms)
+        recompute = dict(rst, value=tokens / (rst["median_ms"] / 1e3), unit="tokens/s")
+
+    # dominant kernel by total event time over pass B
+    dom_name, (launches, total_ms) = max(ktimes.items(), key=lambda kv: kv[1][1])
     avg_s = total_ms / launches / 1e3
     nbytes = kernel_bytes(dom_name, w, s)
     roof = {"bound": "hbm", "kernel": dom_name, "achieved": None, "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": None, "traffic": measured_traffic(name, dom_name),
+            "unit": "GB/s", "frac": None, "traffic": measured_traffic(traffic_key(name, dtype, mode), dom_name),
             "avg_launch_ms": avg_s * 1e3, "algorithmic_bytes_per_launch": nbytes}
     if nbytes is not None:
         ach = nbytes / avg_s / 1e9
@@ -518,28 +661,20 @@ def main():
         roof["frac"] = ach / HBM_PEAK_GBS
     t_roof, step_bytes, step_flops = step_roofline(w, s, causal)
     matrix = any("mfma" in k for k in ktimes)
+    fwd_kernels = [k for k in ktimes if not (k.startswith("k_bwd") or k == "k_scan_R")]
 
-    recompute = None
-    if w.backward:
-        # the same step with the backward computing the state records again
-        # (la_bwd): the rate of a caller that does not keep the workspace
-        log("bench: %d steps with the backward recomputing the forward's state" % args.steps)
-        step(saved=False)
-        torch.cuda.synchronize()
-        la.timing_enable(True)   # timed like the main region (events on every launch)
-        t1 = time.perf_counter()
-        for _ in range(args.steps):
-            step(saved=False)
-        torch.cuda.synchronize()
-        el = time.perf_counter() - t1
-        la.timing_enable(False)
-        la.timing_collect()
-        recompute = {"ms_per_step": el * 1e3 / args.steps, "value": tokens * args.steps / el,
-                     "unit": "tokens/s"}
+    calib = None
+    if not args.no_calibration:
+        log("bench: calibration (copy, read, bf16 GEMM)")
+        calib = calibrate(dev, flush or Flusher(dev))
+        if roof["achieved"] is not None:
+            roof["frac_of_measured_copy"] = roof["achieved"] / calib["copy_gbs"]
 
     result = {
         "metric": ("fwd+bwd tokens/sec and % roofline, causal bf16 N=16384 D=128" if name == si.HEADLINE
-                   else "%s tokens/sec and %% roofline, %s" % ("fwd+bwd" if w.backward else "fwd", name)),
+                   and dtype == "bf16" and causal
+                   else "%s tokens/sec and %% roofline, %s %s %s" % (
+                       "fwd+bwd" if w.backward else "fwd", name, dtype, mode)),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -555,9 +690,15 @@ def main():
                    "phi": w.phi, "causal": causal, "cos_sin": w.cos, "storage": dtype,
                    "eps": w.eps, "pass": "fwd+bwd" if w.backward else "fwd",
                    "bwd_state": "saved by the forward (la_bwd_saved)" if w.backward else None},
+        "timing": dict(st, basis="median of per-step HIP events",
+                       flushed=flush is not None, wall_s_incl_flushes=wall),
         "roofline": roof,
         "step_roofline": {"t_roof_ms": t_roof * 1e3, "frac": t_roof * 1e3 / ms_step,
                           "algorithmic_bytes": step_bytes, "algorithmic_flops": step_flops},
+        "fwd_roofline": {"t_roof_ms": t_froof * 1e3, "ms": fst["median_ms"],
+                         "min_ms": fst["min_ms"], "frac": t_froof * 1e3 / fst["median_ms"],
+                         "algorithmic_bytes": f_bytes, "algorithmic_flops": f_flops,
+                         "kernels": fwd_kernels},
         "kernels_ms_per_step": {k: v[1] / args.steps for k, v in ktimes.items()},
         # algorithmic bytes of each kernel (as for roofline.achieved) over its
         # average launch time, and the step's algorithmic flops over the step
@@ -569,12 +710,13 @@ def main():
                    "frac": step_flops / (ms_step / 1e3) / 1e12 /
                            (BF16_PEAK_TFLOPS if matrix else FP32_PEAK_TFLOPS),
                    "units": "bf16 matrix cores" if matrix else "fp32 vector ALU"},
+        "calibration": calib,
         "bwd_recomputing_state": recompute,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")
-        result["cpu_baseline"] = cpu_baseline(w, t)
+        result["cpu_baseline"] = cpu_baseline(w, t, causal)
     print(json.dumps(result), flush=True)
 
 

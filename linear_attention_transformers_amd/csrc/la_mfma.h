@@ -117,7 +117,28 @@ __device__ __forceinline__ bf16x8 ones8() {
     return o;
 }
 
-// Registers 8s .. 8s+7 of an accumulator as a bf16 operand (round to nearest even).
+// Two floats rounded to bf16 (nearest even) and packed low, high into one
+// word: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pk2(float lo, float hi) {
+    bf16x2 v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Eight floats as a bf16 operand, converted in pairs (four v_cvt_pk_bf16_f32;
+// element-wise casts make the compiler convert one element per instruction
+// and merge the halves with permutes).
+__device__ __forceinline__ bf16x8 pack8(float x0, float x1, float x2, float x3, float x4,
+                                        float x5, float x6, float x7) {
+    const uint4 u = make_uint4(pk2(x0, x1), pk2(x2, x3), pk2(x4, x5), pk2(x6, x7));
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+// Registers 8s .. 8s+7 of an accumulator as a bf16 operand (round to nearest
+// even).  acc_op leaves the conversion to the compiler (which may convert one
+// element per instruction but keeps fewer registers live); acc_pk converts in
+// pairs (four instructions), for kernels that have the registers.
 __device__ __forceinline__ bf16x8 acc_op(const f32x16 &acc, int s) {
     bf16x8 o;
 #pragma unroll
@@ -125,24 +146,36 @@ __device__ __forceinline__ bf16x8 acc_op(const f32x16 &acc, int s) {
     return o;
 }
 
+__device__ __forceinline__ bf16x8 acc_pk(const f32x16 &acc, int s) {
+    const int b = 8 * s;
+    return pack8(acc[b], acc[b + 1], acc[b + 2], acc[b + 3], acc[b + 4], acc[b + 5], acc[b + 6],
+                 acc[b + 7]);
+}
+
 // The rounding remainders of acc_op: x - bf16(x) for registers 8s .. 8s+7,
 // rounded to bf16.  acc_op + acc_lo carry an fp32 accumulator to about 2^-16
 // relative, for products whose results are small differences.
 __device__ __forceinline__ bf16x8 acc_lo(const f32x16 &acc, int s) {
-    bf16x8 o;
+    float r[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float x = acc[8 * s + e];
-        o[e] = (__bf16)(x - (float)(__bf16)x);
+        r[e] = x - (float)(__bf16)x;
     }
-    return o;
+    return pack8(r[0], r[1], r[2], r[3], r[4], r[5], r[6], r[7]);
 }
 
 // phi for values that are rounded to bf16 right after: the hardware exp
-// (__expf, a few ulp) is far below bf16 resolution.
+// (v_exp_f32 of x log2(e), a few ulp) is far below bf16 resolution.  elu+1 is
+// taken as max(x + 1, 2^(-|x| log2 e)): for x > 0 the exponential is
+// e^-x < 1 < x + 1; for x <= 0 it is e^x >= 1 + x, so the maximum is e^x
+// except where the two agree to a few float32 ulp (|x| below about 2^-10),
+// far below bf16 resolution.  Four instructions instead of the six of the
+// branch form (the sign goes in as a source modifier; no compare or select).
 template <int PHI>
 __device__ __forceinline__ float phi_fast(float x) {
-    if constexpr (PHI == kElu1) return x > 0.f ? x + 1.f : __expf(x);
+    if constexpr (PHI == kElu1)
+        return __builtin_fmaxf(x + 1.f, __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * 1.44269504088896341f));
     else return phi_f<PHI>(x);
 }
 
@@ -186,15 +219,6 @@ __device__ __forceinline__ u16 f2bf(float x) {
     return __builtin_bit_cast(u16, b);
 }
 
-// Two floats rounded to bf16 (nearest even) and packed low, high into one
-// word: one v_cvt_pk_bf16_f32.
-__device__ __forceinline__ uint32_t pk2(float lo, float hi) {
-    bf16x2 v;
-    v[0] = (__bf16)lo;
-    v[1] = (__bf16)hi;
-    return __builtin_bit_cast(uint32_t, v);
-}
-
 // phi'(x) from the bf16 feature p = phi(x) of a bf16 input x.  relu: p > 0
 // exactly when x > 0; elu+1: p = x + 1 >= 1 for x > 0 and p = exp(x) <= 1
 // otherwise, so phi' = min(p, 1) (exp(x) to bf16 precision); identity: 1.
@@ -209,27 +233,58 @@ __device__ __forceinline__ float phi_d_feat(float p) {
 // 16-byte vectors (rows >= N read as zeros), so the global loads of the next
 // chunk can be in flight while the current one is computed.  Vector k of
 // thread t is element-row (t + k*NT) / (D/8), columns 8*((t + k*NT) % (D/8)).
-template <int D, int NT, int C = kC>
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte global load / store; STREAM marks data read or written once
+// (non-temporal: the caches keep it at low priority, so it does not push out
+// data that will be read again).
+template <bool STREAM>
+__device__ __forceinline__ uint4 gld16(const u16 *p) {
+    if constexpr (STREAM)
+        return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)));
+    else return *reinterpret_cast<const uint4 *>(p);
+}
+template <bool STREAM>
+__device__ __forceinline__ void gst16(u16 *p, uint4 x) {
+    if constexpr (STREAM)
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, x), reinterpret_cast<u32x4 *>(p));
+    else *reinterpret_cast<uint4 *>(p) = x;
+}
+
+template <int D, int NT, int C = kC, bool FAST = false, bool STREAM = false>
 struct RawTile {
     static constexpr int V8 = D / 8;
     static constexpr int NV = C * V8 / NT;
     static_assert(NV * NT == C * V8, "tile must split evenly over the threads");
     uint4 v[NV];
 
-    // One load per vector from a clamped (in-range) row, then rows >= N
-    // zeroed behind a uniform branch: a single straight path (N >= 1).
+    // FAST (for kernels with registers to spare), a whole tile in range: one
+    // 16-byte load per vector at a uniform base plus this thread's constant
+    // 32-bit offset (scalar base, no 64-bit address arithmetic per load).
+    // Otherwise: loads from clamped (in-range) rows, rows >= N then zeroed
+    // (N >= 1).
     __device__ __forceinline__ void load(const u16 *src, int c0, int N) {
+        if (FAST && c0 + C <= N) {
+            // vector k of thread t sits k * (NT / V8) rows below vector 0: the
+            // row step goes into the uniform base, the thread term is one
+            // 32-bit offset for every k
+            const unsigned toff = (threadIdx.x / V8) * D + (threadIdx.x % V8) * 8;
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const u16 *base = src + ((size_t)c0 + (size_t)k * (NT / V8)) * D;
+                v[k] = gld16<STREAM>(base + toff);
+            }
+            return;
+        }
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int idx = threadIdx.x + k * NT, r = idx / V8, c8 = (idx % V8) * 8;
             v[k] = *reinterpret_cast<const uint4 *>(src + (size_t)min(c0 + r, N - 1) * D + c8);
         }
-        if (c0 + C > N) {
 #pragma unroll
-            for (int k = 0; k < NV; ++k) {
-                const int r = (threadIdx.x + k * NT) / V8;
-                if (c0 + r >= N) v[k] = make_uint4(0, 0, 0, 0);
-            }
+        for (int k = 0; k < NV; ++k) {
+            const int r = (threadIdx.x + k * NT) / V8;
+            if (c0 + r >= N) v[k] = make_uint4(0, 0, 0, 0);
         }
     }
 
@@ -328,14 +383,30 @@ __device__ __forceinline__ void stage_out(u16 *sO, const f32x16 &acc, float scal
 // store_rows: rows 0..31 of the tile sO (row r -> global row c0 + r of a
 // [N][D] tensor, rows >= N skipped; layout L), NT threads storing 16-byte pieces.  Call
 // after a barrier that follows the stage_out of every wave.
-template <int D, int NT, class L>
+// FAST (kernels with registers to spare): the pieces of a thread sit at a
+// uniform base plus one 32-bit offset (as in RawTile::load); otherwise a lean
+// loop.
+template <int D, int NT, class L, bool FAST = false, bool STREAM = false>
 __device__ __forceinline__ void store_rows(u16 *dst, const u16 *sO, int c0, int N) {
-    constexpr int V8 = D / 8;
-    for (int v = threadIdx.x; v < 32 * V8; v += NT) {
-        const int r = v / V8, c8 = (v % V8) * 8;
-        if (c0 + r < N)
-            *reinterpret_cast<uint4 *>(dst + (size_t)(c0 + r) * D + c8) =
-                *reinterpret_cast<const uint4 *>(sO + L::at(r, c8));
+    constexpr int V8 = D / 8, NV = 32 * V8 / NT;
+    static_assert(NV * NT == 32 * V8, "rows split evenly over the threads");
+    if constexpr (FAST) {
+        const unsigned t = threadIdx.x, toff = (t / V8) * D + (t % V8) * 8;
+        const bool whole = c0 + 32 <= N;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int r = (int)(t / V8) + k * (NT / V8);
+            const uint4 x = *reinterpret_cast<const uint4 *>(sO + L::at(r, (t % V8) * 8));
+            u16 *base = dst + ((size_t)c0 + (size_t)k * (NT / V8)) * D;   // uniform
+            if (whole || c0 + r < N) gst16<STREAM>(base + toff, x);
+        }
+    } else {
+        for (int v = threadIdx.x; v < 32 * V8; v += NT) {
+            const int r = v / V8, c8 = (v % V8) * 8;
+            if (c0 + r < N)
+                *reinterpret_cast<uint4 *>(dst + (size_t)(c0 + r) * D + c8) =
+                    *reinterpret_cast<const uint4 *>(sO + L::at(r, c8));
+        }
     }
 }
 
@@ -380,6 +451,33 @@ __device__ __forceinline__ f32x16 get_acc(const float *src) {
 
 // Accumulator row index of register r for lane half h.
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// The causal mask of a 32x32 accumulator tile whose row index is the key j
+// (accumulator row) and whose column is the query i (lane % 32), applied to
+// its bf16 operands: word p of acc_op(T, s) holds registers 8s + 2p and
+// 8s + 2p + 1, i.e. rows j0 = acc_row(8s + 2p, h) and j0 + 1, and is and-ed
+// with a per-lane constant that keeps a half where j <= i.  The same bits as
+// zeroing the masked floats before rounding (a zero rounds to +0), in one
+// instruction per pair instead of a conversion, a select and a permute per
+// element.
+struct CausalMaskT {
+    uint32_t w[8];
+    __device__ __forceinline__ CausalMaskT(int l32, int h) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int j0 = acc_row(2 * p, h);
+            w[p] = j0 + 1 <= l32 ? 0xffffffffu : (j0 <= l32 ? 0x0000ffffu : 0u);
+        }
+    }
+    // acc_op(T, s) with the mask applied
+    __device__ __forceinline__ bf16x8 op(const f32x16 &T, int s) const {
+        const int b = 8 * s;
+        const uint4 u = make_uint4(pk2(T[b], T[b + 1]) & w[4 * s], pk2(T[b + 2], T[b + 3]) & w[4 * s + 1],
+                                   pk2(T[b + 4], T[b + 5]) & w[4 * s + 2],
+                                   pk2(T[b + 6], T[b + 7]) & w[4 * s + 3]);
+        return __builtin_bit_cast(bf16x8, u);
+    }
+};
 
 }  // namespace mf
 }  // namespace la

@@ -41,20 +41,22 @@ struct FwdTiles {
     using TD = PadI<D>;
 };
 
-// S += Phi(K)^T V over the 64 rows of the staged chunk for one wave's tiles:
+// S += Phi(K)^T V over the CS rows of the staged chunk for one wave's tiles:
 // value block vb and feature blocks FBW*fh + i, i < FBW (natural k order:
 // lane half h holds rows 16s + 8h .. +7), and z += Phi(K)^T 1 for the blocks
-// i = vb (mod D/32) of that set into Z[i / (D/32)].
-template <int D, int F, int FBW>
+// i = vb + (D/32) c < FBW of that set into Z[c].  The z products read their K
+// operands at the wave's own feature columns (a uniform address), so no
+// branch depends on the wave index.
+template <int D, int F, int FBW, int CS>
 __device__ __forceinline__ void state_update(f32x16 *S, f32x16 *Z, const u16 *sK, const u16 *sV,
                                              int vb, int fh) {
-    constexpr int NW = D / 32;
+    constexpr int NW = D / 32, ZB = (FBW + NW - 1) / NW;
     using TF = typename FwdTiles<D, F>::TF;
     using TD = typename FwdTiles<D, F>::TD;
     const int h = (threadIdx.x & 63) >> 5;
     const bf16x8 one = ones8();
 #pragma unroll
-    for (int s = 0; s < kC / 16; ++s) {
+    for (int s = 0; s < CS / 16; ++s) {
         const int k0 = 16 * s + 8 * h;
         const bf16x8 vo = tr8(tr_addr<TD>(sV, k0, 32 * vb), tr_addr<TD>(sV, k0 + 4, 32 * vb));
 #pragma unroll
@@ -62,7 +64,12 @@ __device__ __forceinline__ void state_update(f32x16 *S, f32x16 *Z, const u16 *sK
             const int fb = FBW * fh + i;
             const bf16x8 ka = tr8(tr_addr<TF>(sK, k0, 32 * fb), tr_addr<TF>(sK, k0 + 4, 32 * fb));
             S[i] = mfma(ka, vo, S[i]);
-            if (i % NW == vb) Z[i / NW] = mfma(ka, one, Z[i / NW]);
+        }
+#pragma unroll
+        for (int c = 0; c < ZB; ++c) {
+            if (ZB * NW > FBW && vb + NW * c >= FBW) continue;   // uniform: no such block
+            const int zc = 32 * (FBW * fh + vb + NW * c);
+            Z[c] = mfma(tr8(tr_addr<TF>(sK, k0, zc), tr_addr<TF>(sK, k0 + 4, zc)), one, Z[c]);
         }
     }
 }
@@ -80,9 +87,14 @@ __device__ __forceinline__ void state_update(f32x16 *S, f32x16 *Z, const u16 *sK
 // Occupancy the state pass is built for: it streams K and V, so more waves
 // per SIMD hide more load latency (each shape's registers allow this).
 template <int D, int F>
-constexpr int state_sets() { return F == 256 ? 2 : 1; }
+constexpr int state_sets() { return D == 128 ? 2 : 1; }
 template <int D, int F>
-constexpr int state_waves() { return F == 64 ? 4 : F == 128 ? (D == 128 ? 3 : 2) : 2; }
+constexpr int state_waves() { return F == 64 ? 4 : F == 128 && D == 128 ? 4 : 2; }
+// Rows per chunk: at D = F = 128 the two wave sets have the registers for
+// 128-row chunks, which doubles the bytes each workgroup keeps in flight
+// (the pass streams K and V, and in-flight bytes set its rate).
+template <int D, int F>
+constexpr int state_chunk() { return D == 128 && F == 128 ? 128 : kC; }
 
 template <int D, int F, int PHI, bool COS>
 __global__ __launch_bounds__((D * 2 * state_sets<D, F>())) __attribute__((amdgpu_waves_per_eu(state_waves<D, F>()))) void k_state_mfma(Args a, int nseg_run) {
@@ -90,9 +102,10 @@ __global__ __launch_bounds__((D * 2 * state_sets<D, F>())) __attribute__((amdgpu
     using TD = typename FwdTiles<D, F>::TD;
     constexpr int NH = state_sets<D, F>(), NW = D / 32, NT = D * 2 * NH;
     constexpr int FBW = F / 32 / NH, ZB = (FBW + NW - 1) / NW;   // z tiles per wave (at most)
+    constexpr int CS = state_chunk<D, F>();
     static_assert(FBW * NH * 32 == F, "feature blocks split evenly");
-    __shared__ __attribute__((aligned(16))) u16 sK[kC * TF::ld];
-    __shared__ __attribute__((aligned(16))) u16 sV[kC * TD::ld];
+    __shared__ __attribute__((aligned(16))) u16 sK[CS * TF::ld];
+    __shared__ __attribute__((aligned(16))) u16 sV[CS * TD::ld];
     const int seg = blockIdx.x % nseg_run, bg = blockIdx.x / nseg_run;   // segments 0 .. nseg_run-1
     const int t = threadIdx.x, l = t & 63, h = l >> 5, l32 = l & 31;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index, uniform
@@ -105,17 +118,27 @@ __global__ __launch_bounds__((D * 2 * state_sets<D, F>())) __attribute__((amdgpu
 #pragma unroll
     for (int c = 0; c < ZB; ++c) Z[c] = zero16();
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
-    RawTile<D, NT> rK, rV;
-    rK.load(kh, row0, a.N);
-    rV.load(vh, row0, a.N);
-    for (int c0 = row0; c0 < row1; c0 += kC) {
+    // The next chunk's loads are in flight while the current one is summed.
+    // Tiles end at the segment end row1 (segments are multiples of 64 rows,
+    // chunks may be 128): rows at or past it load as zeros, like rows past N,
+    // so they add nothing; a load wholly past it (the prefetch after the
+    // last chunk) is unused.
+    // Chunks are summed last to first: the rows this pass reads last are
+    // the first ones the forward reads back, so they are the most likely to
+    // still sit in the device's last-level cache when it does.
+    RawTile<D, NT, CS, D == 128> rK, rV;
+    const int clast = row0 + (row1 - row0 - 1) / CS * CS;
+    rK.load(kh, clast, row1);
+    rV.load(vh, clast, row1);
+    for (int c0 = clast; c0 >= row0; c0 -= CS) {
         __syncthreads();
-        rK.template store_feat<PHI, COS, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rK.template store_feat<PHI, COS, TF, false>(sK, c0, row1, a.cw, a.sw, nullptr, nullptr);
         rV.template store<TD>(sV);
         __syncthreads();
-        rK.load(kh, c0 + kC, a.N);   // next chunk (past the segment: unused)
-        rV.load(vh, c0 + kC, a.N);
-        state_update<D, F, FBW>(S, Z, sK, sV, vb, fh);
+        const int cn = c0 - CS >= row0 ? c0 - CS : row0;   // the next chunk (after the first: unused)
+        rK.load(kh, cn, row1);
+        rV.load(vh, cn, row1);
+        state_update<D, F, FBW, CS>(S, Z, sK, sV, vb, fh);
     }
     float *out = a.ws_S + ((size_t)bg * (a.nseg + 1) + seg) * ((size_t)F * D + F);
 #pragma unroll
@@ -140,6 +163,11 @@ __global__ __launch_bounds__((D * 2 * state_sets<D, F>())) __attribute__((amdgpu
 
 constexpr int kCf = 32;   // forward chunk length: one 32x32 tile of A per head
 
+// Waves per SIMD the causal forward is built for: D = F = 64 (two-wave
+// workgroups, six per compute unit) three; F = 256 one.
+template <int D, int F>
+constexpr int fwd_waves() { return D == 64 && F == 64 ? 3 : F <= 128 ? 2 : 1; }
+
 // ---------------------------------------------------------------------------
 // k_fwd_mfma: per (batch, KV head, segment): the chunk loop for all n_rep
 // query heads of the KV head, from the segment's exclusive prefix state.
@@ -150,7 +178,7 @@ constexpr int kCf = 32;   // forward chunk length: one 32x32 tile of A per head
 // w, w + D/32, ...) and mirrored to LDS for the Phi(q).z dot of the staging.
 // ---------------------------------------------------------------------------
 template <int D, int F, int PHI, bool COS>
-__global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 ? 2 : 1))) void k_fwd_mfma(Args a) {
+__global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(fwd_waves<D, F>()))) void k_fwd_mfma(Args a) {
     using TF = typename FwdTiles<D, F>::TF;
     using TD = typename FwdTiles<D, F>::TD;
     constexpr int NT = D * 2, NW = D / 32, FB = F / 32, ZB = FB / NW;
@@ -189,9 +217,16 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
             Z[c][r] = Sp[(size_t)F * D + 32 * (w + NW * c) + 8 * (r >> 2) + 4 * h + (r & 3)];
     for (int e = t; e < F; e += NT) sz[e] = Sp[(size_t)F * D + e];
     const bf16x8 one = ones8();
+    // the D = F = 128 instance has registers to spare at two waves per SIMD:
+    // it keeps the mask words and reads the Phi(Q) operands ahead
+    constexpr bool kRich = D == 128 && F == 128;
+    const CausalMaskT cmask(kRich ? l32 : 0, h);
 
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
-    RawTile<D, NT, kCf> rK, rV, rQ;
+    // q is read and out written once: streamed past the caches, which keep
+    // the K, V rows the state pass has just read
+    RawTile<D, NT, kCf, kRich> rK, rV;
+    RawTile<D, NT, kCf, kRich, kRich> rQ;
     rK.load(kh, row0, a.N);
     rV.load(vh, row0, a.N);
     rQ.load(qbase + bh0 * a.N * D, row0, a.N);
@@ -200,7 +235,7 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
     int pend_c0 = 0;
     for (int c0 = row0; c0 < row1; c0 += kCf) {
         __syncthreads();   // previous chunk: every LDS read done, sz updated, sO complete
-        if (pend_oh) store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
+        if (pend_oh) store_rows<D, NT, TD, kRich, kRich>(pend_oh, sO, pend_c0, a.N);
         rK.template store_feat<PHI, COS, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
         rV.template store<TD>(sV);
         // the next chunk's K, V (unconditional: rows past the segment are
@@ -217,7 +252,7 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
             if (rep > 0) {
                 __syncthreads();   // every wave is done with the previous head's sQ; sO complete
                 rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
-                store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);   // after the staging's wait
+                store_rows<D, NT, TD, kRich, kRich>(pend_oh, sO, pend_c0, a.N);   // after the staging's wait
             }
             __syncthreads();
             {   // Q rows of the next head, or of the first head at the next chunk
@@ -228,20 +263,31 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
             // A^T (keys x queries) of the chunk, causal mask, bf16 rounding (the
             // values the A V product consumes) and the in-chunk denominators
             // from the same rounded values
+            // (fully unrolled: the first product starts from a zero accumulator
+            // operand, with no register clearing)
             f32x16 T = zero16();
-#pragma unroll 4
+#pragma unroll
             for (int s = 0; s < F / 16; ++s)
                 T = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), T);
+            if constexpr (!kRich) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int j = 8 * (r >> 2) + 4 * h + (r & 3);
-                T[r] = j <= l32 ? T[r] : 0.f;
+                for (int r = 0; r < 16; ++r) T[r] = acc_row(r, h) <= l32 ? T[r] : 0.f;
             }
-            const bf16x8 B0 = acc_op(T, 0), B1 = acc_op(T, 1);
+            const bf16x8 B0 = kRich ? cmask.op(T, 0) : acc_pk(T, 0);
+            const bf16x8 B1 = kRich ? cmask.op(T, 1) : acc_pk(T, 1);
             // sum_j A_ij on the matrix cores: 1^T A^T, every row holds it
             const float dsum = mfma(one, B1, mfma(one, B0, zero16()))[0];
 
-            // num^T for this wave's value columns: V^T A^T + S^T Phi(Q)^T
+            // num^T for this wave's value columns: V^T A^T + S^T Phi(Q)^T.  With
+            // registers to spare the Phi(Q) operands are all read before the
+            // products, so the chain of products waits for the LDS once.
+            bf16x8 qop[FB][2];
+            if constexpr (kRich) {
+#pragma unroll
+                for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) qop[fb][s] = ld4x2<TF>(sQ, l32, 32 * fb + 16 * s + 4 * h);
+            }
             f32x16 Nt = zero16();
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -253,13 +299,18 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
             for (int fb = 0; fb < FB; ++fb)
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
-                    Nt = mfma(acc_op(S[fb], s), ld4x2<TF>(sQ, l32, 32 * fb + 16 * s + 4 * h), Nt);
+                    Nt = mfma(acc_pk(S[fb], s),
+                              kRich ? qop[fb][s] : ld4x2<TF>(sQ, l32, 32 * fb + 16 * s + 4 * h), Nt);
             const float den = dsum + sQZ[l32] + a.eps;
             stage_out<TD>(sO, Nt, rcp(den), 32 * w);
             pend_oh = oh;
             pend_c0 = c0;
         }
-        // carry (S, z) past this chunk: S += Phi(K)^T V, z += Phi(K)^T 1
+        // carry (S, z) past this chunk: S += Phi(K)^T V, z += Phi(K)^T 1 for
+        // the z blocks of this wave (feature blocks w, w + D/32, ...).  With
+        // registers to spare those read their K operands again at the wave's
+        // own columns (no branch on the block index); otherwise they reuse the
+        // S operand of the block behind a uniform branch.
 #pragma unroll
         for (int s = 0; s < kCf / 16; ++s) {
             const int k0 = 16 * s + 8 * h;
@@ -268,7 +319,14 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
             for (int fb = 0; fb < FB; ++fb) {
                 const bf16x8 ka = tr8(tr_addr<TF>(sK, k0, 32 * fb), tr_addr<TF>(sK, k0 + 4, 32 * fb));
                 S[fb] = mfma(ka, vb, S[fb]);
-                if (fb % NW == w) Z[fb / NW] = mfma(ka, one, Z[fb / NW]);
+                if (!kRich && fb % NW == w) Z[fb / NW] = mfma(ka, one, Z[fb / NW]);
+            }
+            if constexpr (kRich) {
+#pragma unroll
+                for (int c = 0; c < ZB; ++c) {
+                    const int zc = 32 * (w + NW * c);
+                    Z[c] = mfma(tr8(tr_addr<TF>(sK, k0, zc), tr_addr<TF>(sK, k0 + 4, zc)), one, Z[c]);
+                }
             }
         }
         // every head's staging has read sz (they all passed the barrier before
@@ -282,7 +340,7 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(F <= 128 
         }
     }
     __syncthreads();
-    if (pend_oh) store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
+    if (pend_oh) store_rows<D, NT, TD, kRich, kRich>(pend_oh, sO, pend_c0, a.N);
 }
 
 // ---------------------------------------------------------------------------
@@ -377,8 +435,8 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void
                     T = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), T);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) T[r] = acc_row(r, h) <= l32 ? T[r] : 0.f;
-                B0 = acc_op(T, 0);
-                B1 = acc_op(T, 1);
+                B0 = acc_pk(T, 0);
+                B1 = acc_pk(T, 1);
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     const int k0 = 16 * s + 4 * h;
@@ -390,7 +448,7 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void
             for (int i = 0; i < FH; ++i)
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
-                    Nt = mfma(acc_op(S[i], s), ld4x2<TF>(sQ, l32, 32 * (FH * fh + i) + 16 * s + 4 * h), Nt);
+                    Nt = mfma(acc_pk(S[i], s), ld4x2<TF>(sQ, l32, 32 * (FH * fh + i) + 16 * s + 4 * h), Nt);
             if (fh == 1) put_acc(sNp[vb], Nt);
             __syncthreads();
             if (fh == 0) {
