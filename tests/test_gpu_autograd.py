@@ -19,7 +19,10 @@ pytestmark = pytest.mark.gpu
 CASES = [("bf16", 128, True, False, 4, 2, 200, 0), ("bf16", 128, True, False, 4, 2, 200, 64),
          ("bf16", 64, False, False, 4, 4, 150, 64), ("bf16", 128, True, True, 4, 1, 150, 64),
          ("f32", 64, True, False, 2, 1, 130, 64), ("bf16", 32, False, True, 2, 2, 100, 0),
-         ("bf16", 64, False, True, 32, 32, 16384, 0)]
+         ("bf16", 64, False, True, 32, 32, 16384, 0),
+         # D = 128 with many short segments: the dq kernel walks several
+         # segments per workgroup (its multi-segment build)
+         ("bf16", 128, True, False, 4, 4, 16300, 64)]
 
 
 def _id(c):

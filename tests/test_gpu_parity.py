@@ -57,7 +57,7 @@ def test_small_shapes(case):
     ref = oracle_on(t, causal, phi, eps)
     for seg_len in (0, 64):           # automatic split, then many short segments
         out, grads = run_gpu(la, t, causal, phi, eps, seg_len=seg_len)
-        compare(t, out, grads, ref[0], ref[1], dtype, H, Hkv, label="seg_len=%d" % seg_len)
+        compare(t, out, grads, ref[0], ref[1], dtype, H, Hkv, label="%s-seg%d" % (_id(case), seg_len))
 
 
 @pytest.mark.parametrize("N", [1, 5, 31, 33, 64, 65, 129])
@@ -72,7 +72,9 @@ def test_edge_lengths(N, causal):
         say("edge N=%d %s D=%d cos=%s causal=%s eps=%g" % (N, dtype, D, cos, causal, eps))
         ref = oracle_on(t, causal, "elu+1", eps)
         out, grads = run_gpu(la, t, causal, "elu+1", eps)
-        compare(t, out, grads, ref[0], ref[1], dtype, 2, 1, label="N=%d" % N)
+        compare(t, out, grads, ref[0], ref[1], dtype, 2, 1, label="edge-N%d-%s-D%d%s-%s" % (
+            N, dtype, D, "-cos" if cos else "", "causal" if causal else "bidir"),
+            grad_blocks=N > 1)
 
 
 SPAN = [(128, True, 4, 4), (128, False, 8, 4), (128, True, 8, 2)]
@@ -91,8 +93,9 @@ def test_dq_workgroup_spans_segments(D, causal, H, Hkv):
     t = make(B, H, Hkv, N, D, "bf16", scale=0.5, cos=False, seed=D + H + N)
     say("span D=%d causal=%s H=%d Hkv=%d N=%d seg_len=64" % (D, causal, H, Hkv, N))
     ref = oracle_on(t, causal, "elu+1", 1e-6)
-    out, grads = run_gpu(la, t, causal, "elu+1", 1e-6, seg_len=64)
-    compare(t, out, grads, ref[0], ref[1], "bf16", H, Hkv, label="span")
+    out, grads = run_gpu(la, t, causal, "elu+1", 1e-6, seg_len=64, saved=True)
+    compare(t, out, grads, ref[0], ref[1], "bf16", H, Hkv, label="span-D%d-%s-h%dkv%d" % (
+        D, "causal" if causal else "bidir", H, Hkv))
 
 
 def test_tiny_fp32_workload():
@@ -106,7 +109,8 @@ def test_tiny_fp32_workload():
         for seg_len in (0, 64):
             say("tiny_fp32 %s seg_len=%d" % (mode, seg_len))
             out, grads = run_gpu(la, t, causal, w.phi, w.eps, seg_len=seg_len)
-            compare(t, out, grads, ref[0], ref[1], "f32", w.H, w.Hkv, label=mode)
+            compare(t, out, grads, ref[0], ref[1], "f32", w.H, w.Hkv,
+                    label="tiny_fp32-%s-seg%d" % (mode, seg_len))
 
 
 # --------------------------------------------------------------------------
@@ -128,21 +132,30 @@ FULL = [("causal_fwd_b4h16n4096d64", "bf16", 6), ("bidir_enc_b16h12n2048d64", "b
 
 @pytest.mark.parametrize("name,dtype,count", FULL, ids=["%s-%s" % (n, d) for n, d, _ in FULL])
 def test_full_size_workloads(name, dtype, count):
+    """The benchmark's launch configuration: one workspace for la_fwd and the
+    backward on its state records (la_bwd_saved), gated whole and per block of
+    rows on sampled groups; then la_bwd (state computed again) must give the
+    same gradients bit for bit."""
     torch, la = gpu_or_skip()
     w = si.WORKLOADS[name]
     say("workload %s %s: drawing inputs" % (name, dtype))
     t = si.workload_inputs(w, dtype, "cuda")
     causal = w.modes == ("causal",)
-    say("workload %s %s: GPU run" % (name, dtype))
-    out, grads = run_gpu(la, t, causal, w.phi, w.eps, backward=w.backward)
+    say("workload %s %s: GPU run (saved-state backward)" % (name, dtype))
+    out, grads = run_gpu(la, t, causal, w.phi, w.eps, backward=w.backward, saved=w.backward)
     groups = _sample_groups(w, count)
     say("workload %s: oracle on groups %s" % (name, groups))
     ref = oracle_on(t, causal, w.phi, w.eps, backward=w.backward, groups=groups)
-    compare(t, out, grads, ref[0], ref[1], dtype, w.H, w.Hkv, groups=groups, label=name)
+    compare(t, out, grads, ref[0], ref[1], dtype, w.H, w.Hkv, groups=groups,
+            label="%s-%s" % (name, dtype))
     # every output is finite everywhere, not only on the sampled groups
     assert torch.isfinite(out).all()
     if grads is not None:
         assert all(torch.isfinite(x).all() for x in grads)
+        say("workload %s: la_bwd (state computed again) against the saved-state run" % name)
+        _, again = run_gpu(la, t, causal, w.phi, w.eps, backward=True, saved=False)
+        for n, a, b in zip(("dq", "dk", "dv"), grads, again):
+            assert torch.equal(a, b), n
 
 
 # --------------------------------------------------------------------------
