@@ -30,9 +30,10 @@
  * outputs are rounded to nearest-even once at the end).
  *
  * Ownership and execution: all pointers are device memory owned by the
- * caller.  The library allocates nothing, keeps no state between calls and
- * only enqueues work on `stream` (a hipStream_t; NULL = the null stream): a
- * call returns before the work is done.  Inputs are read only; outputs are
+ * caller.  The library allocates nothing and keeps no state between calls
+ * (la_fwd_noalloc's static scratch array aside), and only enqueues work on
+ * `stream` (a hipStream_t; NULL = the null stream): a call returns before
+ * the work is done.  Inputs are read only; outputs are
  * fully overwritten and must not alias inputs or each other.  Results are
  * bitwise reproducible run to run (no floating-point atomics).
  *
@@ -171,6 +172,30 @@ la_status la_bwd_saved_ex(const void *q, const void *k, const void *v,
                           int causal, int phi, float eps, const float *cos_w,
                           const float *sin_w, void *ws, size_t ws_bytes,
                           void *stream, int seg_len);
+
+/*
+ * la_fwd_noalloc -- la_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The workspace is not an argument: it is a static device
+ * array of LA_NOALLOC_SCRATCH_BYTES that the library holds on every device
+ * it runs on until the process ends (its address is looked up on the first
+ * call on a device).  The caller passes inputs and outputs as for la_fwd;
+ * results are bitwise those of la_fwd.  The call allocates nothing (with
+ * kernel timing off): no hipMalloc, no hipFree, no allocating library call.
+ *   stream : must belong to the current device (NULL = its null stream).
+ * Errors: as la_fwd, plus LA_ERR_INVALID when the sizes need more workspace
+ * than LA_NOALLOC_SCRATCH_BYTES (la_workspace_bytes(LA_OP_FWD, ...) tells)
+ * or the stream belongs to another device.  Every call on one device shares
+ * that device's array, which keeps the last call's contents (la_fwd writes
+ * every record it reads, so nothing needs clearing): calls that overlap in
+ * time on one device (other streams, other threads) race and must not be
+ * made.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES (40u << 20)
+
+la_status la_fwd_noalloc(const void *q, const void *k, const void *v, void *out, int B, int H,
+                         int H_kv, int N, int D, int dtype, int causal, int phi, float eps,
+                         const float *cos_w, const float *sin_w, void *stream);
 
 /*
  * Kernel timing, for measurement tools.  la_timing_enable(1) makes every

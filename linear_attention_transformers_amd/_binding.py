@@ -81,6 +81,8 @@ def load_library(path: str = LIB_PATH):
         bwd_args = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, fp, fp, vp, sz, vp]
         lib.la_fwd.argtypes = fwd_args
         lib.la_fwd_ex.argtypes = fwd_args + [i]
+        lib.la_fwd_noalloc.argtypes = fwd_args[:15] + [vp]
+        lib.la_fwd_noalloc.restype = i
         lib.la_bwd.argtypes = bwd_args
         lib.la_bwd_ex.argtypes = bwd_args + [i]
         lib.la_bwd_saved.argtypes = bwd_args

@@ -158,6 +158,11 @@ la_status launch_status(hipError_t e) {
 
 }  // namespace
 
+namespace la {
+// Sets la_last_error for the other translation units of the C ABI.
+la_status api_fail(la_status st, const char *msg) { return fail(st, msg); }
+}  // namespace la
+
 extern "C" {
 
 size_t la_workspace_bytes_ex(int op, int B, int H, int H_kv, int N, int D, int dtype,
