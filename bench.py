@@ -70,7 +70,9 @@ def kernel_bytes(name, w, s):
              "k_bwd_kv_mfma": "bwd_kv_causal", "k_fwd_bidir_mfma": "fwd_bidir",
              "k_bwd_q_bidir_mfma": "bwd_q_bidir", "k_bwd_kv_bidir_mfma": "bwd_kv_bidir",
              "k_bwd_q_cos_mfma": "bwd_q_causal", "k_bwd_r_cos_mfma": "bwd_r",
-             "k_bwd_kv_cos_mfma": "bwd_kv_causal"}
+             "k_bwd_kv_cos_mfma": "bwd_kv_causal", "k_state_f32": "state",
+             "k_fwd_bidir_f32": "fwd_bidir", "k_bwd_q_bidir_f32": "bwd_q_bidir",
+             "k_bwd_kv_bidir_f32": "bwd_kv_bidir"}
     if name in alias:
         return table[alias[name]]
     for key, val in table.items():
@@ -120,9 +122,10 @@ def traffic_key(name, dtype, mode):
 
 def step_roofline(w, s, causal):
     """Time of one step (fwd+bwd, or fwd for a forward-only workload) at the
-    roofline: algorithmic bytes at HBM peak
-    vs algorithmic flops at the bf16 matrix peak (state updates and reads,
-    2*F*D per token each; F = 2D with cos/sin)."""
+    roofline: each pass at the larger of its algorithmic bytes at HBM peak and
+    its algorithmic flops (state updates and reads, 2*F*D per token each;
+    F = 2D with cos/sin) at the matrix peak of the storage type (bf16, or
+    float32 for float32 storage), the two passes summed."""
     br = 2 if w.cos else 1
     tokD = w.B * w.N * w.D
     fwd_bytes = s * tokD * (2 * w.H + 2 * w.Hkv) + (8 * w.N if w.cos else 0)
@@ -131,9 +134,10 @@ def step_roofline(w, s, causal):
     bwd_flops = br * 2 * w.D * w.D * w.B * w.N * (3 * w.H + 3 * w.Hkv)
     if not w.backward:   # forward-only workload
         bwd_bytes = bwd_flops = 0
-    t_bytes = (fwd_bytes + bwd_bytes) / (HBM_PEAK_GBS * 1e9)
-    t_flops = (fwd_flops + bwd_flops) / (BF16_PEAK_TFLOPS * 1e12)
-    return max(t_bytes, t_flops), fwd_bytes + bwd_bytes, fwd_flops + bwd_flops
+    peak = (BF16_PEAK_TFLOPS if s == 2 else FP32_PEAK_TFLOPS) * 1e12
+    t = (max(fwd_bytes / (HBM_PEAK_GBS * 1e9), fwd_flops / peak) +
+         max(bwd_bytes / (HBM_PEAK_GBS * 1e9), bwd_flops / peak))
+    return t, fwd_bytes + bwd_bytes, fwd_flops + bwd_flops
 
 
 def cpu_baseline(w, tensors, causal, budget_heads=None, min_seconds=10.0):
@@ -660,7 +664,8 @@ def main():
         roof["achieved"] = ach
         roof["frac"] = ach / HBM_PEAK_GBS
     t_roof, step_bytes, step_flops = step_roofline(w, s, causal)
-    matrix = any("mfma" in k for k in ktimes)
+    matrix = any("mfma" in k or k.endswith("_f32") for k in ktimes)
+    mpeak = BF16_PEAK_TFLOPS if s == 2 else FP32_PEAK_TFLOPS
     fwd_kernels = [k for k in ktimes if not (k.startswith("k_bwd") or k == "k_scan_R")]
 
     calib = None
@@ -684,7 +689,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if matrix else "f32",
+        "dtype": "bf16" if s == 2 else "f32",
         "data": "synthetic",
         "config": {"workload": name, "B": w.B, "H": w.H, "H_kv": w.Hkv, "N": w.N, "D": w.D,
                    "phi": w.phi, "causal": causal, "cos_sin": w.cos, "storage": dtype,
@@ -706,10 +711,10 @@ def main():
         "kernels_gbs": {k: kernel_bytes(k, w, s) / (v[1] / v[0] / 1e3) / 1e9
                         for k, v in ktimes.items() if v[0] and kernel_bytes(k, w, s) is not None},
         "matrix": {"achieved": step_flops / (ms_step / 1e3) / 1e12,
-                   "peak": BF16_PEAK_TFLOPS if matrix else FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                   "frac": step_flops / (ms_step / 1e3) / 1e12 /
-                           (BF16_PEAK_TFLOPS if matrix else FP32_PEAK_TFLOPS),
-                   "units": "bf16 matrix cores" if matrix else "fp32 vector ALU"},
+                   "peak": mpeak, "unit": "TFLOP/s",
+                   "frac": step_flops / (ms_step / 1e3) / 1e12 / mpeak,
+                   "units": ("%s matrix cores" % ("bf16" if s == 2 else "float32")) if matrix
+                            else "float32 vector ALU"},
         "calibration": calib,
         "bwd_recomputing_state": recompute,
         "cpu_baseline": None,

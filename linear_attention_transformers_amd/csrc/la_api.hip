@@ -200,6 +200,8 @@ la_status la_fwd_ex(const void *q, const void *k, const void *v, void *out, int 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (uses_mfma(0, dtype, causal, D, cos_w != nullptr))
         return launch_status(la::mfma_fwd_run(a, phi, causal, s));
+    if (la::mfma_f32_serves(dtype == LA_BF16, causal, D, cos_w != nullptr))
+        return launch_status(la::mfma_f32_run(a, 0, phi, s));
     return launch_status(la::generic_run(a, dtype == LA_BF16, 0, causal != 0, phi, s));
 }
 
@@ -248,6 +250,8 @@ la_status bwd_impl(const void *q, const void *k, const void *v, const void *grad
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (uses_mfma(1, dtype, causal, D, cos_w != nullptr))
         return launch_status(la::mfma_bwd_run(a, phi, causal, s));
+    if (la::mfma_f32_serves(dtype == LA_BF16, causal, D, cos_w != nullptr))
+        return launch_status(la::mfma_f32_run(a, 1, phi, s));
     return launch_status(la::generic_run(a, dtype == LA_BF16, 1, causal != 0, phi, s));
 }
 

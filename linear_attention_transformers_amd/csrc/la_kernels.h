@@ -34,6 +34,11 @@ bool mfma_bwd_serves(int bf16, int causal, int D, int has_cos);
 hipError_t mfma_bwd_run(const Args &a, int phi, int causal, hipStream_t s);
 hipError_t mfma_bwd_cos_run(const Args &a, int phi, hipStream_t s);
 
+// float32 bidirectional kernels on the matrix cores (F = D in {64, 128}):
+// the float32 path's plan, workspace layout and scans.
+bool mfma_f32_serves(int bf16, int causal, int D, int has_cos);
+hipError_t mfma_f32_run(const Args &a, int bwd, int phi, hipStream_t s);
+
 // Low-rank projection (la_lowrank.hip): bf16 tensors, fp32 scratch in the workspace.
 struct LowRankArgs {
     const unsigned short *x, *U, *V, *bias, *g;   // bf16 inputs (bias, g optional per pass)

@@ -241,8 +241,10 @@ def test_binding_errors_on_gpu():
 
 def test_kernel_family_per_case():
     """bf16 runs on the matrix-core kernels (causal and bidirectional, forward
-    and backward; the cos/sin backward when causal); float32 on the vector-ALU
-    kernels (checked through the library's launch timing)."""
+    and backward; the cos/sin backward when causal); float32 bidirectional
+    without cos/sin at D = 64 and 128 on the float32 matrix-core kernels, other
+    float32 cases on
+    the vector-ALU kernels (checked through the library's launch timing)."""
     torch, la = gpu_or_skip()
     t = make(1, 4, 2, 600, 128, "bf16", scale=0.5, seed=1)   # three 256-row segments
     la.timing_enable(True)
@@ -285,3 +287,13 @@ def test_kernel_family_per_case():
     finally:
         la.timing_enable(False)
     assert {"k_bwd_q_cos_mfma", "k_bwd_r_cos_mfma", "k_bwd_kv_cos_mfma"} <= names, names
+    for D in (64, 128):
+        t = make(1, 4, 2, 300, D, "f32", seed=2)
+        la.timing_enable(True)
+        try:
+            run_gpu(la, t, False, "elu+1", backward=True)
+            names = set(la.timing_collect())
+        finally:
+            la.timing_enable(False)
+        assert {"k_state_f32", "k_fwd_bidir_f32", "k_bwd_q_bidir_f32",
+                "k_bwd_kv_bidir_f32"} <= names, (D, names)
