@@ -25,12 +25,12 @@
 // are conflict-free in it.
 //
 // Layout of the work: one workgroup per (batch, KV head, segment) serving the
-// n_rep query heads.  Each wave computes the chunk's 32x32 tile of A and T
-// itself (so no C x C data crosses waves) and owns a 32-wide block of the
-// feature columns of the state (S^T in the q-kernel, R^T in the kv-kernel),
-// of dPhi(q) / dPhi(k), and of the value columns of dv.  The only cross-wave
-// reduction, Phi(q_i).U_i over the feature blocks, goes through LDS in a
-// fixed order.  In the q-kernel a second set of waves accumulates the
+// n_rep query heads.  Per chunk and head one wave forms each 32x32 C x C
+// tile (A, T in the q-kernel; A, P in the kv-kernel) for the workgroup, and
+// each wave owns a 32-wide block of the feature columns of the state (S^T in
+// the q-kernel, R^T in the kv-kernel), of dPhi(q) / dPhi(k), and of the value
+// columns of dv.  The only cross-wave reduction, Phi(q_i).U_i over the
+// feature blocks, goes through LDS in a fixed order.  In the q-kernel a second set of waves accumulates the
 // segment's (R, r) so the two register-heavy states live in different waves.
 #include <atomic>
 
@@ -400,7 +400,9 @@ int q_segments_per_wg(const Args &a, unsigned n_units) {
 // k_bwd_kv_mfma: backward over the 32-row chunks of one (batch, KV head,
 // segment), from the exclusive suffix (R, r) of the segment.  Wave w holds
 // R^T (every value block x feature block w) and produces dk for feature
-// block w and dv for value block w.
+// block w and dv for value block w.  Per head, wave 0 forms the masked A
+// tile and wave 1 the P tile as bf16 operands for every wave (through LDS),
+// while the waves form the chunk's state terms.
 // ---------------------------------------------------------------------------
 template <int D, int PHI, bool CAUSAL>
 __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2)))
@@ -416,6 +418,11 @@ void k_bwd_kv_mfma(Args a) {
     __shared__ __attribute__((aligned(16))) u16 sGr[kCb * TD::ld];   // raw g rows (for P)
     __shared__ __attribute__((aligned(16))) float sCc[kCb], sIq[kCb];   // c_i, 1 / den_i
     __shared__ float sr[F];
+    __shared__ bf16x8 sAop[2][64];   // A operands of one head, per lane
+    // P operands of one head, per lane: in the raw g rows, which only wave 1
+    // reads (for P, before it writes them) until the next head is staged
+    bf16x8 (*sPop)[64] = reinterpret_cast<bf16x8 (*)[64]>(sGr);
+    static_assert(sizeof(bf16x8) * 2 * 64 <= sizeof(u16) * kCb * TD::ld, "P operands fit the g rows");
 
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
@@ -492,6 +499,43 @@ void k_bwd_kv_mfma(Args a) {
         rG.load(gbase + hn * a.N * D, cq, a.N);
         load_dc(hn, cq);
     };
+    // A = Phi(Q) Phi(K)^T (wave 0) and P = (G V^T) / den - c (wave 1)
+    // (queries x keys), i >= j, masked and turned into bf16 operands, for
+    // every wave through LDS (each lane's operands in its own slot: every
+    // wave's operands of a product sit at the same lanes).  P comes from the
+    // raw g rows (exact operands) scaled in fp32: it can be a small
+    // difference (one key: P_00 = eps / den_0 * g.v / den_0), which products
+    // with bf16-rounded gn would not resolve.
+    auto form_ap = [&]() {
+        if (w == 0) {
+            f32x16 A = zero16();
+#pragma unroll
+            for (int s = 0; s < F / 16; ++s)
+                A = mfma(ld8<TF>(sQ, l32, 16 * s + 8 * h), ld8<TF>(sK, l32, 16 * s + 8 * h), A);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) A[r] = acc_row(r, h) >= l32 ? A[r] : 0.f;
+            sAop[0][l] = acc_op(A, 0);
+            sAop[1][l] = acc_op(A, 1);
+        } else if (w == 1) {
+            f32x16 P = zero16();
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s)
+                P = mfma(ld8<TD>(sGr, l32, 16 * s + 8 * h), ld8<TD>(sV, l32, 16 * s + 8 * h), P);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float4 cv = *reinterpret_cast<const float4 *>(sCc + 8 * q4 + 4 * h);
+                const float4 iv = *reinterpret_cast<const float4 *>(sIq + 8 * q4 + 4 * h);
+                const float cr[4] = {cv.x, cv.y, cv.z, cv.w}, ir[4] = {iv.x, iv.y, iv.z, iv.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * q4 + e;
+                    P[r] = acc_row(r, h) >= l32 ? P[r] * ir[e] - cr[e] : 0.f;
+                }
+            }
+            sPop[0][l] = acc_op(P, 0);
+            sPop[1][l] = acc_op(P, 1);
+        }
+    };
     for (int ci = nch - 1; ci >= 0; --ci) {
         const int c0 = row0 + ci * kCb;
         const int cn = ci > 0 ? c0 - kCb : c0;   // next chunk (none: reload this one)
@@ -516,6 +560,9 @@ void k_bwd_kv_mfma(Args a) {
         }
         if constexpr (CAUSAL) stage_head(c0, 0, cn);
         __syncthreads();
+        // causal: the first head's A and P tiles (waves 0 and 1), ahead of the
+        // state terms that every wave computes meanwhile
+        if constexpr (CAUSAL) form_ap();
         // state terms: dPhi(k)^T = R V^T - r, dv^T = R^T Phi(K)^T
         f32x16 dK = zero16(), dV = zero16();
 #pragma unroll
@@ -548,42 +595,10 @@ void k_bwd_kv_mfma(Args a) {
                 __syncthreads();   // the previous head's LDS reads are done
                 stage_head(c0, rep, cn);
                 __syncthreads();
+                form_ap();
             }
-            // A = Phi(Q) Phi(K)^T and P = (G V^T) / den - c (queries x keys),
-            // i >= j, masked and turned into bf16 operands.  P comes from the
-            // raw g rows (exact operands) scaled in fp32: it can be a small
-            // difference (one key: P_00 = eps / den_0 * g.v / den_0), which
-            // products with bf16-rounded gn would not resolve.
-            bf16x8 Aop[2], Pop[2];
-            {
-                f32x16 A = zero16();
-#pragma unroll 4
-                for (int s = 0; s < F / 16; ++s)
-                    A = mfma(ld8<TF>(sQ, l32, 16 * s + 8 * h), ld8<TF>(sK, l32, 16 * s + 8 * h), A);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) A[r] = acc_row(r, h) >= l32 ? A[r] : 0.f;
-                Aop[0] = acc_op(A, 0);
-                Aop[1] = acc_op(A, 1);
-            }
-            {
-                f32x16 P = zero16();
-#pragma unroll 4
-                for (int s = 0; s < D / 16; ++s)
-                    P = mfma(ld8<TD>(sGr, l32, 16 * s + 8 * h), ld8<TD>(sV, l32, 16 * s + 8 * h), P);
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const float4 cv = *reinterpret_cast<const float4 *>(sCc + 8 * q4 + 4 * h);
-                    const float4 iv = *reinterpret_cast<const float4 *>(sIq + 8 * q4 + 4 * h);
-                    const float cr[4] = {cv.x, cv.y, cv.z, cv.w}, ir[4] = {iv.x, iv.y, iv.z, iv.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 4 * q4 + e;
-                        P[r] = acc_row(r, h) >= l32 ? P[r] * ir[e] - cr[e] : 0.f;
-                    }
-                }
-                Pop[0] = acc_op(P, 0);
-                Pop[1] = acc_op(P, 1);
-            }
+            __syncthreads();   // this head's A, P operands are in LDS
+            const bf16x8 Aop[2] = {sAop[0][l], sAop[1][l]}, Pop[2] = {sPop[0][l], sPop[1][l]};
             // in-chunk terms: dPhi(k)^T += Phi(Q)^T P, dv^T += gn^T A
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
