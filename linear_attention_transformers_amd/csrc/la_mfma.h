@@ -224,7 +224,7 @@ __device__ __forceinline__ u16 f2bf(float x) {
 // otherwise, so phi' = min(p, 1) (exp(x) to bf16 precision); identity: 1.
 template <int PHI>
 __device__ __forceinline__ float phi_d_feat(float p) {
-    if constexpr (PHI == kElu1) return fminf(p, 1.f);
+    if constexpr (PHI == kElu1) return __builtin_amdgcn_fmed3f(p, 0.f, 1.f);   // p >= 0: min(p, 1)
     else if constexpr (PHI == kRelu) return p > 0.f ? 1.f : 0.f;
     else return 1.f;
 }

@@ -417,7 +417,7 @@ void k_bwd_kv_mfma(Args a) {
     __shared__ __attribute__((aligned(16))) u16 sR[F * TD::ld];
     __shared__ __attribute__((aligned(16))) u16 sGr[kCb * TD::ld];   // raw g rows (for P)
     __shared__ __attribute__((aligned(16))) float sCc[kCb], sIq[kCb];   // c_i, 1 / den_i
-    __shared__ float sr[F];
+    __shared__ __attribute__((aligned(16))) float sr[F];
     __shared__ bf16x8 sAop[2][64];   // A operands of one head, per lane
     // P operands of one head, per lane: in the raw g rows, which only wave 1
     // reads (for P, before it writes them) until the next head is staged
@@ -586,7 +586,13 @@ void k_bwd_kv_mfma(Args a) {
                       ld8<TF>(sK, l32, 16 * s + 8 * h), dV);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dK[r] -= sr[32 * w + acc_row(r, h)];
+        for (int q4 = 0; q4 < 4; ++q4) {   // rows 8 q4 + 4h + 0..3 are consecutive
+            const float4 r4 = *reinterpret_cast<const float4 *>(sr + 32 * w + 8 * q4 + 4 * h);
+            dK[4 * q4] -= r4.x;
+            dK[4 * q4 + 1] -= r4.y;
+            dK[4 * q4 + 2] -= r4.z;
+            dK[4 * q4 + 3] -= r4.w;
+        }
 
         // causal: the chunk's own queries (in-chunk terms) and the R update;
         // the first head's rows were staged with the chunk
@@ -607,6 +613,9 @@ void k_bwd_kv_mfma(Args a) {
                 dV = mfma(tr8(tr_addr<TD>(sG, k0, 32 * w), tr_addr<TD>(sG, k0 + 8, 32 * w)), Aop[s], dV);
             }
             // R^T += gn^T Phi(Q) for the rows of this chunk; r += Phi(Q)^T c
+            // from the same Phi(Q) operand: lane (n, h) holds feature 32w + n of
+            // rows 16s + 8h .. +7, so the two halves together cover the chunk
+            float acc = 0.f;
 #pragma unroll
             for (int s = 0; s < kCb / 16; ++s) {
                 const int k0 = 16 * s + 8 * h;
@@ -616,19 +625,13 @@ void k_bwd_kv_mfma(Args a) {
                     const bf16x8 ga = tr8(tr_addr<TD>(sG, k0, 32 * db), tr_addr<TD>(sG, k0 + 4, 32 * db));
                     Rt[db] = mfma(ga, qb, Rt[db]);
                 }
-            }
-            {   // r += Phi(Q)^T c: feature 32w + n, rows 16h .. 16h+15 per lane
-                float acc = 0.f;
+                const float4 c0v = *reinterpret_cast<const float4 *>(sCc + k0);
+                const float4 c1v = *reinterpret_cast<const float4 *>(sCc + k0 + 4);
+                const float cv[8] = {c0v.x, c0v.y, c0v.z, c0v.w, c1v.x, c1v.y, c1v.z, c1v.w};
 #pragma unroll
-                for (int j = 0; j < kCb / 8; ++j) {
-                    const float4 cv = *reinterpret_cast<const float4 *>(sCc + 16 * h + 4 * j);
-                    const float c4[4] = {cv.x, cv.y, cv.z, cv.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        acc += c4[e] * bf2f(sQ[TF::at(16 * h + 4 * j + e, 32 * w + l32)]);
-                }
-                racc += sum_halves(acc);
+                for (int e = 0; e < 8; ++e) acc += cv[e] * (float)qb[e];
             }
+            racc += sum_halves(acc);
         }
         // dk = phi'(k) dPhi(k), dv; lane holds key l32 and columns 32w + 8q + 4h + 0..3,
         // stored straight from the registers (the next chunk's tiles take the LDS)
