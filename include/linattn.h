@@ -123,9 +123,12 @@ la_status la_bwd(const void *q, const void *k, const void *v,
 /*
  * la_fwd_ex / la_bwd_ex -- la_fwd / la_bwd with the sequence split forced to
  * segments of `seg_len` rows (0 = automatic).  seg_len is rounded up to a
- * multiple of the kernel's chunk length.  The result equals la_fwd / la_bwd
- * up to float32 summation order; it exists so tests can exercise the
- * cross-segment state scan at small N.  la_workspace_bytes_ex sizes it.
+ * multiple of 64 rows.  The result equals la_fwd / la_bwd up to float32
+ * summation order; it exists so tests can exercise the cross-segment state
+ * scan at small N.  la_workspace_bytes_ex sizes it.  The chunk length is not
+ * an argument: each kernel's chunk (32 rows in the chunk loops, the 32x32
+ * matrix tile the causal mask is built on) is a compile-time constant, and
+ * the segment is the one split that varies at run time.
  */
 size_t la_workspace_bytes_ex(int op, int B, int H, int H_kv, int N, int D,
                              int dtype, int causal, int has_cos, int seg_len);
