@@ -136,17 +136,30 @@ __global__ __launch_bounds__(kNT) void k_state(Args a) {
 // sums by their exclusive prefix over segments (slot s = rows before segment
 // s) and, with `total`, store the total in slot nseg (without it the last
 // segment's record is neither read nor needed).  Fixed order: deterministic.
+// The records of kScanB segments are loaded before any of their slots is
+// written, so a thread waits for memory once per kScanB segments, not once
+// per segment.
 // ---------------------------------------------------------------------------
+constexpr int kScanB = 8;
+
 __global__ __launch_bounds__(kNT) void k_scan_S(float *ws, int nseg, size_t SD, size_t n_units, int total) {
     const size_t e = (size_t)blockIdx.x * kNT + threadIdx.x;
     const size_t unit = blockIdx.y;
     if (e >= SD || unit >= n_units) return;
     float *base = ws + unit * (nseg + 1) * SD + e;
+    const int nin = total ? nseg : nseg - 1;   // records that exist
     float run = 0.f;
-    for (int s = 0; s < nseg; ++s) {
-        const float x = (total || s + 1 < nseg) ? base[(size_t)s * SD] : 0.f;
-        base[(size_t)s * SD] = run;
-        run += x;
+    for (int s0 = 0; s0 < nseg; s0 += kScanB) {
+        float x[kScanB];
+#pragma unroll
+        for (int i = 0; i < kScanB; ++i) x[i] = s0 + i < nin ? base[(size_t)(s0 + i) * SD] : 0.f;
+#pragma unroll
+        for (int i = 0; i < kScanB; ++i) {
+            if (s0 + i < nseg) {
+                base[(size_t)(s0 + i) * SD] = run;
+                run += x[i];
+            }
+        }
     }
     if (total) base[(size_t)nseg * SD] = run;
 }
@@ -163,15 +176,26 @@ __global__ __launch_bounds__(kNT) void k_scan_R(const float *Rp, float *Rs, int 
     if (e >= SD || unit >= n_units) return;
     const size_t b = unit / Hkv, g = unit % Hkv;
     float *out = Rs + unit * (nseg + 1) * SD + e;
+    const float *in = Rp + (b * H + g * nrep) * nseg * SD + e;   // head r, segment s at (r nseg + s) SD
     float run = 0.f;
-    for (int s = nseg - 1; s >= 0; --s) {
-        float x = 0.f;
+    // kScanB segments' partials summed over the heads (order 0 .. nrep-1)
+    // before their slots are written (the output does not alias the input)
+    for (int s0 = nseg - 1; s0 >= 0; s0 -= kScanB) {
+        float x[kScanB];
+#pragma unroll
+        for (int i = 0; i < kScanB; ++i) x[i] = 0.f;
         for (int r = 0; r < nrep; ++r) {
-            const size_t bh = b * H + g * nrep + r;
-            x += Rp[(bh * nseg + s) * SD + e];
+#pragma unroll
+            for (int i = 0; i < kScanB; ++i)
+                if (s0 - i >= 0) x[i] += in[((size_t)r * nseg + (s0 - i)) * SD];
         }
-        out[(size_t)s * SD] = run;
-        run += x;
+#pragma unroll
+        for (int i = 0; i < kScanB; ++i) {
+            if (s0 - i >= 0) {
+                out[(size_t)(s0 - i) * SD] = run;
+                run += x[i];
+            }
+        }
     }
     out[(size_t)nseg * SD] = run;
 }
