@@ -120,8 +120,12 @@ la::Plan plan_for(int op_bwd, int B, int H, int H_kv, int N, int D, int dtype, i
         return la::make_plan(op_bwd, B, H, H_kv, N, D, causal, has_cos, seg_len,
                              (long long)B * H_kv, target);
     }
+    // float32 kernels: one thread walks every row of its segment, so a
+    // short sequence over few heads is cut down to 64-row segments (the
+    // matrix-core kernels keep 256: their workgroups amortise per-segment
+    // set-up over more rows)
     return la::make_plan(op_bwd, B, H, H_kv, N, D, causal, has_cos, seg_len, (long long)B * H,
-                         1024);
+                         1024, la::kSegAlign);
 }
 
 la::Args make_args(const la::Plan &p, int B, int H, int H_kv, int N, int D, float eps,

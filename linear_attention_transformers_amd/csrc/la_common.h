@@ -97,9 +97,11 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Segment count: about `target` workgroups over the `units` independent
 // sequences (each workgroup runs one segment of one unit), but never segments
-// shorter than 4 * kSegAlign rows (the state record would outweigh the rows).
+// shorter than min_L rows (by default 4 * kSegAlign: shorter, the state
+// record would outweigh the rows).
 inline Plan make_plan(int op_bwd, int B, int H, int Hkv, int N, int D, int causal,
-                      int has_cos, int seg_len, long long units, long long target) {
+                      int has_cos, int seg_len, long long units, long long target,
+                      int min_L = 4 * kSegAlign) {
     Plan p{};
     p.F = has_cos ? 2 * D : D;
     p.SD = (size_t)p.F * D + p.F;
@@ -109,7 +111,7 @@ inline Plan make_plan(int op_bwd, int B, int H, int Hkv, int N, int D, int causa
     } else {
         long long nseg = (target + units - 1) / units;
         L = (int)align_up((size_t)((N + nseg - 1) / nseg), kSegAlign);
-        if (L < 4 * kSegAlign) L = 4 * kSegAlign;
+        if (L < min_L) L = min_L;
     }
     if (L > (int)align_up((size_t)N, kSegAlign)) L = (int)align_up((size_t)N, kSegAlign);
     p.L = L;
