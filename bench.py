@@ -70,7 +70,9 @@ def kernel_bytes(name, w, s):
              "k_bwd_kv_mfma": "bwd_kv_causal", "k_fwd_bidir_mfma": "fwd_bidir",
              "k_bwd_q_bidir_mfma": "bwd_q_bidir", "k_bwd_kv_bidir_mfma": "bwd_kv_bidir",
              "k_bwd_q_cos_mfma": "bwd_q_causal", "k_bwd_r_cos_mfma": "bwd_r",
-             "k_bwd_kv_cos_mfma": "bwd_kv_causal", "k_state_f32": "state",
+             "k_bwd_kv_cos_mfma": "bwd_kv_causal", "k_bwd_q_cos_bidir_mfma": "bwd_q_bidir",
+             "k_bwd_r_cos_bidir_mfma": "bwd_r", "k_bwd_kv_cos_bidir_mfma": "bwd_kv_bidir",
+             "k_state_f32": "state",
              "k_fwd_bidir_f32": "fwd_bidir", "k_bwd_q_bidir_f32": "bwd_q_bidir",
              "k_bwd_kv_bidir_f32": "bwd_kv_bidir"}
     if name in alias:

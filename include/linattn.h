@@ -156,11 +156,7 @@ la_status la_bwd_ex(const void *q, const void *k, const void *v,
  * and be left unchanged in between (any other la_fwd / la_bwd on it
  * overwrites the records).  These preconditions are the caller's: the
  * library cannot check them, and when they do not hold the gradients are
- * wrong.  Results are bitwise equal to la_bwd's.  Where the backward runs
- * other kernels than the forward (bf16, bidirectional, cos/sin weights,
- * D = 64 or 128: the backward takes the float32 kernels), the forward's
- * records do not follow the backward's segmentation and the state is
- * computed again, as la_bwd does.  Errors as la_bwd.
+ * wrong.  Results are bitwise equal to la_bwd's.  Errors as la_bwd.
  */
 la_status la_bwd_saved(const void *q, const void *k, const void *v,
                        const void *grad_out, void *dq, void *dk, void *dv,

@@ -244,10 +244,9 @@ la_status bwd_impl(const void *q, const void *k, const void *v, const void *grad
     a.dk = dk;
     a.dv = dv;
     // The saved records are laid out by the forward's plan, which is the
-    // backward's only when both run the same kernel family.  bf16
-    // bidirectional cos/sin at D = 64 or 128 runs its forward on the matrix
-    // cores and its backward on the float32 kernels, with another
-    // segmentation: there the state is computed again.
+    // backward's only when both run the same kernel family.  Every case
+    // served today pairs them; a pairing that did not would compute the
+    // state again rather than read records of another segmentation.
     const int has_cos = cos_w != nullptr;
     a.state_ready = state_ready && uses_mfma(0, dtype, causal, D, has_cos) ==
                                        uses_mfma(1, dtype, causal, D, has_cos);

@@ -126,7 +126,7 @@ inline Plan make_plan(int op_bwd, int B, int H, int Hkv, int N, int D, int causa
         off = align_up(off + sizeof(float) * (size_t)B * H * p.nseg * p.SD, a);
         p.off_Rs = off;
         off = align_up(off + sizeof(float) * (size_t)B * Hkv * (p.nseg + 1) * p.SD, a);
-        if (causal) {
+        if (causal || has_cos) {   // the cos/sin R pass reads den and c in both modes
             p.off_den = off;
             off = align_up(off + sizeof(float) * (size_t)B * H * N, a);
             p.off_c = off;

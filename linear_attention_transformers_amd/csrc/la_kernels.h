@@ -32,7 +32,7 @@ hipError_t mfma_state_run(const Args &a, int phi, int causal, hipStream_t s);
 // features (F = 2D, la_mfma_bwd_cos.hip)
 bool mfma_bwd_serves(int bf16, int causal, int D, int has_cos);
 hipError_t mfma_bwd_run(const Args &a, int phi, int causal, hipStream_t s);
-hipError_t mfma_bwd_cos_run(const Args &a, int phi, hipStream_t s);
+hipError_t mfma_bwd_cos_run(const Args &a, int phi, int causal, hipStream_t s);
 
 // float32 bidirectional kernels on the matrix cores (F = D in {64, 128}):
 // the float32 path's plan, workspace layout and scans.

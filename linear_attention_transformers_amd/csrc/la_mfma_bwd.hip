@@ -702,11 +702,13 @@ hipError_t by_phi(const Args &a, int phi, hipStream_t s) {
 }  // namespace
 
 bool mfma_bwd_serves(int bf16, int causal, int D, int has_cos) {
-    return bf16 && (D == 64 || D == 128) && (!has_cos || causal);
+    (void)causal;
+    (void)has_cos;
+    return bf16 && (D == 64 || D == 128);
 }
 
 hipError_t mfma_bwd_run(const Args &a, int phi, int causal, hipStream_t s) {
-    if (a.F == 2 * a.D) return mfma_bwd_cos_run(a, phi, s);   // causal (mfma_bwd_serves)
+    if (a.F == 2 * a.D) return mfma_bwd_cos_run(a, phi, causal, s);
     if (a.D == 64) return causal ? by_phi<64, true>(a, phi, s) : by_phi<64, false>(a, phi, s);
     return causal ? by_phi<128, true>(a, phi, s) : by_phi<128, false>(a, phi, s);
 }

@@ -45,7 +45,7 @@ __device__ __forceinline__ float phi_d_raw(float x) {
 // whole workgroup; they reach every wave through LDS with the Phi(q).U
 // partials.  Writes den_i and c_i.
 // ---------------------------------------------------------------------------
-template <int D, int PHI>
+template <int D, int PHI, bool CAUSAL>
 __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bwd_q_cos_mfma(Args a) {
     constexpr int F = 2 * D, NW = D / 32, FW = F / 32, NT = 64 * FW;
@@ -72,9 +72,9 @@ void k_bwd_q_cos_mfma(Args a) {
     const u16 *gbase = static_cast<const u16 *>(a.g);
     u16 *dqbase = static_cast<u16 *>(a.dq);
 
-    // exclusive prefix state of the segment: S^T tiles (value block db x
-    // feature block w) and the z tile of block w
-    const float *Sp = a.ws_S + ((size_t)bg * (a.nseg + 1) + seg) * SD;
+    // exclusive prefix state of the segment (causal) or the sequence total:
+    // S^T tiles (value block db x feature block w) and the z tile of block w
+    const float *Sp = a.ws_S + ((size_t)bg * (a.nseg + 1) + (CAUSAL ? seg : a.nseg)) * SD;
     f32x16 X[NW], Z;
 #pragma unroll
     for (int db = 0; db < NW; ++db)
@@ -109,16 +109,20 @@ void k_bwd_q_cos_mfma(Args a) {
 
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
     RawTile<D, NT, kCc> rK, rV, rQ, rG;
-    rK.load(kh, row0, a.N);
-    rV.load(vh, row0, a.N);
+    if constexpr (CAUSAL) {   // the in-chunk terms and the carry need the keys
+        rK.load(kh, row0, a.N);
+        rV.load(vh, row0, a.N);
+    }
     rQ.load(qbase + bh0 * a.N * D, row0, a.N);
     rG.load(gbase + bh0 * a.N * D, row0, a.N);
     for (int c0 = row0; c0 < row1; c0 += kCc) {
         __syncthreads();
-        rK.template store_feat<PHI, true, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
-        rV.template store<TD>(sV);
-        rK.load(kh, c0 + kCc, a.N);   // next chunk (past the segment: unused)
-        rV.load(vh, c0 + kCc, a.N);
+        if constexpr (CAUSAL) {
+            rK.template store_feat<PHI, true, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+            rV.template store<TD>(sV);
+            rK.load(kh, c0 + kCc, a.N);   // next chunk (past the segment: unused)
+            rV.load(vh, c0 + kCc, a.N);
+        }
         const int ti = min(c0 + l32, a.N - 1);
         const float mq = w < NW ? a.cw[ti] : a.sw[ti];   // this lane's query weight for block w
         // the first head's rows are staged here, in straight-line code (in the
@@ -145,28 +149,33 @@ void k_bwd_q_cos_mfma(Args a) {
             }
             const bool ok = c0 + l32 < a.N;   // this lane's query row exists
 
-            // A^T over the F features (the cos/sin weighting included) on wave
-            // 0, T^T on wave 1, for every wave after the barrier below
-            if (w == 0) {
+            // causal: A^T over the F features (the cos/sin weighting included)
+            // on wave 0, T^T on wave 1, for every wave after the barrier below
+            if (CAUSAL && w == 0) {
                 f32x16 At = zero16();
 #pragma unroll
                 for (int s = 0; s < F / 16; ++s)
                     At = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), At);
                 put_acc(sAt, At);
-            } else if (w == 1) {
+            } else if (CAUSAL && w == 1) {
                 f32x16 Tt = zero16();
 #pragma unroll 4
                 for (int s = 0; s < D / 16; ++s)
                     Tt = mfma(ld8<TD>(sV, l32, 16 * s + 8 * h), ld8<TD>(sG, l32, 16 * s + 8 * h), Tt);
                 put_acc(sTt, Tt);
             }
-            // U^T = S g (feature block w x the chunk's queries), Phi(q).U over the block
+            // U^T = S g (feature block w x the chunk's queries), Phi(q).U over the
+            // block; bidirectional: every term goes through the state, and dq can
+            // be a small difference, so S goes in as two bf16 parts
             f32x16 U = zero16();
 #pragma unroll
             for (int db = 0; db < NW; ++db)
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    U = mfma(acc_op(X[db], s), ld4x2<TD>(sG, l32, 32 * db + 16 * s + 4 * h), U);
+                for (int s = 0; s < 2; ++s) {
+                    const bf16x8 gq = ld4x2<TD>(sG, l32, 32 * db + 16 * s + 4 * h);
+                    U = mfma(acc_op(X[db], s), gq, U);
+                    if constexpr (!CAUSAL) U = mfma(acc_lo(X[db], s), gq, U);
+                }
             float qu = 0.f;
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
@@ -180,9 +189,10 @@ void k_bwd_q_cos_mfma(Args a) {
             __syncthreads();
             if (pend) store_pending();   // the previous head's dq rows
 
-            f32x16 Tt = get_acc(sTt);
+            f32x16 Tt;
             float dA = 0.f, aT = 0.f;
-            {
+            if constexpr (CAUSAL) {
+                Tt = get_acc(sTt);
                 const f32x16 At = get_acc(sAt);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -190,9 +200,9 @@ void k_bwd_q_cos_mfma(Args a) {
                     dA += x;
                     aT += x * Tt[r];
                 }
+                dA = sum_halves(dA);
+                aT = sum_halves(aT);
             }
-            dA = sum_halves(dA);
-            aT = sum_halves(aT);
             const float den = ok ? dA + sQZ[l32] + a.eps : 1.f;
             float gsum = aT;
 #pragma unroll
@@ -204,14 +214,17 @@ void k_bwd_q_cos_mfma(Args a) {
                 a.ws_c[bh * a.N + c0 + l32] = c;
             }
             // P^T = T^T / den - c (masked); dPhi(q)^T = Phi(K)^T P^T + U^T / den - z c
-#pragma unroll
-            for (int r = 0; r < 16; ++r) Tt[r] = acc_row(r, h) <= l32 ? Tt[r] * inv - c : 0.f;
+            // (no in-chunk term: bidirectional)
             f32x16 Qd = zero16();
+            if constexpr (CAUSAL) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int k0 = 16 * s + 4 * h;
-                const bf16x8 ka = tr8(tr_addr<TF>(sK, k0, 32 * w), tr_addr<TF>(sK, k0 + 8, 32 * w));
-                Qd = mfma(ka, acc_op(Tt, s), Qd);
+                for (int r = 0; r < 16; ++r) Tt[r] = acc_row(r, h) <= l32 ? Tt[r] * inv - c : 0.f;
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const int k0 = 16 * s + 4 * h;
+                    const bf16x8 ka = tr8(tr_addr<TF>(sK, k0, 32 * w), tr_addr<TF>(sK, k0 + 8, 32 * w));
+                    Qd = mfma(ka, acc_op(Tt, s), Qd);
+                }
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r)
@@ -234,22 +247,24 @@ void k_bwd_q_cos_mfma(Args a) {
             pbh = bh;
             ++step;
         }
-        // carry (S^T, z) past this chunk
+        if constexpr (CAUSAL) {
+            // carry (S^T, z) past this chunk
 #pragma unroll
-        for (int s = 0; s < kCc / 16; ++s) {
-            const int k0 = 16 * s + 8 * h;
-            const bf16x8 kb = tr8(tr_addr<TF>(sK, k0, 32 * w), tr_addr<TF>(sK, k0 + 4, 32 * w));
-            Z = mfma(kb, one, Z);
+            for (int s = 0; s < kCc / 16; ++s) {
+                const int k0 = 16 * s + 8 * h;
+                const bf16x8 kb = tr8(tr_addr<TF>(sK, k0, 32 * w), tr_addr<TF>(sK, k0 + 4, 32 * w));
+                Z = mfma(kb, one, Z);
 #pragma unroll
-            for (int db = 0; db < NW; ++db) {
-                const bf16x8 va = tr8(tr_addr<TD>(sV, k0, 32 * db), tr_addr<TD>(sV, k0 + 4, 32 * db));
-                X[db] = mfma(va, kb, X[db]);
+                for (int db = 0; db < NW; ++db) {
+                    const bf16x8 va = tr8(tr_addr<TD>(sV, k0, 32 * db), tr_addr<TD>(sV, k0 + 4, 32 * db));
+                    X[db] = mfma(va, kb, X[db]);
+                }
             }
-        }
-        // every staging of this chunk has read sz; only this wave reads block w
-        if (l32 == 0) {
+            // every staging of this chunk has read sz; only this wave reads block w
+            if (l32 == 0) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sz[32 * w + acc_row(r, h)] = Z[r];
+                for (int r = 0; r < 16; ++r) sz[32 * w + acc_row(r, h)] = Z[r];
+            }
         }
     }
     __syncthreads();   // the last head's sin terms are in sX
@@ -266,15 +281,18 @@ void k_bwd_q_cos_mfma(Args a) {
 // (r = Phi(Q)^T c on the matrix cores with c rounded to bf16, every column
 // of an r tile holding r).  The tiles are disjoint, so nothing crosses
 // waves; split, a wave holds 64 accumulator registers per lane instead of
-// 128 and two waves share a SIMD.
+// 128 and two waves share a SIMD.  Bidirectional: dk = R v - r can be a
+// small difference (every term goes through R), so gn and c go in as two
+// bf16 parts each (hi, then the rounding remainder).
 // ---------------------------------------------------------------------------
-template <int D, int PHI>
+template <int D, int PHI, bool CAUSAL>
 __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void k_bwd_r_cos_mfma(Args a) {
     constexpr int F = 2 * D, NW = D / 32, FBW = F / 64, NT = 4 * D;
     using TF = PadI<F>;
     using TD = PadI<D>;
     __shared__ __attribute__((aligned(16))) u16 sQ[kCc * TF::ld];
     __shared__ __attribute__((aligned(16))) u16 sG[kCc * TD::ld];
+    __shared__ __attribute__((aligned(16))) u16 sGl[CAUSAL ? 8 : kCc * TD::ld];   // gn remainders
     __shared__ __attribute__((aligned(16))) float sC[kCc];
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
@@ -310,10 +328,17 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void
                 const float inv = c0 + i < a.N ? rcp(pden[k]) : 0.f;
                 const uint4 u = rG.v[k];
                 uint32_t wds[4] = {u.x, u.y, u.z, u.w};
+                uint32_t lo[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    wds[e] = pk2(__uint_as_float(wds[e] << 16) * inv, __uint_as_float(wds[e] & 0xffff0000u) * inv);
+                for (int e = 0; e < 4; ++e) {
+                    const float x0 = __uint_as_float(wds[e] << 16) * inv, x1 = __uint_as_float(wds[e] & 0xffff0000u) * inv;
+                    wds[e] = pk2(x0, x1);
+                    if constexpr (!CAUSAL)
+                        lo[e] = pk2(x0 - __uint_as_float(wds[e] << 16), x1 - __uint_as_float(wds[e] & 0xffff0000u));
+                }
                 *reinterpret_cast<uint4 *>(sG + TD::at(i, c8)) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+                if constexpr (!CAUSAL)
+                    *reinterpret_cast<uint4 *>(sGl + TD::at(i, c8)) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
             }
             if (t < kCc) sC[t] = c0 + t < a.N ? pc : 0.f;
             __syncthreads();
@@ -334,15 +359,24 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void
                 const float4 c_lo = *reinterpret_cast<const float4 *>(sC + k0);
                 const float4 c_hi = *reinterpret_cast<const float4 *>(sC + k0 + 4);
                 const float cr[8] = {c_lo.x, c_lo.y, c_lo.z, c_lo.w, c_hi.x, c_hi.y, c_hi.z, c_hi.w};
-                bf16x8 cb;
+                bf16x8 cb, cl;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) cb[e] = (__bf16)cr[e];
+                for (int e = 0; e < 8; ++e) {
+                    cb[e] = (__bf16)cr[e];
+                    if constexpr (!CAUSAL) cl[e] = (__bf16)(cr[e] - (float)cb[e]);
+                }
+                bf16x8 gl;
+                if constexpr (!CAUSAL) gl = tr8(tr_addr<TD>(sGl, k0, 32 * vb), tr_addr<TD>(sGl, k0 + 4, 32 * vb));
 #pragma unroll
                 for (int i = 0; i < FBW; ++i) {
                     const int fb = FBW * fh + i;
                     const bf16x8 qa = tr8(tr_addr<TF>(sQ, k0, 32 * fb), tr_addr<TF>(sQ, k0 + 4, 32 * fb));
                     R[i] = mfma(qa, gb, R[i]);
-                    if (i == vb) Zr = mfma(qa, cb, Zr);   // feature block w = FBW * fh + vb
+                    if constexpr (!CAUSAL) R[i] = mfma(qa, gl, R[i]);
+                    if (i == vb) {   // feature block w = FBW * fh + vb
+                        Zr = mfma(qa, cb, Zr);
+                        if constexpr (!CAUSAL) Zr = mfma(qa, cl, Zr);
+                    }
                 }
             }
         }
@@ -369,7 +403,7 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void
 // weighted dPhi(k) tiles to the cos-half waves, which apply phi' and stage
 // dk.
 // ---------------------------------------------------------------------------
-template <int D, int PHI>
+template <int D, int PHI, bool CAUSAL>
 __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2)))
 void k_bwd_kv_cos_mfma(Args a) {
     constexpr int F = 2 * D, NW = D / 32, FW = F / 32, NT = 64 * FW;
@@ -399,7 +433,8 @@ void k_bwd_kv_cos_mfma(Args a) {
     const u16 *qbase = static_cast<const u16 *>(a.q);
     const u16 *gbase = static_cast<const u16 *>(a.g);
 
-    const float *Rp = a.ws_Rs + ((size_t)bg * (a.nseg + 1) + seg) * SD;
+    // the segment's exclusive suffix of (R, r) (causal) or the sequence total
+    const float *Rp = a.ws_Rs + ((size_t)bg * (a.nseg + 1) + (CAUSAL ? seg : a.nseg)) * SD;
     f32x16 Rt[NW];
 #pragma unroll
     for (int db = 0; db < NW; ++db)
@@ -423,9 +458,11 @@ void k_bwd_kv_cos_mfma(Args a) {
         const int c0 = row0 + (nch - 1) * kCc;
         rK.load(kh, c0, a.N);
         rV.load(vh, c0, a.N);
-        rQ.load(qbase + bh0 * a.N * D, c0, a.N);
-        rG.load(gbase + bh0 * a.N * D, c0, a.N);
-        load_dc(bh0, c0);
+        if constexpr (CAUSAL) {   // the in-chunk terms need the queries' rows
+            rQ.load(qbase + bh0 * a.N * D, c0, a.N);
+            rG.load(gbase + bh0 * a.N * D, c0, a.N);
+            load_dc(bh0, c0);
+        }
     }
     for (int ci = nch - 1; ci >= 0; --ci) {
         const int c0 = row0 + ci * kCc;
@@ -436,16 +473,19 @@ void k_bwd_kv_cos_mfma(Args a) {
         rV.template store<TD>(sV);
         rK.load(kh, cn, a.N);
         rV.load(vh, cn, a.N);
-        // R (bf16, [feature][value]) for the state terms
+        // R (bf16, [feature][value]) for the state terms (bidirectional: the
+        // total, staged once)
+        if (CAUSAL || ci == nch - 1) {
 #pragma unroll
-        for (int db = 0; db < NW; ++db)
+            for (int db = 0; db < NW; ++db)
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                float x[4];
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    float x[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = Rt[db][4 * q4 + e];
-                st4bf(sR + TD::at(32 * w + l32, 32 * db + 8 * q4 + 4 * h), x);
-            }
+                    for (int e = 0; e < 4; ++e) x[e] = Rt[db][4 * q4 + e];
+                    st4bf(sR + TD::at(32 * w + l32, 32 * db + 8 * q4 + 4 * h), x);
+                }
+        }
         // one head's query rows into LDS: Phi(Q), gn = g / den (rows past N:
         // zeros), raw g, c, 1 / den
         auto stage_head = [&]() {
@@ -470,7 +510,7 @@ void k_bwd_kv_cos_mfma(Args a) {
         // the first head is staged here, in straight-line code, with the chunk
         // (in the head loop, the wait for its rows would also wait for the K, V
         // loads just issued); the state terms read none of its tiles
-        stage_head();
+        if constexpr (CAUSAL) stage_head();
         __syncthreads();
 
         // state terms: dPhi(k)^T = R V^T - r (block w); dv^T = R^T Phi(K)^T (value block w)
@@ -478,9 +518,17 @@ void k_bwd_kv_cos_mfma(Args a) {
 #pragma unroll
         for (int db = 0; db < NW; ++db)
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-                dK = mfma(ld4x2<TD>(sR, 32 * w + l32, 32 * db + 16 * s + 4 * h),
-                          ld4x2<TD>(sV, l32, 32 * db + 16 * s + 4 * h), dK);
+            for (int s = 0; s < 2; ++s) {
+                const bf16x8 vq = ld4x2<TD>(sV, l32, 32 * db + 16 * s + 4 * h);
+                if constexpr (CAUSAL) {
+                    dK = mfma(ld4x2<TD>(sR, 32 * w + l32, 32 * db + 16 * s + 4 * h), vq, dK);   // R, as staged
+                } else {
+                    // R (total) in two bf16 parts: R v - r is a small difference
+                    // when few queries see a key
+                    dK = mfma(acc_op(Rt[db], s), vq, dK);
+                    dK = mfma(acc_lo(Rt[db], s), vq, dK);
+                }
+            }
 #pragma unroll
         for (int r = 0; r < 16; ++r) dK[r] -= sr[32 * w + acc_row(r, h)];
         if (w < NW) {
@@ -492,7 +540,8 @@ void k_bwd_kv_cos_mfma(Args a) {
             }
         }
 
-        for (int rep = 0; rep < a.nrep; ++rep) {
+        // causal: the chunk's own queries (in-chunk terms) and the R update
+        for (int rep = 0; rep < (CAUSAL ? a.nrep : 0); ++rep) {
             if (rep > 0) {
                 __syncthreads();   // the previous head's LDS reads are done
                 stage_head();
@@ -538,8 +587,10 @@ void k_bwd_kv_cos_mfma(Args a) {
                 sPop[0][l] = acc_op(P, 0);
                 sPop[1][l] = acc_op(P, 1);
             }
-            // R^T += gn^T Phi(Q) for this chunk's rows; r += Phi(Q)^T c (neither
-            // needs A or P)
+            // R^T += gn^T Phi(Q) for this chunk's rows; r += Phi(Q)^T c from the
+            // same Phi(Q) operand (lane (n, h) holds feature 32w + n of rows
+            // 16s + 8h .. +7; the two halves cover the chunk).  Neither needs A or P.
+            float racc = 0.f;
 #pragma unroll
             for (int s = 0; s < kCc / 16; ++s) {
                 const int k0 = 16 * s + 8 * h;
@@ -549,20 +600,14 @@ void k_bwd_kv_cos_mfma(Args a) {
                     const bf16x8 ga = tr8(tr_addr<TD>(sG, k0, 32 * db), tr_addr<TD>(sG, k0 + 4, 32 * db));
                     Rt[db] = mfma(ga, qb, Rt[db]);
                 }
-            }
-            {   // r += Phi(Q)^T c: feature 32w + n, rows 16h .. 16h+15 per lane
-                float acc = 0.f;
+                const float4 c0v = *reinterpret_cast<const float4 *>(sCc + k0);
+                const float4 c1v = *reinterpret_cast<const float4 *>(sCc + k0 + 4);
+                const float cv[8] = {c0v.x, c0v.y, c0v.z, c0v.w, c1v.x, c1v.y, c1v.z, c1v.w};
 #pragma unroll
-                for (int j = 0; j < kCc / 8; ++j) {
-                    const float4 cv = *reinterpret_cast<const float4 *>(sCc + 16 * h + 4 * j);
-                    const float c4[4] = {cv.x, cv.y, cv.z, cv.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        acc += c4[e] * bf2f(sQ[TF::at(16 * h + 4 * j + e, 32 * w + l32)]);
-                }
-                acc = sum_halves(acc);
-                if (h == 0) sr[32 * w + l32] += acc;
+                for (int e = 0; e < 8; ++e) racc += cv[e] * (float)qb[e];
             }
+            racc = sum_halves(racc);
+            if (h == 0) sr[32 * w + l32] += racc;
             __syncthreads();   // the A and P operands are in LDS
             // in-chunk terms: dPhi(k)^T += Phi(Q)^T P (block w), dv^T += gn^T A (value block w)
 #pragma unroll
@@ -601,20 +646,20 @@ void k_bwd_kv_cos_mfma(Args a) {
     }
 }
 
-template <int D, int PHI>
+template <int D, int PHI, bool CAUSAL>
 hipError_t run(const Args &a, hipStream_t s) {
     constexpr int F = 2 * D;
     const unsigned n_units = (unsigned)(a.B * a.Hkv);
     const size_t SD = (size_t)F * D + F;
-    hipError_t e = a.state_ready ? hipSuccess : mfma_state_run(a, PHI, 1, s);
+    hipError_t e = a.state_ready ? hipSuccess : mfma_state_run(a, PHI, CAUSAL ? 1 : 0, s);
     if (e != hipSuccess) return e;
     {
-        TimedLaunch tl("k_bwd_q_cos_mfma", s);
-        hipLaunchKernelGGL((k_bwd_q_cos_mfma<D, PHI>), dim3(n_units * a.nseg), dim3(4 * D), 0, s, a);
+        TimedLaunch tl(CAUSAL ? "k_bwd_q_cos_mfma" : "k_bwd_q_cos_bidir_mfma", s);
+        hipLaunchKernelGGL((k_bwd_q_cos_mfma<D, PHI, CAUSAL>), dim3(n_units * a.nseg), dim3(4 * D), 0, s, a);
     }
     {
-        TimedLaunch tl("k_bwd_r_cos_mfma", s);
-        hipLaunchKernelGGL((k_bwd_r_cos_mfma<D, PHI>), dim3(n_units * a.nseg), dim3(4 * D), 0, s, a);
+        TimedLaunch tl(CAUSAL ? "k_bwd_r_cos_mfma" : "k_bwd_r_cos_bidir_mfma", s);
+        hipLaunchKernelGGL((k_bwd_r_cos_mfma<D, PHI, CAUSAL>), dim3(n_units * a.nseg), dim3(4 * D), 0, s, a);
     }
     {
         TimedLaunch tl("k_scan_R", s);
@@ -623,25 +668,26 @@ hipError_t run(const Args &a, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     {
-        TimedLaunch tl("k_bwd_kv_cos_mfma", s);
-        hipLaunchKernelGGL((k_bwd_kv_cos_mfma<D, PHI>), dim3(n_units * a.nseg), dim3(4 * D), 0, s, a);
+        TimedLaunch tl(CAUSAL ? "k_bwd_kv_cos_mfma" : "k_bwd_kv_cos_bidir_mfma", s);
+        hipLaunchKernelGGL((k_bwd_kv_cos_mfma<D, PHI, CAUSAL>), dim3(n_units * a.nseg), dim3(4 * D), 0, s, a);
     }
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool CAUSAL>
 hipError_t by_phi(const Args &a, int phi, hipStream_t s) {
     switch (phi) {
-        case kElu1: return run<D, kElu1>(a, s);
-        case kRelu: return run<D, kRelu>(a, s);
-        default: return run<D, kIdentity>(a, s);
+        case kElu1: return run<D, kElu1, CAUSAL>(a, s);
+        case kRelu: return run<D, kRelu, CAUSAL>(a, s);
+        default: return run<D, kIdentity, CAUSAL>(a, s);
     }
 }
 
 }  // namespace
 
-hipError_t mfma_bwd_cos_run(const Args &a, int phi, hipStream_t s) {
-    return a.D == 64 ? by_phi<64>(a, phi, s) : by_phi<128>(a, phi, s);
+hipError_t mfma_bwd_cos_run(const Args &a, int phi, int causal, hipStream_t s) {
+    if (causal) return a.D == 64 ? by_phi<64, true>(a, phi, s) : by_phi<128, true>(a, phi, s);
+    return a.D == 64 ? by_phi<64, false>(a, phi, s) : by_phi<128, false>(a, phi, s);
 }
 
 }  // namespace la

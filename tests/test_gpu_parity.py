@@ -77,6 +77,22 @@ def test_edge_lengths(N, causal):
             grad_blocks=N > 1)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_bidir_cos_gqa_many_segments(D):
+    """The bidirectional cos/sin backward on the matrix cores: GQA (n_rep = 4),
+    elu+1, 1100 rows (a ragged tail), at the automatic split and with a
+    segment boundary every 64 rows (17 per-segment records in each scan)."""
+    torch, la = gpu_or_skip()
+    B, H, Hkv, N = 1, 8, 2, 1100
+    t = make(B, H, Hkv, N, D, "bf16", scale=0.5, cos=True, seed=40 + D)
+    say("bidir cos gqa D=%d" % D)
+    ref = oracle_on(t, False, "elu+1")
+    for seg_len in (0, 64):
+        out, grads = run_gpu(la, t, False, "elu+1", seg_len=seg_len)
+        compare(t, out, grads, ref[0], ref[1], "bf16", H, Hkv,
+                label="bidir-cos-gqa-D%d-seg%d" % (D, seg_len))
+
+
 SPAN = [(128, True, 4, 4), (128, False, 8, 4), (128, True, 8, 2)]
 
 
@@ -241,7 +257,7 @@ def test_binding_errors_on_gpu():
 
 def test_kernel_family_per_case():
     """bf16 runs on the matrix-core kernels (causal and bidirectional, forward
-    and backward; the cos/sin backward when causal); float32 bidirectional
+    and backward, with and without cos/sin); float32 bidirectional
     without cos/sin at D = 64 and 128 on the float32 matrix-core kernels, other
     float32 cases on
     the vector-ALU kernels (checked through the library's launch timing)."""
@@ -287,6 +303,14 @@ def test_kernel_family_per_case():
     finally:
         la.timing_enable(False)
     assert {"k_bwd_q_cos_mfma", "k_bwd_r_cos_mfma", "k_bwd_kv_cos_mfma"} <= names, names
+    t = make(1, 4, 2, 300, 128, "bf16", cos=True, seed=3)
+    la.timing_enable(True)
+    try:
+        run_gpu(la, t, False, "relu", backward=True)
+        names = set(la.timing_collect())
+    finally:
+        la.timing_enable(False)
+    assert {"k_bwd_q_cos_bidir_mfma", "k_bwd_r_cos_bidir_mfma", "k_bwd_kv_cos_bidir_mfma"} <= names, names
     for D in (64, 128):
         t = make(1, 4, 2, 300, D, "f32", seed=2)
         la.timing_enable(True)
