@@ -48,8 +48,9 @@ constexpr int kCb = 32;   // backward chunk length: one 32x32 tile per head
 
 // ---------------------------------------------------------------------------
 // k_bwd_q_mfma: forward over the 32-row chunks of one (batch, KV head,
-// segment).  Waves 0 .. D/32-1 ("state waves") hold S^T and z and produce
-// dq; waves D/32 .. 2D/32-1 ("R waves") accumulate the segment's
+// segment).  Waves 0 .. D/32-1 ("state waves") hold S^T (z lives in LDS,
+// each state wave adding its block's chunk sums) and produce dq; waves
+// D/32 .. 2D/32-1 ("R waves") accumulate the segment's
 // R = sum_i Phi(q_i) gn_i^T (feature block w - D/32 x all value blocks) and
 // r = sum_i c_i Phi(q_i), summed over the group's query heads.  Per chunk and
 // head the first two R waves also compute the 32x32 tiles A^T (with the
@@ -95,19 +96,17 @@ void k_bwd_q_mfma(Args a, int qm_arg) {
     const u16 *gbase = static_cast<const u16 *>(a.g);
     u16 *dqbase = static_cast<u16 *>(a.dq);
 
-    // state waves: S^T tiles (value block db x feature block w), z tile (block w),
-    // the segment's exclusive prefix (causal) or the sequence total
+    // state waves: S^T tiles (value block db x feature block w), the
+    // segment's exclusive prefix (causal) or the sequence total
     // R waves: R tiles (feature block wr x value block db)
     const float *Sp = a.ws_S + ((size_t)bg * (a.nseg + 1) + (CAUSAL ? seg0 : a.nseg)) * SD;
-    f32x16 X[NW], Z = zero16();
+    f32x16 X[NW];
     if (state_wave) {
 #pragma unroll
         for (int db = 0; db < NW; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 X[db][r] = Sp[(size_t)(32 * w + l32) * D + 32 * db + acc_row(r, h)];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Z[r] = Sp[(size_t)F * D + 32 * w + acc_row(r, h)];
     } else {
 #pragma unroll
         for (int db = 0; db < NW; ++db) X[db] = zero16();
@@ -117,7 +116,7 @@ void k_bwd_q_mfma(Args a, int qm_arg) {
     const bf16x8 one = ones8();
 
     const int row0 = seg0 * a.L, row1 = min(row0 + qm * a.L, a.N);
-    RawTile<D, NT, kCb> rK, rV, rQ, rG;
+    RawTile<D, NT, kCb, true> rK, rV, rQ, rG;
     if constexpr (CAUSAL) {
         rK.load(kh, row0, a.N);
         rV.load(vh, row0, a.N);
@@ -321,12 +320,14 @@ void k_bwd_q_mfma(Args a, int qm_arg) {
                 }
             }
             if (CAUSAL && state_wave) {
-                // carry (S^T, z) past this chunk
+                // carry (S^T, z) past this chunk: z gets the chunk's sum of its
+                // block (every column of Zc holds it)
+                f32x16 Zc = zero16();
 #pragma unroll
                 for (int s = 0; s < kCb / 16; ++s) {
                     const int k0 = 16 * s + 8 * h;
                     const bf16x8 kb = tr8(tr_addr<TF>(sK, k0, 32 * w), tr_addr<TF>(sK, k0 + 4, 32 * w));
-                    Z = mfma(kb, one, Z);
+                    Zc = mfma(kb, one, Zc);
 #pragma unroll
                     for (int db = 0; db < NW; ++db) {
                         const bf16x8 va = tr8(tr_addr<TD>(sV, k0, 32 * db), tr_addr<TD>(sV, k0 + 4, 32 * db));
@@ -334,10 +335,11 @@ void k_bwd_q_mfma(Args a, int qm_arg) {
                     }
                 }
                 // every staging of this chunk has read sz (each preceded a barrier
-                // this wave has passed), so it can take the new z now
+                // this wave has passed), and only this wave reads block w in its
+                // dq epilogue, so it can take the new z now
                 if (l32 == 0) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) sz[32 * w + acc_row(r, h)] = Z[r];
+                    for (int r = 0; r < 16; ++r) sz[32 * w + acc_row(r, h)] += Zc[r];
                 }
             }
         }
