@@ -108,7 +108,7 @@ void k_bwd_q_cos_mfma(Args a) {
     int step = 0;   // (chunk, head) steps so far: sX buffer parity
 
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
-    RawTile<D, NT, kCc> rK, rV, rQ, rG;
+    RawTile<D, NT, kCc, true> rK, rV, rQ, rG;
     if constexpr (CAUSAL) {   // the in-chunk terms and the carry need the keys
         rK.load(kh, row0, a.N);
         rV.load(vh, row0, a.N);
