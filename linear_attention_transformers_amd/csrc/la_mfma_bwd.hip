@@ -112,7 +112,8 @@ void k_bwd_q_mfma(Args a, int qm_arg) {
         for (int db = 0; db < NW; ++db) X[db] = zero16();
     }
     for (int e = t; e < F; e += NT) sz[e] = Sp[(size_t)F * D + e];
-    f32x16 Rr = zero16();   // R waves: r of feature block wr in every column
+    // R waves: this lane's part of r for feature 32 wr + l32 (rows of its half)
+    float racc = 0.f;
     const bf16x8 one = ones8();
 
     const int row0 = seg0 * a.L, row1 = min(row0 + qm * a.L, a.N);
@@ -280,8 +281,9 @@ void k_bwd_q_mfma(Args a, int qm_arg) {
                     const float iq = sInv[l32];
                     if (h == 0) sCw[wr][l32] = ok ? gsum * iq * iq : 0.f;
                     // R (feature block wr x every value block) += (Phi(Q) / den)^T G,
-                    // r (feature block wr) += Phi(Q)^T c: c in two bf16 parts as the
-                    // B operand of every column, so each column of Rr holds r
+                    // r (feature block wr) += Phi(Q)^T c in fp32 from the same Phi(Q)
+                    // operand: lane (n, h) holds feature 32 wr + n of rows
+                    // 16s + 8h .. +7, so the two halves together cover the chunk
 #pragma unroll
                     for (int s = 0; s < kCb / 16; ++s) {
                         const int k0 = 16 * s + 8 * h;
@@ -290,14 +292,8 @@ void k_bwd_q_mfma(Args a, int qm_arg) {
                             const float4 c0v = *reinterpret_cast<const float4 *>(&sCw[wr][k0]);
                             const float4 c1v = *reinterpret_cast<const float4 *>(&sCw[wr][k0 + 4]);
                             const float cv[8] = {c0v.x, c0v.y, c0v.z, c0v.w, c1v.x, c1v.y, c1v.z, c1v.w};
-                            bf16x8 chi, clo;
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                chi[e] = (__bf16)cv[e];
-                                clo[e] = (__bf16)(cv[e] - (float)chi[e]);
-                            }
-                            Rr = mfma(qa, chi, Rr);
-                            Rr = mfma(qa, clo, Rr);
+                            for (int e = 0; e < 8; ++e) racc += cv[e] * (float)qa[e];
                         }
                         const float4 i0 = *reinterpret_cast<const float4 *>(sInv + k0);
                         const float4 i1 = *reinterpret_cast<const float4 *>(sInv + k0 + 4);
@@ -354,11 +350,9 @@ void k_bwd_q_mfma(Args a, int qm_arg) {
                     Ro[(size_t)(32 * wr + acc_row(r, h)) * D + 32 * db + l32] = X[db][r];
                 X[db] = zero16();
             }
-            if (l32 == 0) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) Ro[(size_t)F * D + 32 * wr + acc_row(r, h)] = Rr[r];
-            }
-            Rr = zero16();
+            const float rt = sum_halves(racc);
+            if (h == 0) Ro[(size_t)F * D + 32 * wr + l32] = rt;
+            racc = 0.f;
         }
     }
 }
