@@ -30,8 +30,9 @@
 // each wave owns a 32-wide block of the feature columns of the state (S^T in
 // the q-kernel, R^T in the kv-kernel), of dPhi(q) / dPhi(k), and of the value
 // columns of dv.  The only cross-wave reduction, Phi(q_i).U_i over the
-// feature blocks, goes through LDS in a fixed order.  In the q-kernel a second set of waves accumulates the
-// segment's (R, r) so the two register-heavy states live in different waves.
+// feature blocks, goes through LDS in a fixed order.  In the q-kernel a
+// second set of waves accumulates the segment's (R, r) so the two
+// register-heavy states live in different waves.
 #include <atomic>
 
 #include "la_common.h"
@@ -55,7 +56,7 @@ constexpr int kCb = 32;   // backward chunk length: one 32x32 tile per head
 // r = sum_i c_i Phi(q_i), summed over the group's query heads.  Per chunk and
 // head the first two R waves also compute the 32x32 tiles A^T (with the
 // denominators) and T^T and pass them to the state waves through LDS, which
-// meanwhile form U = S g: the state waves' chain is the kernel's critical path.
+// meanwhile form U = S g (the A wave's chain is the longer of the two).
 // After that exchange (one barrier) the two wave kinds run independently: the
 // R update needs only 1/den, and the R waves recompute c for r.
 // ---------------------------------------------------------------------------

@@ -1,5 +1,5 @@
-// la_mfma_bwd_cos.hip -- bf16 causal backward with the cos/sin features
-// (F = 2D) on the gfx950 matrix cores.
+// la_mfma_bwd_cos.hip -- bf16 backward with the cos/sin features (F = 2D)
+// on the gfx950 matrix cores, causal and bidirectional.
 //
 // The derivative is the one of la_mfma_bwd.hip (SVD_linear_Attention,
 // "Module neuralops.core.triton_kernels.linear_attn", function bwd; module
@@ -13,8 +13,12 @@
 // dPhi meet through LDS.  With every wave busy with its own state, the
 // per-segment (R, r) sums get a pass of their own (k_bwd_r_cos_mfma) between
 // the dq and the dk/dv kernels; it reads the den_i and c_i the dq kernel
-// writes.  Each wave computes the chunk's A (over the F features) and T
-// tiles itself.
+// writes.  Causal: per chunk and head wave 0 forms the A tile (over the F
+// features) and wave 1 the T (or P) tile for the workgroup.  Bidirectional
+// (CAUSAL = false): every term goes through the total state; there are no
+// in-chunk tiles or carries, and the products whose results can be small
+// differences take two bf16 parts (S for U, gn and c in the R pass, R for
+// R v in dk).
 #include "la_common.h"
 #include "la_kernels.h"
 #include "la_mfma.h"
