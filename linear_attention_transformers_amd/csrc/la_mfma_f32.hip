@@ -179,7 +179,8 @@ __global__ __launch_bounds__(kNT) void k_state_f32(Args a) {
 // each iteration's RB x D output; its slice of S is held as B operands.
 // ---------------------------------------------------------------------------
 template <int D, int PHI>
-__global__ __launch_bounds__(kNT) void k_fwd_bidir_f32(Args a) {
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1)))
+void k_fwd_bidir_f32(Args a) {
     constexpr int RB = rows_blk<D>(), NB = D / 32, LDQ = D + 2;   // Phi(Q) read by column
     __shared__ __attribute__((aligned(16))) float sQ[RB * LDQ];
     __shared__ float sz[D];
@@ -224,8 +225,14 @@ __global__ __launch_bounds__(kNT) void k_fwd_bidir_f32(Args a) {
 //   R += Phi(Q)^T (G / den) (wave: feature block fr, value blocks),
 //   r += Phi(Q)^T c (the wave of value block 0).
 // ---------------------------------------------------------------------------
+// Waves per SIMD the dq kernel is built for: at D = 64 its registers fit
+// two (the compiler, left free, takes a few more than 256 and gets one).
+template <int D>
+constexpr int q_f32_waves() { return D == 64 ? 2 : 1; }
+
 template <int D, int PHI>
-__global__ __launch_bounds__(kNT) void k_bwd_q_bidir_f32(Args a) {
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(q_f32_waves<D>())))
+void k_bwd_q_bidir_f32(Args a) {
     constexpr int RB = rows_blk<D>(), NB = D / 32, VBW = NB * NB / 4;
     constexpr int LDC = D + 2;    // read by column (U's A operand) and by row (R's operands)
     __shared__ __attribute__((aligned(16))) float sQ[RB * LDC];
@@ -330,7 +337,8 @@ __global__ __launch_bounds__(kNT) void k_bwd_q_bidir_f32(Args a) {
 // its slices of R are held as B operands.
 // ---------------------------------------------------------------------------
 template <int D, int PHI>
-__global__ __launch_bounds__(kNT) void k_bwd_kv_bidir_f32(Args a) {
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1)))
+void k_bwd_kv_bidir_f32(Args a) {
     constexpr int RB = rows_blk<D>(), NB = D / 32, LDC = D + 2;   // both read by column
     __shared__ __attribute__((aligned(16))) float sK[RB * LDC];
     __shared__ __attribute__((aligned(16))) float sV[RB * LDC];
