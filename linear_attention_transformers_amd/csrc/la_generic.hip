@@ -132,22 +132,23 @@ __global__ __launch_bounds__(kNT) void k_state(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_scan_S: per (batch, KV head) and state element, replace the per-segment
-// sums by their exclusive prefix over segments (slot s = rows before segment
-// s) and, with `total`, store the total in slot nseg (without it the last
-// segment's record is neither read nor needed).  Fixed order: deterministic.
-// The records of kScanB segments are loaded before any of their slots is
-// written, so a thread waits for memory once per kScanB segments, not once
-// per segment.
+// k_scan_S: per (batch, KV head) and state element, over the per-segment
+// sums in slots 0 .. nseg-1.  Causal: replace them by their exclusive prefix
+// over segments (slot s = rows before segment s; the last segment's record is
+// neither read nor needed).  Bidirectional: store their total in slot nseg
+// and leave the per-segment slots as they are (only the total is read).
+// Fixed order: deterministic.  The records of kScanB segments are loaded
+// before any of their slots is written, so a thread waits for memory once
+// per kScanB segments, not once per segment.
 // ---------------------------------------------------------------------------
 constexpr int kScanB = 8;
 
-__global__ __launch_bounds__(kNT) void k_scan_S(float *ws, int nseg, size_t SD, size_t n_units, int total) {
+__global__ __launch_bounds__(kNT) void k_scan_S(float *ws, int nseg, size_t SD, size_t n_units, int causal) {
     const size_t e = (size_t)blockIdx.x * kNT + threadIdx.x;
     const size_t unit = blockIdx.y;
     if (e >= SD || unit >= n_units) return;
     float *base = ws + unit * (nseg + 1) * SD + e;
-    const int nin = total ? nseg : nseg - 1;   // records that exist
+    const int nin = causal ? nseg - 1 : nseg;   // records that are summed
     float run = 0.f;
     for (int s0 = 0; s0 < nseg; s0 += kScanB) {
         float x[kScanB];
@@ -156,21 +157,24 @@ __global__ __launch_bounds__(kNT) void k_scan_S(float *ws, int nseg, size_t SD, 
 #pragma unroll
         for (int i = 0; i < kScanB; ++i) {
             if (s0 + i < nseg) {
-                base[(size_t)(s0 + i) * SD] = run;
+                if (causal) base[(size_t)(s0 + i) * SD] = run;
                 run += x[i];
             }
         }
     }
-    if (total) base[(size_t)nseg * SD] = run;
+    if (!causal) base[(size_t)nseg * SD] = run;
 }
 
 // ---------------------------------------------------------------------------
 // k_scan_R: per (batch, KV head), sum the per-head partials (R, r) of the
-// n_rep query heads (order 0..n_rep-1) and form the exclusive suffix over
-// segments (slot s = rows after segment s); total in slot nseg.
+// n_rep query heads (order 0..n_rep-1).  Causal: the exclusive suffix over
+// segments (slot s = rows after segment s).  Bidirectional: the total, in
+// slot nseg only.  kScanB segments' records are loaded together, from
+// clamped (existing) slots with no branch around the loads: under a branch
+// each load was followed by its own wait.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kNT) void k_scan_R(const float *Rp, float *Rs, int nseg, size_t SD,
-                                                int H, int Hkv, int nrep, size_t n_units) {
+                                                int H, int Hkv, int nrep, size_t n_units, int causal) {
     const size_t e = (size_t)blockIdx.x * kNT + threadIdx.x;
     const size_t unit = blockIdx.y;  // b * Hkv + g
     if (e >= SD || unit >= n_units) return;
@@ -185,19 +189,21 @@ __global__ __launch_bounds__(kNT) void k_scan_R(const float *Rp, float *Rs, int 
 #pragma unroll
         for (int i = 0; i < kScanB; ++i) x[i] = 0.f;
         for (int r = 0; r < nrep; ++r) {
+            float y[kScanB];
 #pragma unroll
-            for (int i = 0; i < kScanB; ++i)
-                if (s0 - i >= 0) x[i] += in[((size_t)r * nseg + (s0 - i)) * SD];
+            for (int i = 0; i < kScanB; ++i) y[i] = in[((size_t)r * nseg + max(s0 - i, 0)) * SD];
+#pragma unroll
+            for (int i = 0; i < kScanB; ++i) x[i] += s0 - i >= 0 ? y[i] : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < kScanB; ++i) {
             if (s0 - i >= 0) {
-                out[(size_t)(s0 - i) * SD] = run;
+                if (causal) out[(size_t)(s0 - i) * SD] = run;
                 run += x[i];
             }
         }
     }
-    out[(size_t)nseg * SD] = run;
+    if (!causal) out[(size_t)nseg * SD] = run;
 }
 
 // ---------------------------------------------------------------------------
@@ -736,7 +742,7 @@ hipError_t run_fwd(const Args &a, int causal, hipStream_t s) {
     {
         TimedLaunch tl("k_scan_S", s);
         hipLaunchKernelGGL(k_scan_S, scan_grid, dim3(kNT), 0, s, a.ws_S, a.nseg, SD,
-                           (size_t)n_units, 1);
+                           (size_t)n_units, causal);
     }
     if (causal) {
         TimedLaunch tl("k_fwd_causal", s);
@@ -763,7 +769,7 @@ hipError_t run_bwd(const Args &a, int causal, hipStream_t s) {
         }
         TimedLaunch tl("k_scan_S", s);
         hipLaunchKernelGGL(k_scan_S, scan_grid, dim3(kNT), 0, s, a.ws_S, a.nseg, SD,
-                           (size_t)n_units, 1);
+                           (size_t)n_units, causal);
     }
     if (causal) {
         TimedLaunch tl("k_bwd_q_causal", s);
@@ -775,7 +781,7 @@ hipError_t run_bwd(const Args &a, int causal, hipStream_t s) {
     {
         TimedLaunch tl("k_scan_R", s);
         hipLaunchKernelGGL(k_scan_R, scan_grid, dim3(kNT), 0, s, (const float *)a.ws_Rp, a.ws_Rs,
-                           a.nseg, SD, a.H, a.Hkv, a.nrep, (size_t)n_units);
+                           a.nseg, SD, a.H, a.Hkv, a.nrep, (size_t)n_units, causal);
     }
     if (causal) {
         TimedLaunch tl("k_bwd_kv_causal", s);
@@ -815,16 +821,16 @@ hipError_t by_shape(const Args &a, int bwd, int causal, int phi, hipStream_t s) 
 
 }  // namespace
 
-hipError_t scan_state(float *ws, int nseg, size_t SD, unsigned n_units, bool total, hipStream_t s) {
+hipError_t scan_state(float *ws, int nseg, size_t SD, unsigned n_units, bool causal, hipStream_t s) {
     hipLaunchKernelGGL(k_scan_S, dim3((unsigned)((SD + kNT - 1) / kNT), n_units), dim3(kNT), 0, s,
-                       ws, nseg, SD, (size_t)n_units, total ? 1 : 0);
+                       ws, nseg, SD, (size_t)n_units, causal ? 1 : 0);
     return hipGetLastError();
 }
 
 hipError_t scan_suffix(const float *Rp, float *Rs, int nseg, size_t SD, int H, int Hkv, int nrep,
-                       unsigned n_units, hipStream_t s) {
+                       unsigned n_units, bool causal, hipStream_t s) {
     hipLaunchKernelGGL(k_scan_R, dim3((unsigned)((SD + kNT - 1) / kNT), n_units), dim3(kNT), 0, s,
-                       Rp, Rs, nseg, SD, H, Hkv, nrep, (size_t)n_units);
+                       Rp, Rs, nseg, SD, H, Hkv, nrep, (size_t)n_units, causal ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -10,17 +10,18 @@ namespace la {
 // Float32 vector-ALU path: every dtype / D / mode / feature map.
 hipError_t generic_run(const Args &a, int bf16, int bwd, int causal, int phi, hipStream_t s);
 
-// In-place exclusive prefix over segments of per-segment state records
-// ([n_units][nseg + 1][SD] floats; slot nseg receives the total).
-// total: also use the last segment's record and write the total slot (else
-// the last record is not read: the exclusive prefixes do not include it).
-hipError_t scan_state(float *ws, int nseg, size_t SD, unsigned n_units, bool total, hipStream_t s);
+// Per-segment state records ([n_units][nseg + 1][SD] floats, segment s in
+// slot s).  causal: replaced in place by their exclusive prefix over segments
+// (the last segment's record is not read).  Bidirectional: their total into
+// slot nseg (the per-segment slots are left as they are).
+hipError_t scan_state(float *ws, int nseg, size_t SD, unsigned n_units, bool causal, hipStream_t s);
 
-// Exclusive suffix over segments of per-segment (R, r) records
-// ([H units][nseg][SD], n_rep consecutive units summed per output unit) into
-// [n_units][nseg + 1][SD]; slot nseg receives the total.
+// Per-segment (R, r) records ([H units][nseg][SD], n_rep consecutive units
+// summed per output unit) into [n_units][nseg + 1][SD]: causal, the exclusive
+// suffix over segments in slots 0 .. nseg-1; bidirectional, the total in slot
+// nseg.
 hipError_t scan_suffix(const float *Rp, float *Rs, int nseg, size_t SD, int H, int Hkv, int nrep,
-                       unsigned n_units, hipStream_t s);
+                       unsigned n_units, bool causal, hipStream_t s);
 
 // bf16 matrix-core kernels, causal and bidirectional (one workgroup per
 // batch, KV head, segment).

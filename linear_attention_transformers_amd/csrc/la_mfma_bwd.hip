@@ -677,7 +677,7 @@ hipError_t run(const Args &a, hipStream_t s) {
     {
         TimedLaunch tl("k_scan_R", s);
         // per-segment records are already summed over the group's heads
-        e = scan_suffix(a.ws_Rp, a.ws_Rs, a.nseg, SD, a.Hkv, a.Hkv, 1, n_units, s);
+        e = scan_suffix(a.ws_Rp, a.ws_Rs, a.nseg, SD, a.Hkv, a.Hkv, 1, n_units, CAUSAL, s);
         if (e != hipSuccess) return e;
     }
     {

@@ -397,7 +397,7 @@ hipError_t run_fwd(const Args &a, hipStream_t s) {
     hipError_t e;
     {
         TimedLaunch tl("k_scan_S", s);
-        e = scan_state(a.ws_S, a.nseg, (size_t)D * D + D, n_units, true, s);
+        e = scan_state(a.ws_S, a.nseg, (size_t)D * D + D, n_units, false, s);
     }
     if (e != hipSuccess) return e;
     TimedLaunch tl("k_fwd_bidir_f32", s);
@@ -417,7 +417,7 @@ hipError_t run_bwd(const Args &a, hipStream_t s) {
             hipLaunchKernelGGL((k_state_f32<D, PHI>), dim3(n_units * a.nseg), dim3(kNT), 0, s, a);
         }
         TimedLaunch tl("k_scan_S", s);
-        e = scan_state(a.ws_S, a.nseg, SD, n_units, true, s);
+        e = scan_state(a.ws_S, a.nseg, SD, n_units, false, s);
         if (e != hipSuccess) return e;
     }
     {
@@ -427,7 +427,7 @@ hipError_t run_bwd(const Args &a, hipStream_t s) {
     }
     {
         TimedLaunch tl("k_scan_R", s);
-        e = scan_suffix(a.ws_Rp, a.ws_Rs, a.nseg, SD, a.H, a.Hkv, a.nrep, n_units, s);
+        e = scan_suffix(a.ws_Rp, a.ws_Rs, a.nseg, SD, a.H, a.Hkv, a.nrep, n_units, false, s);
     }
     if (e != hipSuccess) return e;
     TimedLaunch tl("k_bwd_kv_bidir_f32", s);

@@ -575,7 +575,7 @@ hipError_t run_state(const Args &a, bool causal, hipStream_t s) {
                            nseg_run);
     }
     TimedLaunch tl("k_scan_S", s);
-    return scan_state(a.ws_S, a.nseg, (size_t)F * D + F, n_units, !causal, s);
+    return scan_state(a.ws_S, a.nseg, (size_t)F * D + F, n_units, causal, s);
 }
 
 template <int D, int F, int PHI, bool COS>
