@@ -21,6 +21,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "la_common.h"
 
 namespace la {
@@ -300,13 +302,14 @@ struct RawTile {
     // Features: phi, then with COS [cos_t phi, sin_t phi] (row width 2D),
     // rounded to bf16.  With QZ, also sQZ[r] = Phi(x_r) . z (features before
     // rounding, fp32; fixed-order register reduction across the V8 threads of
-    // a row).  Branch-free per element: rows >= N hold zeros (load) and phi
-    // of them is finite; only a ragged tile (uniform test) multiplies them
-    // by a 0/1 row factor.
-    template <int PHI, bool COS, class L, bool QZ>
+    // a row).  With a layout LP, also phi itself (unweighted, bf16, row width
+    // D) into dphi, for phi' in a backward.  Branch-free per element: rows
+    // >= N hold zeros (load) and phi of them is finite; only a ragged tile
+    // (uniform test) multiplies them by a 0/1 row factor.
+    template <int PHI, bool COS, class L, bool QZ, class LP = void>
     __device__ __forceinline__ void store_feat(u16 *dst, int c0, int N, const float *cw,
                                                const float *sw, const float *sz,
-                                               float *sQZ) const {
+                                               float *sQZ, u16 *dphi = nullptr) const {
         const bool ragged = c0 + C > N;
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
@@ -326,6 +329,11 @@ struct RawTile {
             }
             const float m0 = COS ? cw[tc] : 1.f;
             uint32_t o[4];
+            if constexpr (!std::is_void_v<LP>) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = pk2(f[2 * e], f[2 * e + 1]);
+                *reinterpret_cast<uint4 *>(dphi + LP::at(r, c8)) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = COS ? pk2(m0 * f[2 * e], m0 * f[2 * e + 1]) : pk2(f[2 * e], f[2 * e + 1]);
             *reinterpret_cast<uint4 *>(dst + L::at(r, c8)) = make_uint4(o[0], o[1], o[2], o[3]);

@@ -31,13 +31,6 @@ using namespace mf;
 
 constexpr int kCc = 32;   // chunk length: one 32x32 tile of A per head
 
-// phi' of a raw bf16 input (the modulated features do not give it back);
-// the gradients it scales are rounded to bf16.
-template <int PHI>
-__device__ __forceinline__ float phi_d_raw(float x) {
-    if constexpr (PHI == kElu1) return x > 0.f ? 1.f : __expf(x);
-    else return phi_d<PHI>(x);
-}
 
 // ---------------------------------------------------------------------------
 // k_bwd_q_cos_mfma: forward over the 32-row chunks of one (batch, KV head,
@@ -58,7 +51,7 @@ void k_bwd_q_cos_mfma(Args a) {
     __shared__ __attribute__((aligned(16))) u16 sK[kCc * TF::ld];
     __shared__ __attribute__((aligned(16))) u16 sV[kCc * TD::ld];
     __shared__ __attribute__((aligned(16))) u16 sQ[kCc * TF::ld];
-    __shared__ __attribute__((aligned(16))) u16 sQr[kCc * TD::ld];   // raw q rows, for phi'
+    __shared__ __attribute__((aligned(16))) u16 sQr[kCc * TD::ld];   // phi(q) rows (unweighted), for phi'
     __shared__ __attribute__((aligned(16))) u16 sG[kCc * TD::ld];
     __shared__ __attribute__((aligned(16))) float sz[F];
     __shared__ __attribute__((aligned(16))) float sX[2][NW][64 * 16];   // sin halves' dq terms, by head parity
@@ -132,15 +125,13 @@ void k_bwd_q_cos_mfma(Args a) {
         // the first head's rows are staged here, in straight-line code (in the
         // head loop, the wait for them would also wait for the K, V loads
         // just issued: the loop header merges the later heads' path)
-        rQ.template store_feat<PHI, true, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
-        rQ.template store<TD>(sQr);
+        rQ.template store_feat<PHI, true, TF, true, TD>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ, sQr);
         rG.template store<TD>(sG);
         for (int rep = 0; rep < a.nrep; ++rep) {
             const size_t bh = bh0 + rep;
             if (rep > 0) {
                 __syncthreads();
-                rQ.template store_feat<PHI, true, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
-                rQ.template store<TD>(sQr);
+                rQ.template store_feat<PHI, true, TF, true, TD>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ, sQr);
                 rG.template store<TD>(sG);
             }
             __syncthreads();
@@ -240,7 +231,7 @@ void k_bwd_q_cos_mfma(Args a) {
                 float qr[4];
                 ld4f(sQr + TD::at(l32, 32 * (w % NW) + 8 * q4 + 4 * h), qr);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) Qd[4 * q4 + e] *= phi_d_raw<PHI>(qr[e]);
+                for (int e = 0; e < 4; ++e) Qd[4 * q4 + e] *= phi_d_feat<PHI>(qr[e]);
             }
             const int buf = step & 1;
             if (w >= NW) put_acc(sX[buf][w - NW], Qd);
@@ -414,7 +405,7 @@ void k_bwd_kv_cos_mfma(Args a) {
     using TF = PadI<F>;
     using TD = PadI<D>;
     __shared__ __attribute__((aligned(16))) u16 sK[kCc * TF::ld];
-    __shared__ __attribute__((aligned(16))) u16 sKr[kCc * TD::ld];   // raw k (phi'), then dk rows
+    __shared__ __attribute__((aligned(16))) u16 sKr[kCc * TD::ld];   // phi(k) rows (phi'), then dk rows
     __shared__ __attribute__((aligned(16))) u16 sV[kCc * TD::ld];
     __shared__ __attribute__((aligned(16))) u16 sQ[kCc * TF::ld];
     __shared__ __attribute__((aligned(16))) float sX[NW][64 * 16];   // sin halves of dPhi(k)
@@ -472,8 +463,7 @@ void k_bwd_kv_cos_mfma(Args a) {
         const int c0 = row0 + ci * kCc;
         const int cn = ci > 0 ? c0 - kCc : c0;   // next chunk (none: reload this one)
         __syncthreads();   // the previous chunk's rows are stored
-        rK.template store_feat<PHI, true, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
-        rK.template store<TD>(sKr);
+        rK.template store_feat<PHI, true, TF, false, TD>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr, sKr);
         rV.template store<TD>(sV);
         rK.load(kh, cn, a.N);
         rV.load(vh, cn, a.N);
@@ -638,9 +628,9 @@ void k_bwd_kv_cos_mfma(Args a) {
                 float kr[4];
                 ld4f(sKr + TD::at(l32, d0), kr);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) dK[4 * q4 + e] = phi_d_raw<PHI>(kr[e]) * (dK[4 * q4 + e] + Ks[4 * q4 + e]);
+                for (int e = 0; e < 4; ++e) dK[4 * q4 + e] = phi_d_feat<PHI>(kr[e]) * (dK[4 * q4 + e] + Ks[4 * q4 + e]);
             }
-            // this lane overwrites exactly the raw-k entries it just read
+            // this lane overwrites exactly the phi(k) entries it just read
             stage_out<TD>(sKr, dK, 1.f, 32 * w);
             stage_out<TD>(sG, dV, 1.f, 32 * w);
         }
