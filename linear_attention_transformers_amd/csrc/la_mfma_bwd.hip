@@ -358,35 +358,37 @@ void k_bwd_q_mfma(Args a, int qm_arg) {
     }
 }
 
-// Segments per dq workgroup.  Where the dq kernel fits one workgroup per
-// compute unit (D = 128), a second round of short workgroups costs more than
-// fewer, longer ones (each starts by loading a state record and ends by
-// writing one): take the qm that minimises rounds x segments per workgroup,
-// the larger one on ties.  Where two fit, workgroups sharing a compute unit
-// slow each other and more of them keeps it busier: one segment each.
+// Segments per dq workgroup.  A round of short workgroups costs about as
+// much as a round of long ones (each starts by loading a state record and
+// ends by writing one), so take the qm that minimises rounds x segments per
+// workgroup, each build (one segment, several) at its own occupancy, the
+// larger qm on ties.
 template <int D, int PHI, bool CAUSAL>
 int q_segments_per_wg(const Args &a, unsigned n_units) {
-    // resident workgroups on the device (0: not yet asked; -1: more than one
-    // per compute unit).  Calls from several host threads may each ask; they
-    // store the same value.
-    static std::atomic<int> cached{0};
-    int slots = cached.load(std::memory_order_relaxed);
-    if (slots == 0) {
-        int dev = 0, cus = 0, per_cu = 0;
+    // resident workgroups on the device of the one-segment and the
+    // multi-segment build (0: not yet asked).  Calls from several host
+    // threads may each ask; they store the same values.
+    static std::atomic<int> cached1{0}, cachedm{0};
+    int slots1 = cached1.load(std::memory_order_relaxed), slotsm = cachedm.load(std::memory_order_relaxed);
+    if (slots1 == 0 || slotsm == 0) {
+        int dev = 0, cus = 0, per1 = 0, perm = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_bwd_q_mfma<D, PHI, CAUSAL, false>,
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per1, k_bwd_q_mfma<D, PHI, CAUSAL, false>,
                                                          4 * D, 0) != hipSuccess ||
-            cus <= 0 || per_cu <= 0)
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&perm, k_bwd_q_mfma<D, PHI, CAUSAL, true>,
+                                                         4 * D, 0) != hipSuccess ||
+            cus <= 0 || per1 <= 0 || perm <= 0)
             return 1;
-        slots = per_cu == 1 ? cus : -1;
-        cached.store(slots, std::memory_order_relaxed);
+        slots1 = cus * per1;
+        slotsm = cus * perm;
+        cached1.store(slots1, std::memory_order_relaxed);
+        cachedm.store(slotsm, std::memory_order_relaxed);
     }
-    if (slots < 0) return 1;
     int best = 1;
     long long best_t = -1;
     for (int m = 1; m <= a.nseg; ++m) {
-        const long long wgs = (long long)n_units * ((a.nseg + m - 1) / m);
+        const long long wgs = (long long)n_units * ((a.nseg + m - 1) / m), slots = m == 1 ? slots1 : slotsm;
         const long long t = (wgs + slots - 1) / slots * m;
         if (best_t < 0 || t <= best_t) best = m, best_t = t;
     }
@@ -660,16 +662,13 @@ hipError_t run(const Args &a, hipStream_t s) {
     if (e != hipSuccess) return e;
     {
         bool launched = false;
-        // several segments per workgroup only where one workgroup fits per
-        // compute unit (D = 128); the one-segment kernel is a separate build
-        const int qm = D == 128 ? q_segments_per_wg<D, PHI, CAUSAL>(a, n_units) : 1;
+        // segments per workgroup: the one-segment kernel is a separate build
+        const int qm = q_segments_per_wg<D, PHI, CAUSAL>(a, n_units);
         const unsigned nq = (unsigned)((a.nseg + qm - 1) / qm);
         TimedLaunch tl(CAUSAL ? "k_bwd_q_mfma" : "k_bwd_q_bidir_mfma", s);
-        if constexpr (D == 128) {
-            if (qm > 1) {
-                hipLaunchKernelGGL((k_bwd_q_mfma<D, PHI, CAUSAL, true>), dim3(n_units * nq), dim3(4 * D), 0, s, a, qm);
-                launched = true;
-            }
+        if (qm > 1) {
+            hipLaunchKernelGGL((k_bwd_q_mfma<D, PHI, CAUSAL, true>), dim3(n_units * nq), dim3(4 * D), 0, s, a, qm);
+            launched = true;
         }
         if (!launched)
             hipLaunchKernelGGL((k_bwd_q_mfma<D, PHI, CAUSAL, false>), dim3(n_units * nq), dim3(4 * D), 0, s, a, 1);
