@@ -395,6 +395,28 @@ int q_segments_per_wg(const Args &a, unsigned n_units) {
     return best;
 }
 
+// Segments per dk/dv workgroup.  Causal: one (the kernel holds two
+// workgroups per compute unit, and fewer, longer ones leave compute units
+// idle).  Bidirectional: every workgroup starts by staging the whole total
+// (R, r), so as many segments per workgroup as still leave at least one
+// workgroup per compute unit.
+inline int kv_segments_per_wg(const Args &a, unsigned n_units, bool causal) {
+    if (causal) return 1;
+    static std::atomic<int> cached{0};   // compute units (0: not yet asked)
+    int cus = cached.load(std::memory_order_relaxed);
+    if (cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return 1;
+        cached.store(cus, std::memory_order_relaxed);
+    }
+    // the fewest workgroups per unit that still give every compute unit one,
+    // then segments spread evenly over them
+    const long long groups = std::min<long long>(a.nseg, ((long long)cus + n_units - 1) / n_units);
+    return (int)((a.nseg + groups - 1) / groups);
+}
+
 // ---------------------------------------------------------------------------
 // k_bwd_kv_mfma: backward over the 32-row chunks of one (batch, KV head,
 // segment), from the exclusive suffix (R, r) of the segment.  Wave w holds
@@ -405,7 +427,7 @@ int q_segments_per_wg(const Args &a, unsigned n_units) {
 // ---------------------------------------------------------------------------
 template <int D, int PHI, bool CAUSAL>
 __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2)))
-void k_bwd_kv_mfma(Args a) {
+void k_bwd_kv_mfma(Args a, int qm) {
     constexpr int F = D, NW = D / 32, NT = 2 * D;
     using TF = PadI<F>;
     using TD = PadI<D>;
@@ -423,7 +445,12 @@ void k_bwd_kv_mfma(Args a) {
     bf16x8 (*sPop)[64] = reinterpret_cast<bf16x8 (*)[64]>(sGr);
     static_assert(sizeof(bf16x8) * 2 * 64 <= sizeof(u16) * kCb * TD::ld, "P operands fit the g rows");
 
-    const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
+    // this workgroup walks the qm consecutive segments seg0 .. seg1 (last to
+    // first; the R carry runs through their boundaries) from the suffix of
+    // the last one
+    const int nq = (a.nseg + qm - 1) / qm;
+    const int seg0 = (blockIdx.x % nq) * qm, bg = blockIdx.x / nq;
+    const int seg1 = min(seg0 + qm, a.nseg) - 1;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int t = threadIdx.x, l = t & 63, h = l >> 5, l32 = l & 31;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index, uniform
@@ -436,8 +463,8 @@ void k_bwd_kv_mfma(Args a) {
     const u16 *qbase = static_cast<const u16 *>(a.q);
     const u16 *gbase = static_cast<const u16 *>(a.g);
 
-    // the segment's exclusive suffix of (R, r) (causal) or the sequence total
-    const float *Rp = a.ws_Rs + ((size_t)bg * (a.nseg + 1) + (CAUSAL ? seg : a.nseg)) * SD;
+    // the exclusive suffix of (R, r) of segment seg1 (causal) or the sequence total
+    const float *Rp = a.ws_Rs + ((size_t)bg * (a.nseg + 1) + (CAUSAL ? seg1 : a.nseg)) * SD;
     f32x16 Rt[NW];
 #pragma unroll
     for (int db = 0; db < NW; ++db)
@@ -447,7 +474,7 @@ void k_bwd_kv_mfma(Args a) {
     // each chunk publishes the wave's block to sr for the state term
     float racc = Rp[(size_t)F * D + 32 * w + l32];
 
-    const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
+    const int row0 = seg0 * a.L, row1 = min((seg1 + 1) * a.L, a.N);
     const int nch = (row1 - row0 + kCb - 1) / kCb;
     RawTile<D, NT, kCb> rK, rV, rQ, rG;
     constexpr int NV = RawTile<D, NT, kCb>::NV, V8 = D / 8;
@@ -681,7 +708,9 @@ hipError_t run(const Args &a, hipStream_t s) {
     }
     {
         TimedLaunch tl(CAUSAL ? "k_bwd_kv_mfma" : "k_bwd_kv_bidir_mfma", s);
-        hipLaunchKernelGGL((k_bwd_kv_mfma<D, PHI, CAUSAL>), dim3(n_units * a.nseg), dim3(2 * D), 0, s, a);
+        const int kqm = kv_segments_per_wg(a, n_units, CAUSAL);
+        const unsigned nk = (unsigned)((a.nseg + kqm - 1) / kqm);
+        hipLaunchKernelGGL((k_bwd_kv_mfma<D, PHI, CAUSAL>), dim3(n_units * nk), dim3(2 * D), 0, s, a, kqm);
     }
     return hipGetLastError();
 }
