@@ -95,6 +95,35 @@ constexpr int kSegAlign = 64;   // every chunk length divides this
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Workgroups of kernel f (nt threads each) the current device holds at once,
+// or 0 if the runtime cannot say.
+template <class K>
+int device_slots(K f, int nt) {
+    int dev = 0, cus = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, f, nt, 0) != hipSuccess || cus <= 0 || per <= 0)
+        return 0;
+    return cus * per;
+}
+
+// Segments per workgroup for a kernel whose workgroups walk consecutive
+// segments: a round of workgroups (as many as the device holds at once)
+// costs about the same whether they are short or long, so the qm that
+// minimises rounds x segments per workgroup, the larger on ties.  slots1 and
+// slotsm: workgroups per round of the build run for qm = 1 and for qm > 1.
+inline int segments_by_rounds(int nseg, long long n_units, long long slots1, long long slotsm) {
+    if (slots1 <= 0 || slotsm <= 0) return 1;
+    int best = 1;
+    long long best_t = -1;
+    for (int m = 1; m <= nseg; ++m) {
+        const long long wgs = n_units * ((nseg + m - 1) / m), slots = m == 1 ? slots1 : slotsm;
+        const long long t = (wgs + slots - 1) / slots * m;
+        if (best_t < 0 || t <= best_t) best = m, best_t = t;
+    }
+    return best;
+}
+
 // Segment count: about `target` workgroups over the `units` independent
 // sequences (each workgroup runs one segment of one unit), but never segments
 // shorter than min_L rows (by default 4 * kSegAlign: shorter, the state

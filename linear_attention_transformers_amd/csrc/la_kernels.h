@@ -34,6 +34,10 @@ hipError_t mfma_state_run(const Args &a, int phi, int causal, hipStream_t s);
 bool mfma_bwd_serves(int bf16, int causal, int D, int has_cos);
 hipError_t mfma_bwd_run(const Args &a, int phi, int causal, hipStream_t s);
 hipError_t mfma_bwd_cos_run(const Args &a, int phi, int causal, hipStream_t s);
+// Segments per bidirectional dk/dv workgroup: such a workgroup first stages
+// the whole total (R, r), so the fewest workgroups per (batch, KV head) unit
+// that still give every compute unit one, the segments spread evenly.
+int bidir_segments_per_wg(int nseg, unsigned n_units);
 
 // float32 bidirectional kernels on the matrix cores (F = D in {64, 128}):
 // the float32 path's plan, workspace layout and scans.

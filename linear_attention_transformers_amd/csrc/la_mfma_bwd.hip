@@ -358,63 +358,22 @@ void k_bwd_q_mfma(Args a, int qm_arg) {
     }
 }
 
-// Segments per dq workgroup.  A round of short workgroups costs about as
-// much as a round of long ones (each starts by loading a state record and
-// ends by writing one), so take the qm that minimises rounds x segments per
-// workgroup, each build (one segment, several) at its own occupancy, the
-// larger qm on ties.
+// Segments per dq workgroup (segments_by_rounds), each build (one segment,
+// several) at its own occupancy.
 template <int D, int PHI, bool CAUSAL>
 int q_segments_per_wg(const Args &a, unsigned n_units) {
-    // resident workgroups on the device of the one-segment and the
-    // multi-segment build (0: not yet asked).  Calls from several host
-    // threads may each ask; they store the same values.
+    // workgroups per round of the two builds (0: not yet asked).  Calls from
+    // several host threads may each ask; they store the same values.
     static std::atomic<int> cached1{0}, cachedm{0};
     int slots1 = cached1.load(std::memory_order_relaxed), slotsm = cachedm.load(std::memory_order_relaxed);
     if (slots1 == 0 || slotsm == 0) {
-        int dev = 0, cus = 0, per1 = 0, perm = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per1, k_bwd_q_mfma<D, PHI, CAUSAL, false>,
-                                                         4 * D, 0) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&perm, k_bwd_q_mfma<D, PHI, CAUSAL, true>,
-                                                         4 * D, 0) != hipSuccess ||
-            cus <= 0 || per1 <= 0 || perm <= 0)
-            return 1;
-        slots1 = cus * per1;
-        slotsm = cus * perm;
+        slots1 = device_slots(k_bwd_q_mfma<D, PHI, CAUSAL, false>, 4 * D);
+        slotsm = device_slots(k_bwd_q_mfma<D, PHI, CAUSAL, true>, 4 * D);
+        if (slots1 <= 0 || slotsm <= 0) return 1;
         cached1.store(slots1, std::memory_order_relaxed);
         cachedm.store(slotsm, std::memory_order_relaxed);
     }
-    int best = 1;
-    long long best_t = -1;
-    for (int m = 1; m <= a.nseg; ++m) {
-        const long long wgs = (long long)n_units * ((a.nseg + m - 1) / m), slots = m == 1 ? slots1 : slotsm;
-        const long long t = (wgs + slots - 1) / slots * m;
-        if (best_t < 0 || t <= best_t) best = m, best_t = t;
-    }
-    return best;
-}
-
-// Segments per dk/dv workgroup.  Causal: one (the kernel holds two
-// workgroups per compute unit, and fewer, longer ones leave compute units
-// idle).  Bidirectional: every workgroup starts by staging the whole total
-// (R, r), so as many segments per workgroup as still leave at least one
-// workgroup per compute unit.
-inline int kv_segments_per_wg(const Args &a, unsigned n_units, bool causal) {
-    if (causal) return 1;
-    static std::atomic<int> cached{0};   // compute units (0: not yet asked)
-    int cus = cached.load(std::memory_order_relaxed);
-    if (cus == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            return 1;
-        cached.store(cus, std::memory_order_relaxed);
-    }
-    // the fewest workgroups per unit that still give every compute unit one,
-    // then segments spread evenly over them
-    const long long groups = std::min<long long>(a.nseg, ((long long)cus + n_units - 1) / n_units);
-    return (int)((a.nseg + groups - 1) / groups);
+    return segments_by_rounds(a.nseg, n_units, slots1, slotsm);
 }
 
 // ---------------------------------------------------------------------------
@@ -708,7 +667,9 @@ hipError_t run(const Args &a, hipStream_t s) {
     }
     {
         TimedLaunch tl(CAUSAL ? "k_bwd_kv_mfma" : "k_bwd_kv_bidir_mfma", s);
-        const int kqm = kv_segments_per_wg(a, n_units, CAUSAL);
+        // causal: one segment per workgroup (two workgroups per compute unit;
+        // fewer, longer ones leave compute units idle)
+        const int kqm = CAUSAL ? 1 : bidir_segments_per_wg(a.nseg, n_units);
         const unsigned nk = (unsigned)((a.nseg + kqm - 1) / kqm);
         hipLaunchKernelGGL((k_bwd_kv_mfma<D, PHI, CAUSAL>), dim3(n_units * nk), dim3(2 * D), 0, s, a, kqm);
     }
@@ -725,6 +686,22 @@ hipError_t by_phi(const Args &a, int phi, hipStream_t s) {
 }
 
 }  // namespace
+
+int bidir_segments_per_wg(int nseg, unsigned n_units) {
+    static std::atomic<int> cached{0};   // compute units (0: not yet asked)
+    int cus = cached.load(std::memory_order_relaxed);
+    if (cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return 1;
+        cached.store(cus, std::memory_order_relaxed);
+    }
+    // the fewest workgroups per unit that still give every compute unit one,
+    // then segments spread evenly over them
+    const long long groups = std::min<long long>(nseg, ((long long)cus + n_units - 1) / n_units);
+    return (int)((nseg + groups - 1) / groups);
+}
 
 bool mfma_bwd_serves(int bf16, int causal, int D, int has_cos) {
     (void)causal;

@@ -114,6 +114,27 @@ def test_many_segments_every_family(dtype, D, causal):
         dtype, D, "causal" if causal else "bidir"))
 
 
+GROUPED = [("bf16", 64, False), ("bf16", 128, False), ("bf16", 64, True), ("f32", 64, False)]
+
+
+@pytest.mark.parametrize("dtype,D,cos", GROUPED,
+                         ids=["%s-D%d%s" % (d, D, "-cos" if c else "") for d, D, c in GROUPED])
+def test_bidir_dkdv_grouped_segments(dtype, D, cos):
+    """Bidirectional dk/dv workgroups that walk several segments: 16 (batch,
+    KV head) units of 17 segments of 64 rows (N = 1070, ragged) give the bf16
+    F = D kernel 16 workgroups per unit, two segments each and the last one a
+    single segment; GQA n_rep = 2.  The cos/sin and float32 dk/dv kernels run
+    one segment per workgroup on the same shape."""
+    torch, la = gpu_or_skip()
+    B, H, Hkv, N = 2, 16, 8, 1070
+    t = make(B, H, Hkv, N, D, dtype, scale=0.5, cos=cos, seed=D + N + cos)
+    say("grouped dk/dv %s D=%d cos=%s" % (dtype, D, cos))
+    ref = oracle_on(t, False, "elu+1", 1e-6)
+    out, grads = run_gpu(la, t, False, "elu+1", 1e-6, seg_len=64)
+    compare(t, out, grads, ref[0], ref[1], dtype, H, Hkv, label="grouped-%s-D%d%s" % (
+        dtype, D, "-cos" if cos else ""))
+
+
 SPAN = [(128, True, 4, 4), (128, False, 8, 4), (128, True, 8, 2)]
 
 
