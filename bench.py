@@ -255,20 +255,9 @@ def bench_gqa(args, name):
         if st:
             raise RuntimeError(lib.la_last_error().decode())
 
-    if args.warmup is None:
-        n, t_w = 0, time.perf_counter()
-        while n < 3 or time.perf_counter() - t_w < 0.5:
-            step()
-            n += 1
-            if n % 8 == 0:
-                torch.cuda.synchronize()
-        args.warmup = n
-    else:
-        for _ in range(args.warmup):
-            step()
-    torch.cuda.synchronize()
-    log("bench: %d warmup steps done; %d timed steps" % (args.warmup, args.steps))
     flush = None if args.no_flush else Flusher(torch.device("cuda:0"))
+    args.warmup = warm_up(step, args.warmup, flush)
+    log("bench: %d warmup steps done; %d timed steps" % (args.warmup, args.steps))
     step_ms, wall = timed_steps(step, args.steps, flush)
     st = stats(step_ms)
     la.timing_enable(True)
@@ -370,20 +359,9 @@ def bench_lowrank(args, name):
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if args.warmup is None:
-        n, t_w = 0, time.perf_counter()
-        while n < 3 or time.perf_counter() - t_w < 0.5:
-            step()
-            n += 1
-            if n % 4 == 0:
-                torch.cuda.synchronize()
-        args.warmup = n
-    else:
-        for _ in range(args.warmup):
-            step()
-    torch.cuda.synchronize()
-    log("bench: %d warmup steps done; %d timed steps" % (args.warmup, args.steps))
     flush = None if args.no_flush else Flusher(torch.device("cuda:0"))
+    args.warmup = warm_up(step, args.warmup, flush, sync_every=4)
+    log("bench: %d warmup steps done; %d timed steps" % (args.warmup, args.steps))
     step_ms, wall = timed_steps(step, args.steps, flush)
     st = stats(step_ms)
     la.timing_enable(True)
@@ -445,6 +423,25 @@ class Flusher:
     def __call__(self):
         import torch
         torch.amax(self.buf, dim=0, out=self.out)
+
+
+def warm_up(step, warmup, flush, sync_every=8):
+    """W untimed steps in the timed steps' own pattern: each after a cache
+    flush when the timed steps flush, so the timed steps start at the device's
+    steady state for that pattern (after unflushed warm-up steps, the first
+    dozen or so flushed steps of the headline ran up to 30% slower).
+    warmup None: as many as fill 0.5 s (at least 3).  Returns W."""
+    import torch
+    n, t_w = 0, time.perf_counter()
+    while (n < 3 or time.perf_counter() - t_w < 0.5) if warmup is None else n < warmup:
+        if flush is not None:
+            flush()
+        step()
+        n += 1
+        if n % sync_every == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
 
 
 def timed_steps(step, K, flush):
@@ -609,18 +606,7 @@ def main():
         del src, dst
         log("bench: calibration copy of %d MiB done" % args.calibration_copy_mib)
 
-    if args.warmup is None:
-        n, t_w = 0, time.perf_counter()
-        while n < 3 or time.perf_counter() - t_w < 0.5:
-            step()
-            n += 1
-            if n % 8 == 0:
-                torch.cuda.synchronize()
-        args.warmup = n
-    else:
-        for _ in range(args.warmup):
-            step()
-    torch.cuda.synchronize()
+    args.warmup = warm_up(step, args.warmup, flush)
     log("bench: %d warmup steps done" % args.warmup)
 
     # A: the headline: per-step events only
