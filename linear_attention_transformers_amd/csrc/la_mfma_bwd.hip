@@ -24,8 +24,9 @@
 // LDS tiles use the permuted padded layout (PadI): transposed 4-row reads
 // are conflict-free in it.
 //
-// Layout of the work: one workgroup per (batch, KV head, segment) serving the
-// n_rep query heads.  Per chunk and head one wave forms each 32x32 C x C
+// Layout of the work: one workgroup per (batch, KV head) and run of
+// consecutive segments (one, or several where fewer, longer workgroups pay)
+// serving the n_rep query heads.  Per chunk and head one wave forms each 32x32 C x C
 // tile (A, T in the q-kernel; A, P in the kv-kernel) for the workgroup, and
 // each wave owns a 32-wide block of the feature columns of the state (S^T in
 // the q-kernel, R^T in the kv-kernel), of dPhi(q) / dPhi(k), and of the value
@@ -377,12 +378,12 @@ int q_segments_per_wg(const Args &a, unsigned n_units) {
 }
 
 // ---------------------------------------------------------------------------
-// k_bwd_kv_mfma: backward over the 32-row chunks of one (batch, KV head,
-// segment), from the exclusive suffix (R, r) of the segment.  Wave w holds
-// R^T (every value block x feature block w) and produces dk for feature
-// block w and dv for value block w.  Per head, wave 0 forms the masked A
-// tile and wave 1 the P tile as bf16 operands for every wave (through LDS),
-// while the waves form the chunk's state terms.
+// k_bwd_kv_mfma: backward over the 32-row chunks of one (batch, KV head) and
+// qm consecutive segments, from the exclusive suffix (R, r) of the last one.
+// Wave w holds R^T (every value block x feature block w) and produces dk for
+// feature block w and dv for value block w.  Per head, wave 0 forms the
+// masked A tile and wave 1 the P tile as bf16 operands for every wave
+// (through LDS), while the waves form the chunk's state terms.
 // ---------------------------------------------------------------------------
 template <int D, int PHI, bool CAUSAL>
 __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2)))
