@@ -259,6 +259,9 @@ struct RawTile {
     static constexpr int NV = C * V8 / NT;
     static_assert(NV * NT == C * V8, "tile must split evenly over the threads");
     uint4 v[NV];
+    // cos/sin weights of the rows of the vectors (cos/sin staging only), read
+    // with the rows so that the staging does not wait for them
+    float wc[NV], ws[NV];
 
     // FAST (for kernels with registers to spare), a whole tile in range: one
     // 16-byte load per vector at a uniform base plus this thread's constant
@@ -290,6 +293,24 @@ struct RawTile {
         }
     }
 
+    // the rows as load(), and with W their cos/sin weights (clamped to an
+    // in-range row like the rows themselves)
+    template <bool W>
+    __device__ __forceinline__ void load(const u16 *src, int c0, int N, const float *cw, const float *sw) {
+        load(src, c0, N);
+        if constexpr (W) load_w(cw, sw, c0, N);
+    }
+    // the weights alone (a tile reloaded with other heads' rows at the same
+    // positions keeps them)
+    __device__ __forceinline__ void load_w(const float *cw, const float *sw, int c0, int N) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int t = min(c0 + (int)(threadIdx.x + k * NT) / V8, N - 1);
+            wc[k] = cw[t];
+            ws[k] = sw[t];
+        }
+    }
+
     template <class L>
     __device__ __forceinline__ void store(u16 *dst) const {
 #pragma unroll
@@ -299,22 +320,20 @@ struct RawTile {
         }
     }
 
-    // Features: phi, then with COS [cos_t phi, sin_t phi] (row width 2D),
-    // rounded to bf16.  With QZ, also sQZ[r] = Phi(x_r) . z (features before
+    // Features: phi, then with COS [cos_t phi, sin_t phi] (row width 2D, the
+    // weights those load<true> read), rounded to bf16.  With QZ, also sQZ[r] = Phi(x_r) . z (features before
     // rounding, fp32; fixed-order register reduction across the V8 threads of
     // a row).  With a layout LP, also phi itself (unweighted, bf16, row width
     // D) into dphi, for phi' in a backward.  Branch-free per element: rows
     // >= N hold zeros (load) and phi of them is finite; only a ragged tile
     // (uniform test) multiplies them by a 0/1 row factor.
     template <int PHI, bool COS, class L, bool QZ, class LP = void>
-    __device__ __forceinline__ void store_feat(u16 *dst, int c0, int N, const float *cw,
-                                               const float *sw, const float *sz,
-                                               float *sQZ, u16 *dphi = nullptr) const {
+    __device__ __forceinline__ void store_feat(u16 *dst, int c0, int N, const float *sz, float *sQZ,
+                                               u16 *dphi = nullptr) const {
         const bool ragged = c0 + C > N;
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int idx = threadIdx.x + k * NT, r = idx / V8, c8 = (idx % V8) * 8, t = c0 + r;
-            const int tc = min(t, N - 1);   // an in-range index for the weights
             const uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
             float f[8];
 #pragma unroll
@@ -327,7 +346,7 @@ struct RawTile {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) f[e] *= vf;
             }
-            const float m0 = COS ? cw[tc] : 1.f;
+            const float m0 = COS ? wc[k] : 1.f;
             uint32_t o[4];
             if constexpr (!std::is_void_v<LP>) {
 #pragma unroll
@@ -345,7 +364,7 @@ struct RawTile {
                 qz = m0 * d;
             }
             if constexpr (COS) {
-                const float m1 = sw[tc];
+                const float m1 = ws[k];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[e] = pk2(m1 * f[2 * e], m1 * f[2 * e + 1]);
                 *reinterpret_cast<uint4 *>(dst + L::at(r, D + c8)) = make_uint4(o[0], o[1], o[2], o[3]);

@@ -131,7 +131,7 @@ void k_bwd_q_mfma(Args a, int qm_arg) {
         for (int c0 = seg * a.L; c0 < s1; c0 += kCb) {
             __syncthreads();
             if constexpr (CAUSAL) {
-                rK.template store_feat<PHI, false, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+                rK.template store_feat<PHI, false, TF, false>(sK, c0, a.N, nullptr, nullptr);
                 rV.template store<TD>(sV);
                 // the next chunk's K, V (unconditional: rows past the workgroup's
                 // segments are loaded clamped and never used, and no register
@@ -142,13 +142,13 @@ void k_bwd_q_mfma(Args a, int qm_arg) {
             // the first head's rows are staged here, in straight-line code (in the
             // head loop, the wait for them would also wait for the K, V loads
             // just issued: the loop header merges the later heads' path)
-            rQ.template store_feat<PHI, false, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+            rQ.template store_feat<PHI, false, TF, true>(sQ, c0, a.N, sz, sQZ);
             rG.template store<TD>(sG);
             for (int rep = 0; rep < a.nrep; ++rep) {
                 const size_t bh = bh0 + rep;
                 if (rep > 0) {
                     __syncthreads();
-                    rQ.template store_feat<PHI, false, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+                    rQ.template store_feat<PHI, false, TF, true>(sQ, c0, a.N, sz, sQZ);
                     rG.template store<TD>(sG);
                 }
                 __syncthreads();
@@ -461,7 +461,7 @@ void k_bwd_kv_mfma(Args a, int qm) {
     // (rows past N: zeros), then the next head's (or the next chunk's first
     // head's) loads
     auto stage_head = [&](int c0, int rep, int cn) {
-        rQ.template store_feat<PHI, false, TF, false>(sQ, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rQ.template store_feat<PHI, false, TF, false>(sQ, c0, a.N, nullptr, nullptr);
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int idx = t + k * NT, i = idx / V8, c8 = (idx % V8) * 8, row = c0 + i;
@@ -526,7 +526,7 @@ void k_bwd_kv_mfma(Args a, int qm) {
         const int c0 = row0 + ci * kCb;
         const int cn = ci > 0 ? c0 - kCb : c0;   // next chunk (none: reload this one)
         __syncthreads();   // every read of the previous chunk's tiles is done
-        rK.template store_feat<PHI, false, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rK.template store_feat<PHI, false, TF, false>(sK, c0, a.N, nullptr, nullptr);
         rV.template store<TD>(sV);
         rK.load(kh, cn, a.N);
         rV.load(vh, cn, a.N);

@@ -31,7 +31,6 @@ using namespace mf;
 
 constexpr int kCc = 32;   // chunk length: one 32x32 tile of A per head
 
-
 // ---------------------------------------------------------------------------
 // k_bwd_q_cos_mfma: forward over the 32-row chunks of one (batch, KV head,
 // segment) for the n_rep query heads.  Wave w (of F/32) holds S^T for
@@ -115,7 +114,8 @@ void k_bwd_q_cos_mfma(Args a) {
     for (int c0 = row0; c0 < row1; c0 += kCc) {
         __syncthreads();
         if constexpr (CAUSAL) {
-            rK.template store_feat<PHI, true, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+            rK.load_w(a.cw, a.sw, c0, a.N);   // read here: read with the rows, a chunk ahead, this kernel ran 2% slower
+            rK.template store_feat<PHI, true, TF, false>(sK, c0, a.N, nullptr, nullptr);
             rV.template store<TD>(sV);
             rK.load(kh, c0 + kCc, a.N);   // next chunk (past the segment: unused)
             rV.load(vh, c0 + kCc, a.N);
@@ -125,13 +125,14 @@ void k_bwd_q_cos_mfma(Args a) {
         // the first head's rows are staged here, in straight-line code (in the
         // head loop, the wait for them would also wait for the K, V loads
         // just issued: the loop header merges the later heads' path)
-        rQ.template store_feat<PHI, true, TF, true, TD>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ, sQr);
+        rQ.load_w(a.cw, a.sw, c0, a.N);   // the chunk's positions, for every head
+        rQ.template store_feat<PHI, true, TF, true, TD>(sQ, c0, a.N, sz, sQZ, sQr);
         rG.template store<TD>(sG);
         for (int rep = 0; rep < a.nrep; ++rep) {
             const size_t bh = bh0 + rep;
             if (rep > 0) {
                 __syncthreads();
-                rQ.template store_feat<PHI, true, TF, true, TD>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ, sQr);
+                rQ.template store_feat<PHI, true, TF, true, TD>(sQ, c0, a.N, sz, sQZ, sQr);
                 rG.template store<TD>(sG);
             }
             __syncthreads();
@@ -316,7 +317,8 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void
     for (int c0 = row0; c0 < row1; c0 += kCc) {
         for (int rep = 0; rep < a.nrep; ++rep) {
             __syncthreads();   // the previous head's LDS reads are done
-            rQ.template store_feat<PHI, true, TF, false>(sQ, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+            rQ.load_w(a.cw, a.sw, c0, a.N);   // read here: read with the rows, a chunk ahead, this kernel ran 2% slower
+            rQ.template store_feat<PHI, true, TF, false>(sQ, c0, a.N, nullptr, nullptr);
 #pragma unroll
             for (int k = 0; k < NV; ++k) {   // gn = g / den (rows past N: zeros)
                 const int idx = t + k * NT, i = idx / V8, c8 = (idx % V8) * 8;
@@ -451,10 +453,10 @@ void k_bwd_kv_cos_mfma(Args a) {
     };
     {
         const int c0 = row0 + (nch - 1) * kCc;
-        rK.load(kh, c0, a.N);
+        rK.template load<true>(kh, c0, a.N, a.cw, a.sw);
         rV.load(vh, c0, a.N);
         if constexpr (CAUSAL) {   // the in-chunk terms need the queries' rows
-            rQ.load(qbase + bh0 * a.N * D, c0, a.N);
+            rQ.template load<true>(qbase + bh0 * a.N * D, c0, a.N, a.cw, a.sw);
             rG.load(gbase + bh0 * a.N * D, c0, a.N);
             load_dc(bh0, c0);
         }
@@ -463,9 +465,9 @@ void k_bwd_kv_cos_mfma(Args a) {
         const int c0 = row0 + ci * kCc;
         const int cn = ci > 0 ? c0 - kCc : c0;   // next chunk (none: reload this one)
         __syncthreads();   // the previous chunk's rows are stored
-        rK.template store_feat<PHI, true, TF, false, TD>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr, sKr);
+        rK.template store_feat<PHI, true, TF, false, TD>(sK, c0, a.N, nullptr, nullptr, sKr);
         rV.template store<TD>(sV);
-        rK.load(kh, cn, a.N);
+        rK.template load<true>(kh, cn, a.N, a.cw, a.sw);
         rV.load(vh, cn, a.N);
         // R (bf16, [feature][value]) for the state terms (bidirectional: the
         // total, staged once)
@@ -483,7 +485,7 @@ void k_bwd_kv_cos_mfma(Args a) {
         // one head's query rows into LDS: Phi(Q), gn = g / den (rows past N:
         // zeros), raw g, c, 1 / den
         auto stage_head = [&]() {
-            rQ.template store_feat<PHI, true, TF, false>(sQ, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+            rQ.template store_feat<PHI, true, TF, false>(sQ, c0, a.N, nullptr, nullptr);
 #pragma unroll
             for (int k = 0; k < NV; ++k) {
                 const int idx = t + k * NT, i = idx / V8, c8 = (idx % V8) * 8;
@@ -546,6 +548,7 @@ void k_bwd_kv_cos_mfma(Args a) {
                 const size_t hn = bh0 + (last ? 0 : rep + 1);
                 const int cq = last ? cn : c0;
                 rQ.load(qbase + hn * a.N * D, cq, a.N);
+                if (last) rQ.load_w(a.cw, a.sw, cq, a.N);   // new positions
                 rG.load(gbase + hn * a.N * D, cq, a.N);
                 load_dc(hn, cq);
             }

@@ -128,15 +128,15 @@ __global__ __launch_bounds__((D * 2 * state_sets<D, F>())) __attribute__((amdgpu
     // still sit in the device's last-level cache when it does.
     RawTile<D, NT, CS, D == 128> rK, rV;
     const int clast = row0 + (row1 - row0 - 1) / CS * CS;
-    rK.load(kh, clast, row1);
+    rK.template load<COS>(kh, clast, row1, a.cw, a.sw);
     rV.load(vh, clast, row1);
     for (int c0 = clast; c0 >= row0; c0 -= CS) {
         __syncthreads();
-        rK.template store_feat<PHI, COS, TF, false>(sK, c0, row1, a.cw, a.sw, nullptr, nullptr);
+        rK.template store_feat<PHI, COS, TF, false>(sK, c0, row1, nullptr, nullptr);
         rV.template store<TD>(sV);
         __syncthreads();
         const int cn = c0 - CS >= row0 ? c0 - CS : row0;   // the next chunk (after the first: unused)
-        rK.load(kh, cn, row1);
+        rK.template load<COS>(kh, cn, row1, a.cw, a.sw);
         rV.load(vh, cn, row1);
         state_update<D, F, FBW, CS>(S, Z, sK, sV, vb, fh);
     }
@@ -227,37 +227,38 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(fwd_waves
     // the K, V rows the state pass has just read
     RawTile<D, NT, kCf, kRich> rK, rV;
     RawTile<D, NT, kCf, kRich, kRich> rQ;
-    rK.load(kh, row0, a.N);
+    rK.template load<COS>(kh, row0, a.N, a.cw, a.sw);
     rV.load(vh, row0, a.N);
-    rQ.load(qbase + bh0 * a.N * D, row0, a.N);
+    rQ.template load<COS>(qbase + bh0 * a.N * D, row0, a.N, a.cw, a.sw);
     // rows staged in sO wait for the next barrier to be stored (pend_* = where)
     u16 *pend_oh = nullptr;
     int pend_c0 = 0;
     for (int c0 = row0; c0 < row1; c0 += kCf) {
         __syncthreads();   // previous chunk: every LDS read done, sz updated, sO complete
         if (pend_oh) store_rows<D, NT, TD, kRich, kRich>(pend_oh, sO, pend_c0, a.N);
-        rK.template store_feat<PHI, COS, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rK.template store_feat<PHI, COS, TF, false>(sK, c0, a.N, nullptr, nullptr);
         rV.template store<TD>(sV);
         // the next chunk's K, V (unconditional: rows past the segment are
         // loaded clamped and never used, and no register copies are needed)
-        rK.load(kh, c0 + kCf, a.N);
+        rK.template load<COS>(kh, c0 + kCf, a.N, a.cw, a.sw);
         rV.load(vh, c0 + kCf, a.N);
         // the first head's rows are staged here, in straight-line code: staged
         // at the top of the head loop, they would share its header with the
         // later heads, whose wait for their own rows would also wait for the
         // K, V loads just issued
-        rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+        rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, sz, sQZ);
         for (int rep = 0; rep < a.nrep; ++rep) {
             u16 *oh = obase + (bh0 + rep) * a.N * D;
             if (rep > 0) {
                 __syncthreads();   // every wave is done with the previous head's sQ; sO complete
-                rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+                rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, sz, sQZ);
                 store_rows<D, NT, TD, kRich, kRich>(pend_oh, sO, pend_c0, a.N);   // after the staging's wait
             }
             __syncthreads();
             {   // Q rows of the next head, or of the first head at the next chunk
                 const bool last = rep + 1 == a.nrep;
                 rQ.load(qbase + (bh0 + (last ? 0 : rep + 1)) * a.N * D, last ? c0 + kCf : c0, a.N);
+                if (COS && last) rQ.load_w(a.cw, a.sw, c0 + kCf, a.N);   // new positions
             }
 
             // A^T (keys x queries) of the chunk, causal mask, bf16 rounding (the
@@ -396,31 +397,32 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void
 
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
     RawTile<D, NT, kCf> rK, rV, rQ;
-    rK.load(kh, row0, a.N);
+    rK.template load<COS>(kh, row0, a.N, a.cw, a.sw);
     rV.load(vh, row0, a.N);
-    rQ.load(qbase + bh0 * a.N * D, row0, a.N);
+    rQ.template load<COS>(qbase + bh0 * a.N * D, row0, a.N, a.cw, a.sw);
     // rows staged in sO wait for the next barrier to be stored (pend_* = where)
     u16 *pend_oh = nullptr;
     int pend_c0 = 0;
     for (int c0 = row0; c0 < row1; c0 += kCf) {
         __syncthreads();   // previous chunk: every LDS read done, sz updated, sO complete
         if (pend_oh) store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
-        rK.template store_feat<PHI, COS, TF, false>(sK, c0, a.N, a.cw, a.sw, nullptr, nullptr);
+        rK.template store_feat<PHI, COS, TF, false>(sK, c0, a.N, nullptr, nullptr);
         rV.template store<TD>(sV);
-        rK.load(kh, c0 + kCf, a.N);   // next chunk (past the segment: clamped, unused)
+        rK.template load<COS>(kh, c0 + kCf, a.N, a.cw, a.sw);   // next chunk (past the segment: clamped, unused)
         rV.load(vh, c0 + kCf, a.N);
-        rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+        rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, sz, sQZ);
         for (int rep = 0; rep < a.nrep; ++rep) {
             u16 *oh = obase + (bh0 + rep) * a.N * D;
             if (rep > 0) {
                 __syncthreads();   // every wave is done with the previous head's sQ; sO complete
-                rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+                rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, sz, sQZ);
                 store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
             }
             __syncthreads();
             {   // Q rows of the next head, or of the first head at the next chunk
                 const bool last = rep + 1 == a.nrep;
                 rQ.load(qbase + (bh0 + (last ? 0 : rep + 1)) * a.N * D, last ? c0 + kCf : c0, a.N);
+                if (COS && last) rQ.load_w(a.cw, a.sw, c0 + kCf, a.N);   // new positions
             }
             // num^T of value block vb: the first half adds V^T A^T, each half
             // its feature blocks' S^T Phi(Q)^T.  The first half forms A^T
@@ -530,7 +532,7 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2))) void
 
     const int row0 = seg * a.L, row1 = min(row0 + a.L, a.N);
     RawTile<D, NT, kCf> rQ;
-    rQ.load(qbase + bh0 * a.N * D, row0, a.N);
+    rQ.template load<COS>(qbase + bh0 * a.N * D, row0, a.N, a.cw, a.sw);
     u16 *pend_oh = nullptr;   // rows staged in sO, stored after the next barrier
     int pend_c0 = 0;
     for (int c0 = row0; c0 < row1; c0 += kCf) {
@@ -538,12 +540,13 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(2))) void
             __syncthreads();   // previous head: sQ reads done, sO complete (and sz written)
             // staging first: its wait for the Q rows would otherwise also wait
             // for the output stores issued just before
-            rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, a.cw, a.sw, sz, sQZ);
+            rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, sz, sQZ);
             if (pend_oh) store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
             __syncthreads();
             {   // Q rows of the next head, or of the first head at the next chunk
                 const bool last = rep + 1 == a.nrep;
                 rQ.load(qbase + (bh0 + (last ? 0 : rep + 1)) * a.N * D, last ? c0 + kCf : c0, a.N);
+                if (COS && last) rQ.load_w(a.cw, a.sw, c0 + kCf, a.N);   // new positions
             }
             f32x16 Nt = zero16();
 #pragma unroll
