@@ -26,11 +26,11 @@
 //
 // Layout of the work: one workgroup per (batch, KV head) and run of
 // consecutive segments (one, or several where fewer, longer workgroups pay)
-// serving the n_rep query heads.  Per chunk and head one wave forms each 32x32 C x C
-// tile (A, T in the q-kernel; A, P in the kv-kernel) for the workgroup, and
-// each wave owns a 32-wide block of the feature columns of the state (S^T in
-// the q-kernel, R^T in the kv-kernel), of dPhi(q) / dPhi(k), and of the value
-// columns of dv.  The only cross-wave reduction, Phi(q_i).U_i over the
+// serving the n_rep query heads.  Per chunk and head one wave forms each
+// 32x32 C x C tile (A, T in the q-kernel; A, P in the kv-kernel) for the
+// workgroup, and each wave owns a 32-wide block of the feature columns of
+// the state (S^T in the q-kernel, R^T in the kv-kernel), of dPhi(q) /
+// dPhi(k), and of the value columns of dv.  The only cross-wave reduction, Phi(q_i).U_i over the
 // feature blocks, goes through LDS in a fixed order.  In the q-kernel a
 // second set of waves accumulates the segment's (R, r) so the two
 // register-heavy states live in different waves.
