@@ -3,7 +3,8 @@
 // Method (SVD_linear_Attention, "Module neuralops.core.triton_kernels.
 // linear_attn", module docstring: chunked causal streaming, O(N) memory,
 // tiled in on-chip memory; cos/sin modulation; fwd arguments): rows are cut
-// into chunks of C = 64; for chunk c with exclusive carried state (S, z)
+// into chunks of C = 32 (the state pass sums 64- or 128-row chunks); for
+// chunk c with exclusive carried state (S, z)
 //   A = (Phi(Q_c) Phi(K_c)^T) masked to j <= i,
 //   num = A V_c + Phi(Q_c) S,   den = A 1 + Phi(Q_c) z + eps,   out = num / den,
 //   S += Phi(K_c)^T V_c,   z += Phi(K_c)^T 1.
