@@ -93,25 +93,28 @@ def test_bidir_cos_gqa_many_segments(D):
                 label="bidir-cos-gqa-D%d-seg%d" % (D, seg_len))
 
 
-MANYSEG = [("f32", 32, True), ("f32", 32, False), ("f32", 64, False), ("f32", 128, False),
-           ("bf16", 64, False), ("bf16", 64, True)]
+MANYSEG = [("f32", 32, True, False), ("f32", 32, False, False), ("f32", 64, False, False),
+           ("f32", 128, False, False), ("bf16", 64, False, False), ("bf16", 64, True, False),
+           ("bf16", 64, True, True), ("bf16", 128, True, True)]
 
 
-@pytest.mark.parametrize("dtype,D,causal", MANYSEG,
-                         ids=["%s-D%d-%s" % (d, D, "causal" if c else "bidir") for d, D, c in MANYSEG])
-def test_many_segments_every_family(dtype, D, causal):
+@pytest.mark.parametrize("dtype,D,causal,cos", MANYSEG,
+                         ids=["%s-D%d-%s%s" % (d, D, "causal" if c else "bidir", "-cos" if w else "")
+                              for d, D, c, w in MANYSEG])
+def test_many_segments_every_family(dtype, D, causal, cos):
     """18 segments of 64 rows (N = 1100): the segment scans then load their
     records in more than one batch, in both modes and on every kernel family
-    (float32 vector-ALU at D = 32, float32 matrix cores, bf16 matrix cores);
-    GQA with n_rep = 2."""
+    (float32 vector-ALU at D = 32, float32 matrix cores, bf16 matrix cores,
+    and the causal cos/sin kernels with their R-record pass); GQA with
+    n_rep = 2."""
     torch, la = gpu_or_skip()
     B, H, Hkv, N = 1, 4, 2, 1100
-    t = make(B, H, Hkv, N, D, dtype, scale=0.5, cos=False, seed=D + N)
-    say("many segments %s D=%d causal=%s" % (dtype, D, causal))
+    t = make(B, H, Hkv, N, D, dtype, scale=0.5, cos=cos, seed=D + N + cos)
+    say("many segments %s D=%d causal=%s cos=%s" % (dtype, D, causal, cos))
     ref = oracle_on(t, causal, "relu", 1e-6)
     out, grads = run_gpu(la, t, causal, "relu", 1e-6, seg_len=64)
-    compare(t, out, grads, ref[0], ref[1], dtype, H, Hkv, label="manyseg-%s-D%d-%s" % (
-        dtype, D, "causal" if causal else "bidir"))
+    compare(t, out, grads, ref[0], ref[1], dtype, H, Hkv, label="manyseg-%s-D%d-%s%s" % (
+        dtype, D, "causal" if causal else "bidir", "-cos" if cos else ""))
 
 
 GROUPED = [("bf16", 64, False), ("bf16", 128, False), ("bf16", 64, True), ("f32", 64, False)]
