@@ -112,6 +112,33 @@ __device__ __forceinline__ bf16x8 tr8(const u16 *p_lo, const u16 *p_hi) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// acc + sum over s < S of mfma(lda(s), ldb(s)), in the order s = 0 .. S-1,
+// with the LDS reads of step s + AHEAD issued right after the product of step
+// s.  Left to itself the scheduler sinks each read next to its product (it
+// saves registers), and the chain then waits for a whole LDS round trip every
+// product or two; the scheduling fences keep the reads ahead.
+template <int S, int AHEAD, class FA, class FB>
+__device__ __forceinline__ f32x16 mfma_chain(FA lda, FB ldb, f32x16 acc) {
+    constexpr int P = AHEAD < S ? AHEAD : S;
+    bf16x8 ra[P], rb[P];
+#pragma unroll
+    for (int s = 0; s < P; ++s) {
+        ra[s] = lda(s);
+        rb[s] = ldb(s);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        acc = mfma(ra[s % P], rb[s % P], acc);
+        if (s + P < S) {
+            ra[s % P] = lda(s + P);
+            rb[s % P] = ldb(s + P);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return acc;
+}
+
 __device__ __forceinline__ bf16x8 ones8() {
     bf16x8 o;
 #pragma unroll

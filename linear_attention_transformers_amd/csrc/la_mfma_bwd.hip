@@ -162,17 +162,23 @@ void k_bwd_q_mfma(Args a, int qm_arg) {
                 const bool ok = c0 + l32 < a.N;   // this lane's query row exists
                 f32x16 U;
                 if (state_wave) {
-                    // U^T = S g (this feature block x the chunk's queries)
+                    // U^T = S g (this feature block x the chunk's queries); the g
+                    // operands all read before the products
                     U = zero16();
+                    bf16x8 gq[NW][2];
+#pragma unroll
+                    for (int db = 0; db < NW; ++db)
+#pragma unroll
+                        for (int s = 0; s < 2; ++s) gq[db][s] = ld4x2<TD>(sG, l32, 32 * db + 16 * s + 4 * h);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int db = 0; db < NW; ++db)
 #pragma unroll
                         for (int s = 0; s < 2; ++s) {
-                            const bf16x8 gq = ld4x2<TD>(sG, l32, 32 * db + 16 * s + 4 * h);
-                            U = mfma(acc_op(X[db], s), gq, U);
+                            U = mfma(acc_op(X[db], s), gq[db][s], U);
                             // bidirectional: every term goes through the state, and with
                             // few keys dq is a small difference: S in two bf16 parts
-                            if constexpr (!CAUSAL) U = mfma(acc_lo(X[db], s), gq, U);
+                            if constexpr (!CAUSAL) U = mfma(acc_lo(X[db], s), gq[db][s], U);
                         }
                     float qu = 0.f, x4[4];
 #pragma unroll
@@ -188,10 +194,9 @@ void k_bwd_q_mfma(Args a, int qm_arg) {
                     // (the forward's A), the tile for the state waves; the denominators
                     float dA = 0.f;
                     if constexpr (CAUSAL) {
-                        f32x16 At = zero16();
-#pragma unroll 4
-                        for (int s = 0; s < F / 16; ++s)
-                            At = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), At);
+                        f32x16 At = mfma_chain<F / 16, 4>([&](int s) { return ld8<TF>(sK, l32, 16 * s + 8 * h); },
+                                                          [&](int s) { return ld8<TF>(sQ, l32, 16 * s + 8 * h); },
+                                                          zero16());
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             At[r] = acc_row(r, h) <= l32 ? (float)(__bf16)At[r] : 0.f;
@@ -207,10 +212,9 @@ void k_bwd_q_mfma(Args a, int qm_arg) {
                     }
                 } else if (CAUSAL && w == NW + 1) {
                     // T^T = V G^T (keys x queries), unmasked: the state waves mask
-                    f32x16 Tt = zero16();
-#pragma unroll 4
-                    for (int s = 0; s < D / 16; ++s)
-                        Tt = mfma(ld8<TD>(sV, l32, 16 * s + 8 * h), ld8<TD>(sG, l32, 16 * s + 8 * h), Tt);
+                    const f32x16 Tt = mfma_chain<D / 16, 4>([&](int s) { return ld8<TD>(sV, l32, 16 * s + 8 * h); },
+                                                            [&](int s) { return ld8<TD>(sG, l32, 16 * s + 8 * h); },
+                                                            zero16());
                     put_acc(sTt, Tt);
                 }
                 __syncthreads();
@@ -494,19 +498,15 @@ void k_bwd_kv_mfma(Args a, int qm) {
     // with bf16-rounded gn would not resolve.
     auto form_ap = [&]() {
         if (w == 0) {
-            f32x16 A = zero16();
-#pragma unroll
-            for (int s = 0; s < F / 16; ++s)
-                A = mfma(ld8<TF>(sQ, l32, 16 * s + 8 * h), ld8<TF>(sK, l32, 16 * s + 8 * h), A);
+            f32x16 A = mfma_chain<F / 16, 4>([&](int s) { return ld8<TF>(sQ, l32, 16 * s + 8 * h); },
+                                             [&](int s) { return ld8<TF>(sK, l32, 16 * s + 8 * h); }, zero16());
 #pragma unroll
             for (int r = 0; r < 16; ++r) A[r] = acc_row(r, h) >= l32 ? A[r] : 0.f;
             sAop[0][l] = acc_op(A, 0);
             sAop[1][l] = acc_op(A, 1);
         } else if (w == 1) {
-            f32x16 P = zero16();
-#pragma unroll
-            for (int s = 0; s < D / 16; ++s)
-                P = mfma(ld8<TD>(sGr, l32, 16 * s + 8 * h), ld8<TD>(sV, l32, 16 * s + 8 * h), P);
+            f32x16 P = mfma_chain<D / 16, 4>([&](int s) { return ld8<TD>(sGr, l32, 16 * s + 8 * h); },
+                                             [&](int s) { return ld8<TD>(sV, l32, 16 * s + 8 * h); }, zero16());
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const float4 cv = *reinterpret_cast<const float4 *>(sCc + 8 * q4 + 4 * h);
@@ -565,12 +565,9 @@ void k_bwd_kv_mfma(Args a, int qm) {
                     dK = mfma(acc_lo(Rt[db], s), vq, dK);
                 }
             }
-#pragma unroll 4
-        for (int s = 0; s < F / 16; ++s) {
-            const int k0 = 16 * s + 8 * h;
-            dV = mfma(tr8(tr_addr<TD>(sR, k0, 32 * w), tr_addr<TD>(sR, k0 + 4, 32 * w)),
-                      ld8<TF>(sK, l32, 16 * s + 8 * h), dV);
-        }
+        dV = mfma_chain<F / 16, 2>(
+            [&](int s) { return tr8(tr_addr<TD>(sR, 16 * s + 8 * h, 32 * w), tr_addr<TD>(sR, 16 * s + 8 * h + 4, 32 * w)); },
+            [&](int s) { return ld8<TF>(sK, l32, 16 * s + 8 * h); }, dV);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {   // rows 8 q4 + 4h + 0..3 are consecutive
             const float4 r4 = *reinterpret_cast<const float4 *>(sr + 32 * w + 8 * q4 + 4 * h);

@@ -432,10 +432,8 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void
             f32x16 Nt = zero16();
             bf16x8 B0, B1;
             if (fh == 0) {
-                f32x16 T = zero16();
-#pragma unroll 4
-                for (int s = 0; s < F / 16; ++s)
-                    T = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), T);
+                f32x16 T = mfma_chain<F / 16, 4>([&](int s) { return ld8<TF>(sK, l32, 16 * s + 8 * h); },
+                                                 [&](int s) { return ld8<TF>(sQ, l32, 16 * s + 8 * h); }, zero16());
 #pragma unroll
                 for (int r = 0; r < 16; ++r) T[r] = acc_row(r, h) <= l32 ? T[r] : 0.f;
                 B0 = acc_pk(T, 0);
@@ -447,11 +445,18 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void
                     Nt = mfma(va, s ? B1 : B0, Nt);
                 }
             }
+            // (the Phi(Q) operands all read before the products: the chain
+            // then waits for the LDS once)
+            bf16x8 qop[FH][2];
 #pragma unroll
             for (int i = 0; i < FH; ++i)
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    Nt = mfma(acc_pk(S[i], s), ld4x2<TF>(sQ, l32, 32 * (FH * fh + i) + 16 * s + 4 * h), Nt);
+                for (int s = 0; s < 2; ++s) qop[i][s] = ld4x2<TF>(sQ, l32, 32 * (FH * fh + i) + 16 * s + 4 * h);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < FH; ++i)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) Nt = mfma(acc_pk(S[i], s), qop[i][s], Nt);
             if (fh == 1) put_acc(sNp[vb], Nt);
             __syncthreads();
             if (fh == 0) {
