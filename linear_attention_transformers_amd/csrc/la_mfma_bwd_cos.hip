@@ -148,16 +148,14 @@ void k_bwd_q_cos_mfma(Args a) {
             // causal: A^T over the F features (the cos/sin weighting included)
             // on wave 0, T^T on wave 1, for every wave after the barrier below
             if (CAUSAL && w == 0) {
-                f32x16 At = zero16();
-#pragma unroll
-                for (int s = 0; s < F / 16; ++s)
-                    At = mfma(ld8<TF>(sK, l32, 16 * s + 8 * h), ld8<TF>(sQ, l32, 16 * s + 8 * h), At);
+                const f32x16 At = mfma_chain<F / 16, 2>([&](int s) { return ld8<TF>(sK, l32, 16 * s + 8 * h); },
+                                                        [&](int s) { return ld8<TF>(sQ, l32, 16 * s + 8 * h); },
+                                                        zero16());
                 put_acc(sAt, At);
             } else if (CAUSAL && w == 1) {
-                f32x16 Tt = zero16();
-#pragma unroll 4
-                for (int s = 0; s < D / 16; ++s)
-                    Tt = mfma(ld8<TD>(sV, l32, 16 * s + 8 * h), ld8<TD>(sG, l32, 16 * s + 8 * h), Tt);
+                const f32x16 Tt = mfma_chain<D / 16, 2>([&](int s) { return ld8<TD>(sV, l32, 16 * s + 8 * h); },
+                                                        [&](int s) { return ld8<TD>(sG, l32, 16 * s + 8 * h); },
+                                                        zero16());
                 put_acc(sTt, Tt);
             }
             // U^T = S g (feature block w x the chunk's queries), Phi(q).U over the
@@ -528,12 +526,9 @@ void k_bwd_kv_cos_mfma(Args a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) dK[r] -= sr[32 * w + acc_row(r, h)];
         if (w < NW) {
-#pragma unroll 4
-            for (int s = 0; s < F / 16; ++s) {
-                const int k0 = 16 * s + 8 * h;
-                dV = mfma(tr8(tr_addr<TD>(sR, k0, 32 * w), tr_addr<TD>(sR, k0 + 4, 32 * w)),
-                          ld8<TF>(sK, l32, 16 * s + 8 * h), dV);
-            }
+            dV = mfma_chain<F / 16, 2>(
+                [&](int s) { return tr8(tr_addr<TD>(sR, 16 * s + 8 * h, 32 * w), tr_addr<TD>(sR, 16 * s + 8 * h + 4, 32 * w)); },
+                [&](int s) { return ld8<TF>(sK, l32, 16 * s + 8 * h); }, dV);
         }
 
         // causal: the chunk's own queries (in-chunk terms) and the R update
@@ -557,19 +552,15 @@ void k_bwd_kv_cos_mfma(Args a) {
             // P from the raw g rows scaled in fp32 (it can be a small
             // difference, which bf16-rounded gn would not resolve)
             if (w == 0) {
-                f32x16 A = zero16();
-#pragma unroll 4
-                for (int s = 0; s < F / 16; ++s)
-                    A = mfma(ld8<TF>(sQ, l32, 16 * s + 8 * h), ld8<TF>(sK, l32, 16 * s + 8 * h), A);
+                f32x16 A = mfma_chain<F / 16, 4>([&](int s) { return ld8<TF>(sQ, l32, 16 * s + 8 * h); },
+                                                 [&](int s) { return ld8<TF>(sK, l32, 16 * s + 8 * h); }, zero16());
 #pragma unroll
                 for (int r = 0; r < 16; ++r) A[r] = acc_row(r, h) >= l32 ? A[r] : 0.f;
                 sAop[0][l] = acc_op(A, 0);
                 sAop[1][l] = acc_op(A, 1);
             } else if (w == 1) {
-                f32x16 P = zero16();
-#pragma unroll 4
-                for (int s = 0; s < D / 16; ++s)
-                    P = mfma(ld8<TD>(sGr, l32, 16 * s + 8 * h), ld8<TD>(sV, l32, 16 * s + 8 * h), P);
+                f32x16 P = mfma_chain<D / 16, 4>([&](int s) { return ld8<TD>(sGr, l32, 16 * s + 8 * h); },
+                                                 [&](int s) { return ld8<TD>(sV, l32, 16 * s + 8 * h); }, zero16());
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const float4 cv = *reinterpret_cast<const float4 *>(sCc + 8 * q4 + 4 * h);
