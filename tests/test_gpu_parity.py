@@ -138,19 +138,22 @@ def test_bidir_dkdv_grouped_segments(dtype, D, cos):
         dtype, D, "-cos" if cos else ""))
 
 
-SPAN = [(128, True, 4, 4), (128, False, 8, 4), (128, True, 8, 2)]
+SPAN = [(128, True, 4, 4, 16300), (128, False, 8, 4, 16300), (128, True, 8, 2, 16300),
+        (64, False, 8, 8, 32000)]
 
 
-@pytest.mark.parametrize("D,causal,H,Hkv", SPAN,
-                         ids=["D%d-%s-h%dkv%d" % (D, "causal" if c else "bidir", H, Hkv)
-                              for D, c, H, Hkv in SPAN])
-def test_dq_workgroup_spans_segments(D, causal, H, Hkv):
-    """Many short segments (seg_len 64) over a long ragged sequence at D = 128,
-    where the dq kernel runs one workgroup per compute unit: it then walks
+@pytest.mark.parametrize("D,causal,H,Hkv,N", SPAN,
+                         ids=["D%d-%s-h%dkv%d-n%d" % (D, "causal" if c else "bidir", H, Hkv, N)
+                              for D, c, H, Hkv, N in SPAN])
+def test_dq_workgroup_spans_segments(D, causal, H, Hkv, N):
+    """Many short segments (seg_len 64) over a long ragged sequence, where the
+    dq kernel runs one workgroup per compute unit at D = 128: it then walks
     several consecutive segments per workgroup (its state carry crosses their
-    boundaries) and writes one (R, r) record per segment."""
+    boundaries) and writes one (R, r) record per segment.  The D = 64
+    bidirectional case (8 units x 500 segments) also has each dk/dv
+    workgroup walk 16 segments."""
     torch, la = gpu_or_skip()
-    B, N = 1, 16300
+    B = 1
     t = make(B, H, Hkv, N, D, "bf16", scale=0.5, cos=False, seed=D + H + N)
     say("span D=%d causal=%s H=%d Hkv=%d N=%d seg_len=64" % (D, causal, H, Hkv, N))
     ref = oracle_on(t, causal, "elu+1", 1e-6)
