@@ -354,7 +354,9 @@ __global__ __launch_bounds__(D * 2) __attribute__((amdgpu_waves_per_eu(fwd_waves
 // w % (D/32) and the feature blocks of half w / (D/32) (its z block is
 // feature block w).  The first half forms the chunk's masked A tile over all
 // F features; the second half's partial numerators reach the first half
-// through LDS, which then normalises and stages the output rows.
+// through LDS, which then normalises and stages the output rows.  Phi(Q) and
+// Phi(q).z are double-buffered by head: a chunk's later heads are staged
+// during the previous head's products, two barriers per head instead of three.
 // ---------------------------------------------------------------------------
 template <int D, int F, int PHI, bool COS>
 __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void k_fwd_split_mfma(Args a) {
@@ -363,12 +365,12 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void
     constexpr int NT = D * 4, NW = D / 32, FH = F / 64;   // FH feature blocks per half
     static_assert(F == 2 * D, "two feature halves of D/32 blocks each");
     __shared__ __attribute__((aligned(16))) u16 sK[kCf * TF::ld];
-    __shared__ __attribute__((aligned(16))) u16 sQ[kCf * TF::ld];
+    __shared__ __attribute__((aligned(16))) u16 sQ2[2][kCf * TF::ld];   // Phi(Q) of a head, by head parity
     __shared__ __attribute__((aligned(16))) u16 sV[kCf * TD::ld];
     __shared__ __attribute__((aligned(16))) u16 sO[kCf * TD::ld];   // output rows of one head
     __shared__ __attribute__((aligned(16))) float sNp[NW][64 * 16];   // second half's numerators
     __shared__ __attribute__((aligned(16))) float sz[F];
-    __shared__ float sQZ[kCf];
+    __shared__ float sQZ2[2][kCf];
     const int seg = blockIdx.x % a.nseg, bg = blockIdx.x / a.nseg;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int t = threadIdx.x, l = t & 63, h = l >> 5, l32 = l & 31;
@@ -407,24 +409,23 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void
     for (int c0 = row0; c0 < row1; c0 += kCf) {
         __syncthreads();   // previous chunk: every LDS read done, sz updated, sO complete
         if (pend_oh) store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
+        pend_oh = nullptr;
         rK.template store_feat<PHI, COS, TF, false>(sK, c0, a.N, nullptr, nullptr);
         rV.template store<TD>(sV);
         rK.template load<COS>(kh, c0 + kCf, a.N, a.cw, a.sw);   // next chunk (past the segment: clamped, unused)
         rV.load(vh, c0 + kCf, a.N);
-        rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, sz, sQZ);
+        rQ.template store_feat<PHI, COS, TF, true>(sQ2[0], c0, a.N, sz, sQZ2[0]);
+        {   // Q rows of the second head, or of the first head at the next chunk
+            const bool last = a.nrep == 1;
+            rQ.load(qbase + (bh0 + (last ? 0 : 1)) * a.N * D, last ? c0 + kCf : c0, a.N);
+            if (COS && last) rQ.load_w(a.cw, a.sw, c0 + kCf, a.N);   // new positions
+        }
         for (int rep = 0; rep < a.nrep; ++rep) {
             u16 *oh = obase + (bh0 + rep) * a.N * D;
-            if (rep > 0) {
-                __syncthreads();   // every wave is done with the previous head's sQ; sO complete
-                rQ.template store_feat<PHI, COS, TF, true>(sQ, c0, a.N, sz, sQZ);
-                store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);
-            }
-            __syncthreads();
-            {   // Q rows of the next head, or of the first head at the next chunk
-                const bool last = rep + 1 == a.nrep;
-                rQ.load(qbase + (bh0 + (last ? 0 : rep + 1)) * a.N * D, last ? c0 + kCf : c0, a.N);
-                if (COS && last) rQ.load_w(a.cw, a.sw, c0 + kCf, a.N);   // new positions
-            }
+            const int cur = rep & 1;
+            const u16 *const sQ = sQ2[cur];
+            __syncthreads();   // this head's Phi(Q) (and the chunk's K, V) staged; sO complete
+            if (pend_oh) store_rows<D, NT, TD>(pend_oh, sO, pend_c0, a.N);   // the previous head's rows
             // num^T of value block vb: the first half adds V^T A^T, each half
             // its feature blocks' S^T Phi(Q)^T.  The first half forms A^T
             // (keys x queries) over all F features, causal mask, bf16 rounding
@@ -458,6 +459,14 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
                 for (int s = 0; s < 2; ++s) Nt = mfma(acc_pk(S[i], s), qop[i][s], Nt);
             if (fh == 1) put_acc(sNp[vb], Nt);
+            // the next head's Phi(Q) into the other buffer (last read by the
+            // previous head, before the barrier above), then the rows after it
+            if (rep + 1 < a.nrep) {
+                rQ.template store_feat<PHI, COS, TF, true>(sQ2[cur ^ 1], c0, a.N, sz, sQZ2[cur ^ 1]);
+                const bool last = rep + 2 >= a.nrep;
+                rQ.load(qbase + (bh0 + (last ? 0 : rep + 2)) * a.N * D, last ? c0 + kCf : c0, a.N);
+                if (COS && last) rQ.load_w(a.cw, a.sw, c0 + kCf, a.N);   // new positions
+            }
             __syncthreads();
             if (fh == 0) {
                 const f32x16 P = get_acc(sNp[vb]);
@@ -465,7 +474,7 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void
                 for (int r = 0; r < 16; ++r) Nt[r] += P[r];
                 // sum_j A_ij on the matrix cores: 1^T A^T, every row holds it
                 const float dsum = mfma(one, B1, mfma(one, B0, zero16()))[0];
-                const float den = dsum + sQZ[l32] + a.eps;
+                const float den = dsum + sQZ2[cur][l32] + a.eps;
                 stage_out<TD>(sO, Nt, rcp(den), 32 * vb);
             }
             pend_oh = oh;
@@ -484,8 +493,8 @@ __global__ __launch_bounds__(D * 4) __attribute__((amdgpu_waves_per_eu(2))) void
                 if (i == vb) Z = mfma(ka, one, Z);   // feature block w = FH * fh + vb
             }
         }
-        // every head's staging has read sz (they all passed the barrier before
-        // their products), so it can take the new z now
+        // every head's staging has read sz (each before a barrier this wave has
+        // passed since), so it can take the new z now
         if (l32 == 0) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) sz[32 * w + acc_row(r, h)] = Z[r];
