@@ -117,6 +117,26 @@ def test_many_segments_every_family(dtype, D, causal, cos):
         dtype, D, "causal" if causal else "bidir", "-cos" if cos else ""))
 
 
+COS_HEADS = [(3, 1, 0), (3, 1, 64), (2, 2, 64), (5, 1, 0)]
+
+
+@pytest.mark.parametrize("H,Hkv,seg_len", COS_HEADS,
+                         ids=["h%dkv%d-seg%d" % c for c in COS_HEADS])
+def test_causal_cos_head_counts(H, Hkv, seg_len):
+    """The causal cos/sin kernels (D = 128, F = 256) at odd and single head
+    counts per KV head: n_rep = 3 and 5 (the forward's per-head buffers then
+    end a chunk on the buffer the next chunk's first head takes) and
+    n_rep = 1; a ragged N = 700 over several 32-row chunks per segment, at
+    the automatic split and at 64-row segments."""
+    torch, la = gpu_or_skip()
+    B, N, D = 1, 700, 128
+    t = make(B, H, Hkv, N, D, "bf16", scale=0.5, cos=True, seed=H + 10 * Hkv + seg_len)
+    say("causal cos heads H=%d Hkv=%d seg_len=%d" % (H, Hkv, seg_len))
+    ref = oracle_on(t, True, "elu+1", 1e-6)
+    out, grads = run_gpu(la, t, True, "elu+1", 1e-6, seg_len=seg_len)
+    compare(t, out, grads, ref[0], ref[1], "bf16", H, Hkv, label="cos-heads-h%dkv%d-seg%d" % (H, Hkv, seg_len))
+
+
 GROUPED = [("bf16", 64, False), ("bf16", 128, False), ("bf16", 64, True), ("f32", 64, False)]
 
 
