@@ -498,14 +498,14 @@ void k_bwd_kv_mfma(Args a, int qm) {
     // with bf16-rounded gn would not resolve.
     auto form_ap = [&]() {
         if (w == 0) {
-            f32x16 A = mfma_chain<F / 16, 4>([&](int s) { return ld8<TF>(sQ, l32, 16 * s + 8 * h); },
+            f32x16 A = mfma_chain<F / 16, 2>([&](int s) { return ld8<TF>(sQ, l32, 16 * s + 8 * h); },
                                              [&](int s) { return ld8<TF>(sK, l32, 16 * s + 8 * h); }, zero16());
 #pragma unroll
             for (int r = 0; r < 16; ++r) A[r] = acc_row(r, h) >= l32 ? A[r] : 0.f;
             sAop[0][l] = acc_op(A, 0);
             sAop[1][l] = acc_op(A, 1);
         } else if (w == 1) {
-            f32x16 P = mfma_chain<D / 16, 4>([&](int s) { return ld8<TD>(sGr, l32, 16 * s + 8 * h); },
+            f32x16 P = mfma_chain<D / 16, 2>([&](int s) { return ld8<TD>(sGr, l32, 16 * s + 8 * h); },
                                              [&](int s) { return ld8<TD>(sV, l32, 16 * s + 8 * h); }, zero16());
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
@@ -522,6 +522,13 @@ void k_bwd_kv_mfma(Args a, int qm) {
             sPop[1][l] = acc_op(P, 1);
         }
     };
+    // The dk, dv rows of a chunk are staged in the query tiles sQ, sG and
+    // stored as whole rows after the next barrier: by each thread, ahead of
+    // its own staging of the next head's rows, which writes exactly the pieces
+    // it reads (the same thread-to-piece map), so no barrier separates them.
+    // (From the registers, 8-byte pieces scattered over 32 rows per
+    // instruction, the stores cost far more.)
+    int pend_c0 = -1;
     for (int ci = nch - 1; ci >= 0; --ci) {
         const int c0 = row0 + ci * kCb;
         const int cn = ci > 0 ? c0 - kCb : c0;   // next chunk (none: reload this one)
@@ -544,6 +551,13 @@ void k_bwd_kv_mfma(Args a, int qm) {
                 }
             if (h == 0) sr[32 * w + l32] = racc;
         }
+        if (pend_c0 >= 0) {   // the previous chunk's rows (fences: one tile's registers at a time)
+            __builtin_amdgcn_sched_barrier(0);
+            store_rows<D, NT, TF, true>(dkh, sQ, pend_c0, a.N);
+            __builtin_amdgcn_sched_barrier(0);
+            store_rows<D, NT, TD, true>(dvh, sG, pend_c0, a.N);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         if constexpr (CAUSAL) stage_head(c0, 0, cn);
         __syncthreads();
         // causal: the first head's A and P tiles (waves 0 and 1), ahead of the
@@ -565,9 +579,12 @@ void k_bwd_kv_mfma(Args a, int qm) {
                     dK = mfma(acc_lo(Rt[db], s), vq, dK);
                 }
             }
-        dV = mfma_chain<F / 16, 2>(
-            [&](int s) { return tr8(tr_addr<TD>(sR, 16 * s + 8 * h, 32 * w), tr_addr<TD>(sR, 16 * s + 8 * h + 4, 32 * w)); },
-            [&](int s) { return ld8<TF>(sK, l32, 16 * s + 8 * h); }, dV);
+#pragma unroll 4
+        for (int s = 0; s < F / 16; ++s) {
+            const int k0 = 16 * s + 8 * h;
+            dV = mfma(tr8(tr_addr<TD>(sR, k0, 32 * w), tr_addr<TD>(sR, k0 + 4, 32 * w)),
+                      ld8<TF>(sK, l32, 16 * s + 8 * h), dV);
+        }
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {   // rows 8 q4 + 4h + 0..3 are consecutive
             const float4 r4 = *reinterpret_cast<const float4 *>(sr + 32 * w + 8 * q4 + 4 * h);
@@ -618,8 +635,8 @@ void k_bwd_kv_mfma(Args a, int qm) {
         }
         // dk = phi'(k) dPhi(k), dv; lane holds key l32 and columns 32w + 8q + 4h + 0..3,
         // stored straight from the registers (the next chunk's tiles take the LDS)
-        const int row = c0 + l32;
-        if (row < a.N) {
+        if constexpr (CAUSAL) __syncthreads();   // every read of the last head's sQ, sG is done
+        {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int f0 = 32 * w + 8 * q4 + 4 * h;
@@ -630,10 +647,16 @@ void k_bwd_kv_mfma(Args a, int qm) {
                     ok4[e] = dK[4 * q4 + e] * phi_d_feat<PHI>(kf[e]);
                     ov4[e] = dV[4 * q4 + e];
                 }
-                st4bf(dkh + (size_t)row * D + f0, ok4);
-                st4bf(dvh + (size_t)row * D + f0, ov4);
+                st4bf(sQ + TF::at(l32, f0), ok4);
+                st4bf(sG + TD::at(l32, f0), ov4);
             }
         }
+        pend_c0 = c0;
+    }
+    if (pend_c0 >= 0) {
+        __syncthreads();
+        store_rows<D, NT, TF>(dkh, sQ, pend_c0, a.N);
+        store_rows<D, NT, TD>(dvh, sG, pend_c0, a.N);
     }
 }
 
