@@ -25,7 +25,10 @@
 // fragments per 16-wide substep (ld8 for K-contiguous tiles, the transposed
 // LDS read for the others) and issues 32 MFMAs.  The next K step's
 // tiles are loaded into registers while the current one computes and stored
-// to the other half of a double-buffered LDS tile, one barrier per K step.
+// to the other half of a double-buffered LDS tile, one barrier per K step;
+// the stores go out during the last two sub-steps, one between each pair of
+// MFMAs, so the LDS writes overlap the products instead of preceding the
+// barrier on their own.
 // Loads past M, N or the K range stage zeros.  K-contiguous operands need
 // K % 8 == 0, the others M (or N) % 8 == 0, all bases 16-byte aligned.
 #include <type_traits>
@@ -43,6 +46,7 @@ using namespace mf;
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int WAVES_M = 2, WAVES_N = 4, GT = 64 * WAVES_M * WAVES_N;   // 8 waves, 2 per SIMD
 constexpr int FM = BM / WAVES_M / 32, FN = BN / WAVES_N / 32;          // 32x32 blocks per wave: 4 x 2
+constexpr int STA = BK / 16 - 2, STB = BK / 16 - 1;   // sub-steps that store the next A and B tiles
 
 // LDS tile of one operand for one K step: K-contiguous operands as
 // [256 rows (m or n)][64], the others as [64 rows (k)][256].
@@ -73,12 +77,11 @@ __device__ __forceinline__ void load_tile(uint4 (&r)[OpTile<KC>::NV], const u16 
     }
 }
 
-// Stores the loaded tile to LDS; a tile that reaches past MN or kend (uniform
-// test) first has its vectors there replaced by zeros.  Masking at the store
-// rather than at the load keeps the loads in flight through the K step.
+// Replaces the loaded vectors that lie past MN or kend by zeros; a tile that
+// reaches past neither (uniform test) is left as loaded.  Masking after the
+// load rather than at it keeps the loads in flight through the K step.
 template <bool KC>
-__device__ __forceinline__ void store_tile(u16 *s, uint4 (&r)[OpTile<KC>::NV], int mn0, int k0, int MN,
-                                           int kend) {
+__device__ __forceinline__ void mask_tile(uint4 (&r)[OpTile<KC>::NV], int mn0, int k0, int MN, int kend) {
     using T = OpTile<KC>;
     if (mn0 + BM > MN || k0 + BK > kend) {
 #pragma unroll
@@ -89,6 +92,12 @@ __device__ __forceinline__ void store_tile(u16 *s, uint4 (&r)[OpTile<KC>::NV], i
             if (!(mn < MN && k < kend)) r[j] = make_uint4(0, 0, 0, 0);
         }
     }
+}
+
+// Stores the (masked) tile to LDS.
+template <bool KC>
+__device__ __forceinline__ void put_tile(u16 *s, uint4 (&r)[OpTile<KC>::NV]) {
+    using T = OpTile<KC>;
 #pragma unroll
     for (int j = 0; j < T::NV; ++j) {
         const int v = threadIdx.x + j * GT, row = v / T::V8, c8 = (v % T::V8) * 8;
@@ -161,8 +170,10 @@ void k_lowrank_gemm(GemmArgs g) {
     uint4 rA[OpTile<AKC>::NV], rB[OpTile<BKC>::NV];
     load_tile<AKC>(rA, g.A, g.lda, m0, kbeg, g.M, g.K);
     load_tile<BKC>(rB, g.B, g.ldb, n0, kbeg, g.N, g.K);
-    store_tile<AKC>(sA(0), rA, m0, kbeg, g.M, kend);
-    store_tile<BKC>(sB(0), rB, n0, kbeg, g.N, kend);
+    mask_tile<AKC>(rA, m0, kbeg, g.M, kend);
+    mask_tile<BKC>(rB, n0, kbeg, g.N, kend);
+    put_tile<AKC>(sA(0), rA);
+    put_tile<BKC>(sB(0), rB);
     __syncthreads();
     for (int kt = 0; kt < nkt; ++kt) {
         const int cur = kt & 1;
@@ -179,13 +190,30 @@ void k_lowrank_gemm(GemmArgs g) {
             for (int i = 0; i < FM; ++i) a[i] = frag<AKC>(sA(cur), wm * WTM + 32 * i, sub);
 #pragma unroll
             for (int j = 0; j < FN; ++j) b[j] = frag<BKC>(sB(cur), wn * WTN + 32 * j, sub);
+            // the next K step goes to the other buffer (free since the last
+            // barrier): A's vectors during sub-step STA, B's during STB, each
+            // store issued between two products so the writes overlap them
+            if (sub == STA) {
+                mask_tile<AKC>(rA, m0, kn, g.M, kend);
+                put_tile<AKC>(sA(cur ^ 1), rA);
+            }
+            if (sub == STB) {
+                mask_tile<BKC>(rB, n0, kn, g.N, kend);
+                put_tile<BKC>(sB(cur ^ 1), rB);
+            }
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int i = 0; i < FM; ++i) acc[j][i] = mfma(b[j], a[i], acc[j][i]);
+            if (sub == STA || sub == STB) {
+                const int nst = sub == STA ? OpTile<AKC>::NV : OpTile<BKC>::NV;
+#pragma unroll
+                for (int q = 0; q < FM * FN; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
+                    if (q < nst) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // one LDS write
+                }
+            }
         }
-        store_tile<AKC>(sA(cur ^ 1), rA, m0, kn, g.M, kend);
-        store_tile<BKC>(sB(cur ^ 1), rB, n0, kn, g.N, kend);
         __syncthreads();
     }
 
