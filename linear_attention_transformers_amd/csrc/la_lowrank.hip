@@ -378,10 +378,12 @@ hipError_t gemm(const char *name, const u16 *A, long long lda, const u16 *B, lon
 }  // namespace
 
 int lowrank_splits(int M, int rows, int cols) {
-    // enough tiles x splits to fill the chip twice, with at least 1024 tokens per split
+    // enough tiles x splits to fill the chip once (one workgroup per CU), with at
+    // least 1024 tokens per split; twice that many took longer, in the products
+    // and in summing twice the partials
     const long long tiles = (long long)((rows + BM - 1) / BM) * ((cols + BN - 1) / BN);
     int s = 1;
-    while (tiles * s < 512 && (long long)M / (2 * s) >= 1024) s *= 2;
+    while (tiles * s < 256 && (long long)M / (2 * s) >= 1024) s *= 2;
     return s;
 }
 
