@@ -4,6 +4,9 @@ CPU oracle on the same seeded inputs.
 * small shapes that span several chunks, several segments and a ragged tail,
   for every storage type, head size, feature map, mode, cos/sin and GQA;
 * edge cases (N = 1, N shorter than a chunk, one row past a chunk boundary);
+* 64 seeded random configurations, every argument drawn at once (storage
+  type, D, feature map, mode, cos/sin, B, H, H_kv, ragged N, segment length,
+  saved or recomputed state);
 * the five specified workloads at full size in the launch configuration the
   benchmark times, compared on sampled (batch, KV head) groups, which the
   oracle computes exactly because groups never interact;
@@ -58,6 +61,50 @@ def test_small_shapes(case):
     for seg_len in (0, 64):           # automatic split, then many short segments
         out, grads = run_gpu(la, t, causal, phi, eps, seg_len=seg_len)
         compare(t, out, grads, ref[0], ref[1], dtype, H, Hkv, label="%s-seg%d" % (_id(case), seg_len))
+
+
+# --------------------------------------------------------------------------
+# seeded random configurations: every argument drawn at once, so that
+# combinations the grids above do not list (GQA with cos/sin in float32 at
+# D = 32, identity with a forced segment length, the saved-state backward on
+# ragged N, ...) are also run against the oracle
+# --------------------------------------------------------------------------
+def _random_cases(count=64, seed=20261203):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        Hkv = int(rng.integers(1, 3))
+        cases.append(dict(
+            dtype=str(rng.choice(["bf16", "f32"])), D=int(rng.choice([32, 64, 128])),
+            phi=str(rng.choice(["elu+1", "relu", "identity"])), causal=bool(rng.integers(0, 2)),
+            cos=bool(rng.integers(0, 2)), B=int(rng.integers(1, 3)), Hkv=Hkv,
+            H=Hkv * int(rng.integers(1, 4)), N=int(rng.integers(1, 701)),
+            seg_len=int(rng.choice([0, 64, 128, 192])), saved=bool(rng.integers(0, 2)), seed=1000 + i))
+    return cases
+
+
+RANDOM = _random_cases()
+
+
+def _rid(c):
+    return "%s-D%d-%s-%s%s-b%dh%dkv%d-n%d-seg%d%s" % (
+        c["dtype"], c["D"], c["phi"], "causal" if c["causal"] else "bidir", "-cos" if c["cos"] else "",
+        c["B"], c["H"], c["Hkv"], c["N"], c["seg_len"], "-saved" if c["saved"] else "")
+
+
+@pytest.mark.parametrize("c", RANDOM, ids=[_rid(c) for c in RANDOM])
+def test_random_configurations(c):
+    torch, la = gpu_or_skip()
+    t = make(c["B"], c["H"], c["Hkv"], c["N"], c["D"], c["dtype"], scale=0.5, cos=c["cos"], seed=c["seed"])
+    positive = c["phi"] == "identity"
+    if positive:   # identity is not non-negative: keep the denominators away from 0
+        for n in ("q", "k"):
+            t[n] = t[n].abs()
+    eps = 1.0 if positive else 1e-6
+    say("case %s" % _rid(c))
+    ref = oracle_on(t, c["causal"], c["phi"], eps)
+    out, grads = run_gpu(la, t, c["causal"], c["phi"], eps, seg_len=c["seg_len"], saved=c["saved"])
+    compare(t, out, grads, ref[0], ref[1], c["dtype"], c["H"], c["Hkv"], label=_rid(c))
 
 
 @pytest.mark.parametrize("N", [1, 5, 31, 33, 64, 65, 129])
