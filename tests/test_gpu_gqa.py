@@ -6,8 +6,8 @@ The expansion is byte work and the sum is the exact float64 sum rounded once
 to the storage type on both sides, so every comparison is bitwise.  Cases:
 the 16-byte vector path with ragged block tails, the element path (slab size
 not a multiple of 16 bytes, or a base off 16-byte alignment), k alone (v pair
-NULL), n_rep = 1, and the long GQA workload's shapes at full size on sampled
-rows."""
+NULL), n_rep = 1, 12 seeded random shapes, and the long GQA workload's shapes
+at full size on sampled rows."""
 import ctypes
 
 import numpy as np
@@ -37,6 +37,10 @@ for dtype in ("bf16", "f32"):
                                  (2, 2, 1, 17, 64), (1, 3, 3, 1, 8)]:
         CASES.append((dtype, B, Hkv, nrep, N, D))
     CASES.append((dtype, 2, 2, 4, 37, 3))    # element path: slab bytes not a multiple of 16
+_rng = np.random.default_rng(20261205)
+for _ in range(12):   # seeded random shapes (D = 3 takes the element path)
+    CASES.append((str(_rng.choice(["bf16", "f32"])), int(_rng.integers(1, 4)), int(_rng.integers(1, 5)),
+                  int(_rng.integers(1, 9)), int(_rng.integers(1, 400)), int(_rng.choice([3, 8, 16, 32, 64, 128]))))
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "%s-B%d-Hkv%d-rep%d-N%d-D%d" % c)

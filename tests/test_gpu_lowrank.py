@@ -6,7 +6,8 @@ Tolerance: max |gpu - oracle| / max |oracle| per output <= 2e-2 (bf16
 storage; t and g U rounded to bf16 between products, float32 accumulation).
 Shapes span ragged edges of every GEMM tile (M, in, rank, out not multiples
 of 256; K ranges not multiples of 64), several K splits, leading axes, bias
-on and off; the benchmark's full shapes are checked on sampled entries;
+on and off, plus 16 seeded random shapes; the benchmark's full shapes are
+checked on sampled entries;
 results are bitwise reproducible."""
 import numpy as np
 import pytest
@@ -36,6 +37,10 @@ CASES = [
     (0, 40, 16, 48, True, (3, 5)),          # leading axes [3, 5]
     (4096, 128, 64, 96, True, None),        # token-axis products in several K splits
 ]
+_rng = np.random.default_rng(20261204)
+for _ in range(16):   # seeded random shapes, every dimension ragged against the 256 x 256 x 64 tiles
+    CASES.append((int(_rng.integers(1, 5000)), 8 * int(_rng.integers(1, 80)), 8 * int(_rng.integers(1, 48)),
+                  8 * int(_rng.integers(1, 80)), bool(_rng.integers(0, 2)), None))
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "M%d-in%d-r%d-out%d-bias%d-lead%s" % (
