@@ -1,7 +1,9 @@
 """Host-side measurement logic of bench.py (no GPU): the algorithmic bytes it
 assigns to each kernel the library's timing can report for the attention
-workloads, and the step roofline of the headline workload against figures
-derived by hand from the workload's shape."""
+workloads, the step roofline of the headline workload against figures
+derived by hand from the workload's shape, the traffic field's lookup in the
+committed counter summaries (dropped once a kernel source changes), and the
+refusal of more than one GPU."""
 import os
 import re
 
@@ -62,3 +64,52 @@ def test_headline_step_roofline():
     assert flops == 2 * 128 * 128 * 32768 * (2 * 32 + 6 * 32)
     assert t_roof == pytest.approx(11 * 2 ** 28 / 8.0e12)   # HBM-bound: 0.369 ms
     assert t_roof * 1e3 == pytest.approx(0.369, abs=1e-3)
+
+
+# --------------------------------------------------------------------------
+# traffic field: read from the committed counter summaries, and dropped as
+# soon as a kernel source differs from the one the counters were taken on
+# --------------------------------------------------------------------------
+LOWRANK = "lowrank_m32768_in4096_r1024_out4096"
+
+
+def _copy_tree(tmp_path):
+    import shutil
+    shutil.copytree(os.path.join(ROOT, "profiles"), str(tmp_path / "profiles"))
+    shutil.copytree(CSRC, str(tmp_path / "linear_attention_transformers_amd" / "csrc"))
+    return tmp_path
+
+
+def test_traffic_from_committed_summary():
+    t = bench.measured_traffic(LOWRANK, "k_lowrank_gemm_xVt")
+    if t is None:
+        pytest.skip("the low-rank counter summary predates the current la_lowrank.hip")
+    # x V^T moves at least its algorithmic bytes: x and V read, t written
+    M, n_in, rank = 32768, 4096, 1024
+    algorithmic = 2 * (M * n_in + rank * n_in + M * rank)
+    assert algorithmic <= t <= 3 * algorithmic
+
+
+def test_traffic_dropped_when_a_source_changes(tmp_path, monkeypatch):
+    root = _copy_tree(tmp_path)
+    monkeypatch.setattr(bench, "ROOT", str(root))
+    before = bench.measured_traffic(LOWRANK, "k_lowrank_gemm_xVt")
+    src = root / "linear_attention_transformers_amd" / "csrc" / "la_lowrank.hip"
+    src.write_text(src.read_text() + "\n// edited\n")
+    assert bench.measured_traffic(LOWRANK, "k_lowrank_gemm_xVt") is None
+    if before is None:
+        pytest.skip("the committed summary was already stale")
+
+
+def test_traffic_none_without_summary_or_kernel():
+    assert bench.measured_traffic("no_such_workload", "k_lowrank_gemm_xVt") is None
+    assert bench.measured_traffic(LOWRANK, "k_no_such_kernel") is None
+
+
+def test_more_than_one_gpu_refused():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], cwd=ROOT,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr or "1 GPU" in r.stderr, r.stderr[-400:]
