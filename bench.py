@@ -18,8 +18,8 @@ a read of a 1 GiB buffer that evicts the L2 and last-level caches, and each
 bracketed by a pair of HIP events on the stream the library launches on; the
 K steps are bracketed by device synchronisations.  value = tokens / median
 step time.  Further passes of K flushed steps give the per-kernel breakdown
-(the library's own launch events), the forward alone (la_fwd, the north-star
-quantity) and the step with the backward recomputing the state (la_bwd).  The
+(the library's own launch events), the forward alone (la_fwd, with its own
+roofline fraction) and the step with the backward recomputing the state (la_bwd).  The
 forward and the backward of a step share one workspace, so the backward reuses
 the forward's state records (la_bwd_saved, as the autograd form does).  One
 JSON line on stdout.
